@@ -1,0 +1,264 @@
+"""CPU oracle for deterministic sparse MLA: stable top-k, canonical order, paged gather, MQA attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it.  It shares no code with the HIP path.
+
+Everything here is written for a reader checking it by eye against the
+definitions: plain numpy, float64 for all floating point, no blocking, no
+fusion.  Library primitives used as single steps: ``np.lexsort`` (a sort),
+``@`` (a matmul), ``np.exp`` / ``np.log``.
+
+Sources (pages as titled; sections named):
+
+* "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL"
+  (vllm-project/vllm PR 54955), section "Deterministic sparse top-k": the
+  selector ranks candidates by a composite score/index key with a stable
+  tie-break, and the selected indices are put into one canonical order before
+  attention so the reduction order is fixed.  Section "Sparse MLA and
+  FlashMLA": decode gathers KV for the selected tokens and runs the same sparse
+  attention as prefill; prefill chunks each request on its own.
+* "[Bugfix] Make DSV4 sparse MLA work end-to-end for plain decode, MTP, and
+  DSpark" (vllm-project/vllm PR 51538), "What is fixed", items "Negative
+  indexer context lengths under MTP" and "Top-k kernels hardened against
+  out-of-range lengths": lengths are clamped to [0, row stride] before any
+  decision; rows with fewer candidates than k are padded with -1.  Item
+  "Graph replay and draft KV": a token's cache slot is its physical block id
+  times the block size plus its offset in the block.
+* "Port DeepSeek-V4 optimization PR #174 to v0.26 ..." (MooreThreads/vllm-musa
+  PR 178), table "Optimizations carried from PR #174": FP8 KV with fp32 scale
+  groups kept contiguous.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+
+* ties between equal scores go to the lower index; -0.0 equals +0.0 (IEEE
+  comparison); +-inf are ordinary values; NaN ranks below -inf and NaNs tie
+  among themselves by index;
+* the selected indices are emitted in ascending index order, then -1 padding;
+* indices are logical token positions in the row's request; the gather maps
+  position p to physical slot block_table[req, p // 64] * 64 + p % 64;
+* all heads share one 576-wide latent record K_j (512 latent + 64 rope) and
+  the value vector is its first 512 entries;
+* LSE is the natural-log log-sum-exp of the scaled scores; a row with no
+  selected token has output 0 and LSE -inf;
+* the FP8 record is [512 e4m3 codes | 4 fp32 scales | 64 bf16 rope]; latent
+  entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+KV_BF16 = 0
+KV_FP8 = 1
+BF16_RECORD_BYTES = 1152
+FP8_RECORD_BYTES = 656
+
+
+# ----------------------------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64.  A bf16 value is the binary32 number whose upper 16 bits
+    are the pattern and whose lower 16 bits are zero; the widening is exact."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns widen to NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_to_f64(codes) -> np.ndarray:
+    """OCP 8-bit floating point, E4M3 (FN) variant -> float64, from the format definition:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
+    subnormals (m/8) * 2**-6; S.1111.111 is NaN; there are no infinities."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    val = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+
+
+def decode_record(rec: np.ndarray, kv_dtype: int) -> np.ndarray:
+    """One token record (raw bytes, uint8) -> float64 [576] = [512 latent | 64 rope]."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    if kv_dtype == KV_BF16:
+        assert rec.shape[-1] == BF16_RECORD_BYTES
+        return bf16_to_f64(rec.view(np.uint16))
+    assert rec.shape[-1] == FP8_RECORD_BYTES
+    codes = rec[..., :512]
+    scales = rec[..., 512:528].view(np.float32).astype(np.float64)       # [..., 4]
+    rope = bf16_to_f64(rec[..., 528:656].view(np.uint16))                # [..., 64]
+    lat = e4m3fn_to_f64(codes) * np.repeat(scales, 128, axis=-1)          # group g = d // 128
+    return np.concatenate([lat, rope], axis=-1)
+
+
+# ----------------------------------------------------------------------------------------------
+# A0: candidate counts
+# ----------------------------------------------------------------------------------------------
+
+def clamp_length(length: int, row_stride: int) -> int:
+    """A row's candidate count is its length clamped to [0, row_stride]."""
+    return int(min(max(int(length), 0), int(row_stride)))
+
+
+def causal_lengths(first_pos: int, T: int) -> np.ndarray:
+    """Query token t of a chunk sits at position first_pos + t and may attend to positions
+    0..first_pos + t, so its candidate count is first_pos + t + 1, never below 0."""
+    return np.array([max(0, first_pos + t + 1) for t in range(T)], dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------------------
+# A1-A3: stable top-k and canonical order
+# ----------------------------------------------------------------------------------------------
+
+def topk_row(scores_row: np.ndarray, length: int, k: int) -> np.ndarray:
+    """Indices of the top n = min(k, L) candidates of one row, ascending, then -1 padding.
+
+    Total order on candidates j in [0, L): a higher score comes first; equal scores (IEEE
+    equality, so -0.0 == +0.0) come in increasing index order; NaN comes after every number
+    and NaNs come in increasing index order.  The first n candidates in that order are the
+    selection; the emitted list is the selection sorted by index.
+    """
+    L = clamp_length(length, len(scores_row))
+    n = min(int(k), L)
+    out = np.full(int(k), -1, dtype=np.int32)
+    if n == 0:
+        return out
+    v = np.asarray(scores_row[:L], dtype=np.float64)
+    is_nan = np.isnan(v)
+    vv = np.where(is_nan, 0.0, v)
+    # np.lexsort orders by the LAST key first: NaN flag (numbers first), then -score
+    # (so higher scores first; -0.0 and +0.0 compare equal), then index.
+    order = np.lexsort((np.arange(L), -vv, is_nan))
+    out[:n] = np.sort(order[:n]).astype(np.int32)
+    return out
+
+
+def topk_rows(scores: np.ndarray, lengths: Optional[Sequence[int]], k: int,
+              row_offsets: Optional[Sequence[int]] = None, row_stride: Optional[int] = None,
+              rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """topk_row for each requested row.  ``scores`` is either a 2-D [R, stride] array or a flat
+    array addressed through ``row_offsets`` (element offsets) with ``row_stride`` entries per row."""
+    flat = scores.reshape(-1) if row_offsets is not None else None
+    nrows = len(lengths) if lengths is not None else scores.shape[0]
+    stride = int(row_stride if row_stride is not None else scores.shape[-1])
+    idx = list(range(nrows)) if rows is None else list(rows)
+    out = np.empty((len(idx), int(k)), dtype=np.int32)
+    for o, r in enumerate(idx):
+        if row_offsets is not None:
+            base = int(row_offsets[r])
+            row = flat[base:base + stride]
+        else:
+            row = scores[r]
+        L = stride if lengths is None else int(lengths[r])
+        out[o] = topk_row(row, L, k)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A4-A5: paged gather
+# ----------------------------------------------------------------------------------------------
+
+def physical_slot(block_table_row: np.ndarray, pos: int, page: int = PAGE) -> int:
+    """Logical position -> physical cache slot: block id * block size + offset in the block."""
+    return int(block_table_row[pos // page]) * page + pos % page
+
+
+def gather_tokens(kv: np.ndarray, kv_dtype: int, block_table_row: np.ndarray,
+                  positions: Sequence[int]) -> np.ndarray:
+    """Records of the given logical positions (in the given order) as float64 [n, 576].
+    ``kv`` holds the raw bytes [num_pages, 64, record_bytes]."""
+    flat = kv.reshape(-1, kv.shape[-1])
+    recs = [decode_record(flat[physical_slot(block_table_row, int(p))], kv_dtype) for p in positions]
+    if not recs:
+        return np.zeros((0, D_QK))
+    return np.stack(recs)
+
+
+# ----------------------------------------------------------------------------------------------
+# A7-A9: MQA attention over the gathered latent tokens
+# ----------------------------------------------------------------------------------------------
+
+def attention(q: np.ndarray, K: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of every head of ``q`` [H, 576] over the shared tokens ``K`` [n, 576].
+
+    s[h, j] = scale * <q_h, K_j> over all 576 entries; p[h, :] = softmax(s[h, :]);
+    O[h, :] = sum_j p[h, j] * K_j[:512]; LSE[h] = log sum_j exp(s[h, j]).
+    With n = 0 the output is 0 and LSE is -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    H = q.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros((H, D_V)), np.full(H, -np.inf)
+    s = scale * (q @ K.T)                       # [H, n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    O = p @ K[:, :D_V]
+    lse = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def split_combine(parts: Sequence[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine per-split (O_s, LSE_s) results of disjoint token subsets of one row, in the
+    listed order: LSE = log sum_s exp(LSE_s); O = sum_s exp(LSE_s - LSE) * O_s.  Splits with
+    LSE_s = -inf contribute nothing; if every split is empty the result is (0, -inf)."""
+    lses = np.stack([p[1] for p in parts])      # [S, H]
+    Os = np.stack([p[0] for p in parts])        # [S, H, D]
+    m = lses.max(axis=0)                        # [H]
+    H = lses.shape[1]
+    O = np.zeros(Os.shape[1:])
+    LSE = np.full(H, -np.inf)
+    for h in range(H):
+        if not np.isfinite(m[h]):
+            continue
+        w = np.exp(lses[:, h] - m[h])
+        tot = w.sum()
+        LSE[h] = m[h] + math.log(tot)
+        for s in range(len(parts)):
+            O[h] += (w[s] / tot) * Os[s, h]
+    return O, LSE
+
+
+# ----------------------------------------------------------------------------------------------
+# Whole rows: top-k -> canonical indices -> gather -> attention
+# ----------------------------------------------------------------------------------------------
+
+def attention_rows(q_bits: np.ndarray, kv: np.ndarray, kv_dtype: int, block_table: np.ndarray,
+                   row_req: Optional[Sequence[int]], idx: np.ndarray, scale: float,
+                   rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention for each requested row over the tokens listed in ``idx`` [R, k] (entries -1
+    are skipped).  ``q_bits`` holds bf16 patterns [R, H, 576]."""
+    sel = list(range(idx.shape[0])) if rows is None else list(rows)
+    H = q_bits.shape[1]
+    O = np.zeros((len(sel), H, D_V))
+    LSE = np.zeros((len(sel), H))
+    for o, r in enumerate(sel):
+        req = 0 if row_req is None else int(row_req[r])
+        pos = [int(p) for p in idx[r] if p >= 0]
+        K = gather_tokens(kv, kv_dtype, block_table[req], pos)
+        O[o], LSE[o] = attention(bf16_to_f64(q_bits[r]), K, scale)
+    return O, LSE
+
+
+def decode_rows(q_bits, kv, kv_dtype, block_table, row_req, scores, lengths, k, scale,
+                rows=None, row_offsets=None, row_stride=None):
+    """The whole decode path for the requested rows: (indices, O, LSE)."""
+    sel = list(range(len(lengths))) if rows is None else list(rows)
+    idx = topk_rows(scores, lengths, k, row_offsets=row_offsets, row_stride=row_stride, rows=sel)
+    q_sel = np.asarray(q_bits)[sel]
+    req_sel = None if row_req is None else [int(row_req[r]) for r in sel]
+    O, LSE = attention_rows(q_sel, kv, kv_dtype, block_table, req_sel, idx, scale)
+    return idx, O, LSE

@@ -1,0 +1,274 @@
+"""Seeded synthetic inputs for the sparse-MLA decode / prefill path.
+
+This module only draws random numbers and lays them out in the buffers the
+library consumes.  It holds none of the method's arithmetic: no top-k, no
+gather, no softmax.  Both the CPU oracle (under ``oracle/``) and the HIP path
+consume the same bytes produced here.
+
+Layouts (all row-major, contiguous):
+
+* ``kv`` bf16 cache: ``uint16 [num_pages, 64, 576]`` (bf16 bit patterns); one
+  token record is 576 bf16 = 1152 B: 512 latent values followed by 64 rope
+  values.
+* ``kv`` FP8 cache: ``uint8 [num_pages, 64, 656]``; one token record is
+  ``[512 B e4m3 codes | 4 x fp32 group scales | 64 x bf16 rope]``.
+* ``block_table`` ``int32 [num_requests, max_pages]``: logical page ``p`` of
+  request ``r`` lives in physical page ``block_table[r, p]``.  Unused entries
+  are 0, the null page.
+* Physical page 0 is the null page and is filled with NaN.  Slots at or past a
+  request's length inside its last page are NaN as well, so any read that is
+  not asked for shows up as NaN in an output.
+* ``scores`` ``float32 [rows, stride]``: entries at or past a row's candidate
+  count are +inf, so a selector that looks past the length picks them.
+
+Random draws are made with ``torch.Generator`` on the requested device, so the
+same seed gives the same bytes on every run on that device kind.  Draw order
+for a decode workload: context lengths, physical page permutation, scores, Q,
+KV (latent/codes, then scales, then rope for FP8).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import torch
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+D_ROPE = 64
+BF16_RECORD_BYTES = D_QK * 2
+FP8_RECORD_BYTES = 512 + 4 * 4 + D_ROPE * 2  # 656
+KV_BF16 = 0
+KV_FP8 = 1
+
+BF16_NAN_BITS = 0x7FC0
+FP8_NAN_CODE = 0x7F
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+@dataclasses.dataclass
+class PagedCache:
+    kv: torch.Tensor            # uint8 bytes [num_pages, 64, record_bytes]
+    kv_dtype: int               # KV_BF16 or KV_FP8
+    block_table: torch.Tensor   # int32 [num_requests, max_pages]
+    ctx_lens: torch.Tensor      # int64 [num_requests]
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def record_bytes(self) -> int:
+        return int(self.kv.shape[2])
+
+
+@dataclasses.dataclass
+class RowSet:
+    """One batch of query rows against a paged cache."""
+    q: torch.Tensor             # bf16 [rows, H, 576]
+    scores: torch.Tensor        # fp32 [rows, stride]
+    lengths: torch.Tensor       # int32 [rows]  candidate count per row
+    row_req: torch.Tensor       # int32 [rows]  request each row reads
+
+
+def uniform_int(lo: int, hi: int, n: int, g: torch.Generator, device) -> torch.Tensor:
+    """n integers drawn uniformly from the inclusive range [lo, hi]."""
+    return torch.randint(lo, hi + 1, (n,), generator=g, device=device, dtype=torch.int64)
+
+
+def make_paged_cache(ctx_lens: torch.Tensor, kv_dtype: int, g: torch.Generator, device,
+                     chunk_pages: int = 4096) -> PagedCache:
+    """Allocate a paged cache holding one context per entry of ``ctx_lens``.
+
+    Physical pages 1..N are handed out through a seeded random permutation;
+    page 0 is the NaN null page.  Values: bf16 N(0,1) for the bf16 cache; for
+    the FP8 cache, e4m3 codes of N(0,1) (round to nearest even), fp32 scales
+    2**U(-4, 4) per (token, 128-group) and bf16 N(0,1) rope.
+    """
+    ctx_lens = ctx_lens.to(torch.int64).cpu()
+    npages = [int(math.ceil(int(L) / PAGE)) for L in ctx_lens]
+    total = sum(npages)
+    max_pages = max(1, max(npages) if npages else 1)
+    perm = torch.randperm(total, generator=g, device=device).cpu() + 1
+    bt = torch.zeros((len(npages), max_pages), dtype=torch.int32)
+    off = 0
+    for r, n in enumerate(npages):
+        bt[r, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    rec = BF16_RECORD_BYTES if kv_dtype == KV_BF16 else FP8_RECORD_BYTES
+    kv = torch.empty((total + 1, PAGE, rec), dtype=torch.uint8, device=device)
+    # Fill physical pages in chunks so the fp32 intermediates stay small.
+    for p0 in range(1, total + 1, chunk_pages):
+        p1 = min(total + 1, p0 + chunk_pages)
+        ntok = (p1 - p0) * PAGE
+        if kv_dtype == KV_BF16:
+            vals = torch.randn((ntok, D_QK), generator=g, device=device, dtype=torch.float32)
+            kv[p0:p1] = vals.to(torch.bfloat16).view(torch.uint8).view(p1 - p0, PAGE, rec)
+        else:
+            lat = torch.randn((ntok, 512), generator=g, device=device, dtype=torch.float32)
+            codes = lat.to(torch.float8_e4m3fn).view(torch.uint8)
+            expo = torch.rand((ntok, 4), generator=g, device=device, dtype=torch.float32) * 8.0 - 4.0
+            scales = torch.exp2(expo).contiguous().view(torch.uint8).view(ntok, 16)
+            rope = torch.randn((ntok, D_ROPE), generator=g, device=device, dtype=torch.float32)
+            rope_b = rope.to(torch.bfloat16).view(torch.uint8).view(ntok, 128)
+            kv[p0:p1] = torch.cat([codes, scales, rope_b], dim=1).view(p1 - p0, PAGE, rec)
+    poison_cache(kv, bt, ctx_lens, kv_dtype)
+    return PagedCache(kv=kv, kv_dtype=kv_dtype, block_table=bt.to(device), ctx_lens=ctx_lens)
+
+
+def _poison_record(kv_dtype: int, device) -> torch.Tensor:
+    if kv_dtype == KV_BF16:
+        return torch.full((D_QK,), BF16_NAN_BITS, dtype=torch.int16, device=device).view(torch.uint8)
+    codes = torch.full((512,), FP8_NAN_CODE, dtype=torch.uint8, device=device)
+    scales = torch.full((4,), float("nan"), dtype=torch.float32, device=device).view(torch.uint8)
+    rope = torch.full((D_ROPE,), BF16_NAN_BITS, dtype=torch.int16, device=device).view(torch.uint8)
+    return torch.cat([codes, scales, rope])
+
+
+def poison_cache(kv: torch.Tensor, bt_cpu: torch.Tensor, ctx_lens, kv_dtype: int) -> None:
+    """NaN-fill the null page and every slot past a context's end in its last page."""
+    rec = _poison_record(kv_dtype, kv.device)
+    kv[0] = rec
+    for r, L in enumerate(ctx_lens):
+        L = int(L)
+        if L % PAGE:
+            last = int(bt_cpu[r, L // PAGE])
+            kv[last, L % PAGE:] = rec
+
+
+def _scores_block(rows: int, stride: int, g, device, kind: str) -> torch.Tensor:
+    if kind == "normal":
+        return torch.randn((rows, stride), generator=g, device=device, dtype=torch.float32)
+    if kind == "eighths":  # N(0,1) rounded to multiples of 1/8: forces ties and produces -0.0
+        return torch.round(torch.randn((rows, stride), generator=g, device=device,
+                                       dtype=torch.float32) * 8.0) / 8.0
+    raise ValueError(kind)
+
+
+def poison_score_tails(scores: torch.Tensor, lengths: torch.Tensor) -> None:
+    """Set scores at or past each row's candidate count to +inf."""
+    stride = scores.shape[1]
+    pos = torch.arange(stride, device=scores.device).unsqueeze(0)
+    mask = pos >= lengths.to(scores.device).to(torch.int64).clamp(min=0).unsqueeze(1)
+    scores.masked_fill_(mask, float("inf"))
+
+
+def make_rowset(cache: PagedCache, row_req: torch.Tensor, lengths: torch.Tensor, H: int, stride: int,
+                g: torch.Generator, device, score_kind: str = "normal") -> RowSet:
+    rows = int(row_req.numel())
+    scores = _scores_block(rows, stride, g, device, score_kind)
+    poison_score_tails(scores, lengths)
+    q = torch.randn((rows, H, D_QK), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return RowSet(q=q, scores=scores, lengths=lengths.to(torch.int32).to(device),
+                  row_req=row_req.to(torch.int32).to(device))
+
+
+# --------------------------------------------------------------------------------------------
+# Named workloads.  Sizes follow the decode / top-k / prefill shapes the method is run at.
+# --------------------------------------------------------------------------------------------
+
+SOFTMAX_SCALE = 1.0 / math.sqrt(D_QK)
+
+
+@dataclasses.dataclass
+class DecodeWorkload:
+    name: str
+    cache: PagedCache
+    sets: List[RowSet]
+    H: int
+    k: int
+    scale: float
+    stride: int
+
+
+def decode_workload(name: str, B: int, H: int, k: int, ctx_lo: int, ctx_hi: int, kv_dtype: int,
+                    seed: int, device, n_sets: int = 1, score_kind: str = "normal",
+                    stride: Optional[int] = None) -> DecodeWorkload:
+    """B decode rows, one request each, context lengths uniform in [ctx_lo, ctx_hi].
+
+    ``n_sets`` independent (Q, scores) sets share one cache; timing loops rotate
+    through them so a step's gathered set is not already cache-resident.
+    """
+    g = _gen(seed, device)
+    ctx = uniform_int(ctx_lo, ctx_hi, B, g, device).cpu()
+    cache = make_paged_cache(ctx, kv_dtype, g, device)
+    stride = int(stride if stride is not None else ctx_hi)
+    row_req = torch.arange(B, dtype=torch.int32)
+    sets = [make_rowset(cache, row_req, ctx.to(torch.int32), H, stride, g, device, score_kind)
+            for _ in range(n_sets)]
+    return DecodeWorkload(name=name, cache=cache, sets=sets, H=H, k=k, scale=SOFTMAX_SCALE, stride=stride)
+
+
+def tiny_decode(device, seed: int = 0) -> DecodeWorkload:
+    """B=2, H=16, 4096-token contexts (64 pages each), k=256, scores in steps of 1/8."""
+    return decode_workload("tiny_decode_B2_H16_L4096_k256", B=2, H=16, k=256, ctx_lo=4096, ctx_hi=4096,
+                           kv_dtype=KV_BF16, seed=seed, device=device, score_kind="eighths")
+
+
+def decode_bf16(device, seed: int = 2, n_sets: int = 1) -> DecodeWorkload:
+    """B=64, H=64, k=2048, contexts uniform in [8192, 65536], bf16 KV."""
+    return decode_workload("decode_bf16_B64_H64_k2048_L8K-64K", B=64, H=64, k=2048, ctx_lo=8192, ctx_hi=65536,
+                           kv_dtype=KV_BF16, seed=seed, device=device, n_sets=n_sets)
+
+
+def decode_fp8(device, seed: int = 3, n_sets: int = 1) -> DecodeWorkload:
+    """B=128, H=64, k=2048, contexts uniform in [32768, 131072], FP8 e4m3 latent with per-128 fp32 scales."""
+    return decode_workload("decode_fp8_B128_H64_k2048_L32K-128K", B=128, H=64, k=2048, ctx_lo=32768,
+                           ctx_hi=131072, kv_dtype=KV_FP8, seed=seed, device=device, n_sets=n_sets)
+
+
+def topk_levels(device, rows: int = 64, L: int = 65536, levels: int = 256, seed: int = 1) -> torch.Tensor:
+    """rows x L fp32 scores; each row uses ``levels`` distinct nonzero N(0,1) values (heavy ties)."""
+    g = _gen(seed, device)
+    out = torch.empty((rows, L), dtype=torch.float32, device=device)
+    for r in range(rows):
+        while True:
+            lv = torch.randn((levels,), generator=g, device=device, dtype=torch.float32)
+            if torch.unique(lv).numel() == levels and bool((lv != 0).all()):
+                break
+        pick = torch.randint(0, levels, (L,), generator=g, device=device)
+        out[r] = lv[pick]
+    return out
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    name: str
+    cache: PagedCache           # request 0 is the prefill context; 1..63 the decode rows' contexts
+    q: torch.Tensor             # bf16 [T, H, 576] prefill query rows
+    scores: torch.Tensor        # fp32 [T, ctx] prefill scores (+inf past each row's causal length)
+    first_pos: int              # position of query row 0
+    decode: RowSet              # the decode rows mixed in later (row_req 1..63)
+    mix_order: torch.Tensor     # int64 [T + n_dec]: mixed-batch slot -> source (< T prefill row, else decode row)
+    H: int
+    k: int
+    scale: float
+
+
+def prefill_chunk(device, seed: int = 4, T: int = 4096, ctx: int = 131072, H: int = 64, k: int = 2048,
+                  n_dec: int = 63, dec_lo: int = 8192, dec_hi: int = 65536) -> PrefillWorkload:
+    """One request: T query tokens at positions ctx-T .. ctx-1 of a ctx-token paged context (causal),
+    plus n_dec decode rows (contexts uniform in [dec_lo, dec_hi]) to be mixed into one batch."""
+    g = _gen(seed, device)
+    dec_ctx = uniform_int(dec_lo, dec_hi, n_dec, g, device).cpu()
+    all_ctx = torch.cat([torch.tensor([ctx], dtype=torch.int64), dec_ctx])
+    cache = make_paged_cache(all_ctx, KV_BF16, g, device)
+    first_pos = ctx - T
+    causal = torch.arange(T, dtype=torch.int64) + first_pos + 1
+    scores = _scores_block(T, ctx, g, device, "normal")
+    poison_score_tails(scores, causal)
+    q = torch.randn((T, H, D_QK), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    dec_req = torch.arange(1, n_dec + 1, dtype=torch.int32)
+    dec = make_rowset(cache, dec_req, dec_ctx.to(torch.int32), H, dec_hi, g, device, "normal")
+    mix_order = torch.randperm(T + n_dec, generator=g, device=device).cpu()
+    return PrefillWorkload(name=f"prefill_T{T}_ctx{ctx}_H{H}_k{k}_mixed{n_dec}", cache=cache, q=q,
+                           scores=scores, first_pos=first_pos, decode=dec, mix_order=mix_order, H=H, k=k,
+                           scale=SOFTMAX_SCALE)

@@ -1,0 +1,415 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something other than itself
+(brute force on tiny inputs, closed forms, library special cases, invariants, hand-derived
+fixtures).  CPU only."""
+
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as O
+
+
+def _num(x):
+    if isinstance(x, str):
+        return float(x)
+    return float(x)
+
+
+# ----------------------------------------------------------------------------------------------
+# Top-k
+# ----------------------------------------------------------------------------------------------
+
+def _precedes(vi, i, vj, j):
+    """Brute-force reading of the order, with Python float comparisons only."""
+    ni, nj = math.isnan(vi), math.isnan(vj)
+    if ni and nj:
+        return i < j
+    if ni != nj:
+        return nj            # numbers before NaN
+    if vi > vj:
+        return True
+    if vi == vj:
+        return i < j
+    return False
+
+
+def brute_topk(scores, length, k):
+    L = min(max(length, 0), len(scores))
+    n = min(k, L)
+    sel = []
+    for j in range(L):
+        ahead = sum(1 for i in range(L) if i != j and _precedes(scores[i], i, scores[j], j))
+        if ahead < n:
+            sel.append(j)
+    assert len(sel) == n
+    return sel + [-1] * (k - n)
+
+
+VALUE_POOL = [0.0, -0.0, 1.0, -1.0, 0.5, 2.0, float("inf"), float("-inf"), float("nan"), 1e-30, -1e-30]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_matches_brute_force_on_tiny_rows(seed):
+    rng = random.Random(seed)
+    L = rng.randint(0, 24)
+    pool = rng.sample(VALUE_POOL, rng.randint(1, len(VALUE_POOL)))
+    row = [rng.choice(pool) for _ in range(L)] + [123.0] * rng.randint(0, 3)   # tail past the length
+    for k in {1, 3, 16, max(1, L - 1), max(1, L), L + 5}:
+        for length in {L, 0, -3, L + 7}:
+            got = O.topk_row(np.array(row, dtype=np.float32), length, k).tolist()
+            ref = brute_topk(row, length, k)
+            assert got == ref, (row, length, k)
+
+
+def test_topk_brute_force_random_float_rows():
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        L = int(rng.integers(1, 60))
+        row = rng.standard_normal(L).astype(np.float32)
+        row[rng.integers(0, L, size=L // 3)] = row[0]            # planted ties
+        k = int(rng.integers(1, L + 3))
+        assert O.topk_row(row, L, k).tolist() == brute_topk(row.tolist(), L, k)
+
+
+def test_topk_golden_hand_cases(golden_dir):
+    data = json.load(open(os.path.join(golden_dir, "topk_hand_cases.json")))
+    for c in data["cases"]:
+        row = np.array([_num(x) for x in c["scores"]], dtype=np.float32)
+        got = O.topk_row(row, c["length"], c["k"]).tolist()
+        assert got == c["expected"], c["name"]
+
+
+def test_topk_special_cases():
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal(1000).astype(np.float32)
+    # k >= L: every candidate, in order
+    assert O.topk_row(row, 100, 100).tolist() == list(range(100))
+    assert O.topk_row(row, 100, 130).tolist() == list(range(100)) + [-1] * 30
+    # all equal: the k lowest indices
+    assert O.topk_row(np.full(500, 3.5, np.float32), 500, 37).tolist() == list(range(37))
+    # k = 1 is the first maximum (np.argmax returns the first occurrence)
+    tied = np.round(row * 2) / 2
+    assert O.topk_row(tied, 1000, 1).tolist() == [int(np.argmax(tied))]
+    # strictly decreasing / increasing rows
+    dec = np.arange(1000, 0, -1).astype(np.float32)
+    assert O.topk_row(dec, 1000, 10).tolist() == list(range(10))
+    assert O.topk_row(dec[::-1].copy(), 1000, 10).tolist() == list(range(990, 1000))
+    # negative / zero lengths
+    assert O.topk_row(row, -5, 4).tolist() == [-1] * 4
+    assert O.topk_row(row, 0, 4).tolist() == [-1] * 4
+
+
+def test_topk_selected_set_matches_partition_on_distinct_values():
+    """With distinct values the selected set is the set np.argpartition picks."""
+    rng = np.random.default_rng(11)
+    for L, k in [(5000, 2048), (65536, 2048), (300, 299)]:
+        row = rng.permutation(L).astype(np.float32) - L / 2
+        part = np.argpartition(-row, k - 1)[:k]
+        assert O.topk_row(row, L, k).tolist() == sorted(part.tolist())
+
+
+def test_topk_heavy_ties_invariants():
+    """256 distinct levels, 65536 candidates: selected count, ascending order, and that the
+    cut respects both the score order and the lower-index rule."""
+    rng = np.random.default_rng(5)
+    levels = rng.standard_normal(256).astype(np.float32)
+    row = levels[rng.integers(0, 256, 65536)]
+    out = O.topk_row(row, 65536, 2048)
+    assert (np.diff(out) > 0).all() and len(out) == 2048
+    selv = row[out]
+    mask = np.zeros(65536, bool)
+    mask[out] = True
+    t = selv.min()
+    assert (row[~mask] <= t).all()                       # nothing better left out
+    eq_idx = np.nonzero(row == t)[0]
+    taken = eq_idx[mask[eq_idx]]
+    assert (taken == eq_idx[:len(taken)]).all()          # ties at the cut: lowest indices
+
+
+# Mutants: plausible mistakes, planted in copies of the oracle's top-k on the CPU, must fail a pin.
+
+def _mutant_reverse_ties(row, length, k):
+    L = O.clamp_length(length, len(row)); n = min(k, L)
+    v = np.asarray(row[:L], np.float64); nan = np.isnan(v)
+    order = np.lexsort((-np.arange(L), -np.where(nan, 0, v), nan))
+    out = np.full(k, -1, np.int32); out[:n] = np.sort(order[:n]); return out
+
+
+def _mutant_signed_zero(row, length, k):
+    L = O.clamp_length(length, len(row)); n = min(k, L)
+    v = np.asarray(row[:L], np.float64)
+    key = np.where(np.isnan(v), -np.inf, v) + np.where(np.signbit(v) & (v == 0), -1e-300, 0.0)
+    order = np.lexsort((np.arange(L), -key))
+    out = np.full(k, -1, np.int32); out[:n] = np.sort(order[:n]); return out
+
+
+def _mutant_no_clamp(row, length, k):
+    L = len(row) if length < 0 else min(length, len(row))
+    return O.topk_row(row, L, k)
+
+
+@pytest.mark.parametrize("mutant", [_mutant_reverse_ties, _mutant_signed_zero, _mutant_no_clamp])
+def test_pins_catch_topk_mutants(mutant, golden_dir):
+    data = json.load(open(os.path.join(golden_dir, "topk_hand_cases.json")))
+    caught = False
+    for c in data["cases"]:
+        row = np.array([_num(x) for x in c["scores"]], dtype=np.float32)
+        if mutant(row, c["length"], c["k"]).tolist() != c["expected"]:
+            caught = True
+    assert caught
+
+
+# ----------------------------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------------------------
+
+def test_bf16_all_patterns_match_torch():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = O.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+    assert np.array_equal(np.signbit(ours[~np.isnan(ours)]), np.signbit(ref[~np.isnan(ref)]))
+
+
+def test_e4m3fn_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3fn_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3fn_spec_values(golden_dir):
+    data = json.load(open(os.path.join(golden_dir, "fp8_e4m3fn_values.json")))
+    for v in data["values"]:
+        got = float(O.e4m3fn_to_f64(np.array([v["code"]], np.uint8))[0])
+        exp = _num(v["value"])
+        if math.isnan(exp):
+            assert math.isnan(got)
+        else:
+            assert got == exp and math.copysign(1, got) == math.copysign(1, exp), v
+
+
+def test_fp8_record_group_scales_and_rope():
+    rec = np.zeros(656, np.uint8)
+    rec[:512] = 0x38                                              # every code is 1.0
+    rec[512:528] = np.array([1.0, 2.0, 0.25, -8.0], np.float32).view(np.uint8)
+    rope = np.arange(64, dtype=np.float32) - 20.0                  # bf16-exact values
+    rec[528:] = (rope.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8)
+    out = O.decode_record(rec, O.KV_FP8)
+    assert out.shape == (576,)
+    np.testing.assert_array_equal(out[:512], np.repeat([1.0, 2.0, 0.25, -8.0], 128))
+    np.testing.assert_array_equal(out[512:], rope)
+
+
+def test_bf16_record_layout():
+    vals = (np.arange(576, dtype=np.float32) % 64 - 32.0) / 4.0  # at most 7 significant bits: bf16-exact
+    rec = (vals.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8)
+    np.testing.assert_array_equal(O.decode_record(rec, O.KV_BF16), vals)
+
+
+# ----------------------------------------------------------------------------------------------
+# Lengths and gather
+# ----------------------------------------------------------------------------------------------
+
+def test_causal_lengths_golden(golden_dir):
+    data = json.load(open(os.path.join(golden_dir, "causal_lengths.json")))
+    for c in data["cases"]:
+        got = O.causal_lengths(c["first_pos"], c["T"])
+        if "expected" in c:
+            assert got.tolist() == c["expected"], c["name"]
+        else:
+            assert got[0] == c["expected_first"] and got[-1] == c["expected_last"]
+            assert (np.diff(got) == 1).all()
+
+
+def test_physical_slot_hand_example():
+    bt = np.array([5, 2, 9])
+    # position 130 is in logical block 2 (-> physical 9) at offset 2
+    assert O.physical_slot(bt, 130) == 9 * 64 + 2
+    assert O.physical_slot(bt, 0) == 5 * 64
+    assert O.physical_slot(bt, 127) == 2 * 64 + 63
+
+
+def test_gather_round_trips_a_dense_context():
+    """Write a dense context into pages through a random block table, then gather it back."""
+    rng = np.random.default_rng(2)
+    L, npages = 300, 5
+    dense = rng.standard_normal((L, 576)).astype(np.float32)
+    dense_bits = (dense.view(np.uint32) >> 16).astype(np.uint16)
+    perm = rng.permutation(np.arange(1, 9))[:npages]
+    kv = np.full((9, 64, 576), 0x7FC0, np.uint16)                # NaN everywhere else
+    for p in range(L):
+        kv[perm[p // 64], p % 64] = dense_bits[p]
+    pos = rng.permutation(L)[:50]
+    got = O.gather_tokens(kv.view(np.uint8).reshape(9, 64, 1152), O.KV_BF16, perm, pos)
+    np.testing.assert_array_equal(got, O.bf16_to_f64(dense_bits[pos]))
+
+
+# ----------------------------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------------------------
+
+def _bf16_round(x):
+    return O.bf16_to_f64((np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_attention_two_token_closed_form():
+    """q is nonzero only in a rope entry, so the scores are (0, scale*c); the output mixes the
+    two latent rows with weights 1/(1+e^x), e^x/(1+e^x); LSE = log(1 + e^x)."""
+    rng = np.random.default_rng(0)
+    H, c, scale = 3, 2.0, 1.0 / 24.0
+    q = np.zeros((H, 576)); q[:, 512] = c * np.array([1.0, -1.0, 4.0])
+    K = np.zeros((2, 576)); K[:, :512] = _bf16_round(rng.standard_normal((2, 512)))
+    K[1, 512] = 1.0
+    Oo, lse = O.attention(q, K, scale)
+    for h, mult in enumerate([1.0, -1.0, 4.0]):
+        x = scale * c * mult
+        w1 = math.exp(x) / (1 + math.exp(x))
+        np.testing.assert_allclose(Oo[h], (1 - w1) * K[0, :512] + w1 * K[1, :512], rtol=0, atol=1e-14)
+        assert abs(lse[h] - math.log(1 + math.exp(x))) < 1e-14
+
+
+def test_attention_q_zero_gives_mean_and_log_n():
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((37, 576))
+    Oo, lse = O.attention(np.zeros((4, 576)), K, 0.1)
+    np.testing.assert_allclose(Oo, np.tile(K[:, :512].mean(0), (4, 1)), atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(37), atol=1e-13)
+
+
+def test_attention_weights_sum_to_one():
+    """If every value row is the same vector v, the output is v: the weights sum to 1."""
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((50, 576)) * 3
+    v = rng.standard_normal(512)
+    K[:, :512] = v
+    Oo, _ = O.attention(rng.standard_normal((8, 576)), K, 1 / 24)
+    np.testing.assert_allclose(Oo, np.tile(v, (8, 1)), atol=1e-12)
+
+
+def test_attention_matches_torch_sdpa_dense():
+    """With every context token selected the method is textbook dense softmax attention."""
+    rng = np.random.default_rng(6)
+    H, n = 16, 200
+    q = rng.standard_normal((H, 576)); K = rng.standard_normal((n, 576))
+    Oo, lse = O.attention(q, K, 1 / 24)
+    qt = torch.from_numpy(q)[None, :, None, :]                   # [1, H, 1, 576]
+    kt = torch.from_numpy(K)[None, None].expand(1, H, n, 576)
+    vt = torch.from_numpy(K[:, :512].copy())[None, None].expand(1, H, n, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / 24)[0, :, 0].numpy()
+    np.testing.assert_allclose(Oo, ref, atol=1e-12)
+    ref_lse = torch.logsumexp(torch.from_numpy(q @ K.T / 24), dim=1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, atol=1e-12)
+
+
+def test_attention_order_invariance_and_hull():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((4, 576)); K = rng.standard_normal((64, 576))
+    O1, l1 = O.attention(q, K, 1 / 24)
+    perm = rng.permutation(64)
+    O2, l2 = O.attention(q, K[perm], 1 / 24)
+    np.testing.assert_allclose(O1, O2, atol=1e-13); np.testing.assert_allclose(l1, l2, atol=1e-13)
+    lo, hi = K[:, :512].min(0), K[:, :512].max(0)
+    assert ((O1 >= lo - 1e-12) & (O1 <= hi + 1e-12)).all()
+
+
+def test_attention_single_token_and_empty():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, 576)); K = rng.standard_normal((1, 576))
+    Oo, lse = O.attention(q, K, 0.5)
+    np.testing.assert_allclose(Oo, np.tile(K[0, :512], (2, 1)), atol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * (q @ K[0]), atol=1e-13)
+    Oe, le = O.attention(q, np.zeros((0, 576)), 0.5)
+    assert (Oe == 0).all() and np.isneginf(le).all()
+
+
+def test_split_combine_equals_single_pass():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((6, 576)); K = rng.standard_normal((90, 576)) * 2
+    full = O.attention(q, K, 1 / 24)
+    cuts = [0, 0, 17, 40, 40, 90]                                 # includes empty splits
+    parts = [O.attention(q, K[a:b], 1 / 24) for a, b in zip(cuts[:-1], cuts[1:])]
+    comb = O.split_combine(parts)
+    np.testing.assert_allclose(comb[0], full[0], atol=1e-13)
+    np.testing.assert_allclose(comb[1], full[1], atol=1e-13)
+    empty = O.split_combine([O.attention(q, K[:0], 1 / 24)] * 3)
+    assert (empty[0] == 0).all() and np.isneginf(empty[1]).all()
+
+
+def test_decode_rows_composes_selection_gather_and_attention():
+    """The composed path equals dense attention over exactly the brute-force-selected tokens."""
+    rng = np.random.default_rng(12)
+    L, H, k = 150, 2, 10
+    npages = 3
+    perm = np.array([3, 1, 2])
+    dense = rng.standard_normal((L, 576)).astype(np.float32)
+    bits = (dense.view(np.uint32) >> 16).astype(np.uint16)
+    kv = np.full((4, 64, 576), 0x7FC0, np.uint16)
+    for p in range(L):
+        kv[perm[p // 64], p % 64] = bits[p]
+    scores = np.round(rng.standard_normal((1, 160)) * 2) / 2
+    q = (rng.standard_normal((1, H, 576)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    idx, Oo, lse = O.decode_rows(q, kv.view(np.uint8).reshape(4, 64, 1152), O.KV_BF16, perm[None],
+                                 [0], scores.astype(np.float32), [L], k, 1 / 24)
+    sel = brute_topk(scores[0].astype(np.float32).tolist(), L, k)
+    assert idx[0].tolist() == sel
+    Kd = O.bf16_to_f64(bits[sel])
+    qd = O.bf16_to_f64(q[0])
+    s = qd @ Kd.T / 24
+    p = np.exp(s - s.max(1, keepdims=True)); p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(Oo[0], p @ Kd[:, :512], atol=1e-13)
+
+
+# Attention mutants, planted in copies of the oracle's attention on the CPU: each must fail a pin.
+
+def _att_mutant_v_tail(q, K, scale):            # value taken from the last 512 entries
+    s = scale * (q @ K.T); p = np.exp(s - s.max(1, keepdims=True)); l = p.sum(1, keepdims=True)
+    return (p / l) @ K[:, -512:], (s.max(1, keepdims=True) + np.log(l))[:, 0]
+
+
+def _att_mutant_no_scale(q, K, scale):
+    return O.attention(q, K, 1.0)
+
+
+def _att_mutant_log2(q, K, scale):
+    Oo, lse = O.attention(q, K, scale)
+    return Oo, lse / math.log(2)
+
+
+def _att_mutant_rope_dropped(q, K, scale):      # scores over the latent part only
+    K2 = K.copy(); K2[:, 512:] = 0
+    Oo, lse = O.attention(q, K2, scale)
+    return Oo, lse
+
+
+@pytest.mark.parametrize("mutant", [_att_mutant_v_tail, _att_mutant_no_scale, _att_mutant_log2,
+                                    _att_mutant_rope_dropped])
+def test_pins_catch_attention_mutants(mutant):
+    """The two-token closed form (rope-only query) and the SDPA comparison reject each mutant."""
+    rng = np.random.default_rng(0)
+    H, c, scale = 3, 2.0, 1.0 / 24.0
+    q = np.zeros((H, 576)); q[:, 512] = c * np.array([1.0, -1.0, 4.0])
+    K = np.zeros((2, 576)); K[:, :512] = _bf16_round(rng.standard_normal((2, 512)))
+    K[1, 512] = 1.0
+    Oo, lse = mutant(q, K, scale)
+    ok_closed = True
+    for h, mult in enumerate([1.0, -1.0, 4.0]):
+        x = scale * c * mult
+        w1 = math.exp(x) / (1 + math.exp(x))
+        ok_closed &= bool(np.allclose(Oo[h], (1 - w1) * K[0, :512] + w1 * K[1, :512], atol=1e-12))
+        ok_closed &= abs(lse[h] - math.log(1 + math.exp(x))) < 1e-12
+    q2 = rng.standard_normal((4, 576)); K2 = rng.standard_normal((30, 576))
+    Om, lm = mutant(q2, K2, 1 / 24)
+    qt = torch.from_numpy(q2)[None, :, None, :]
+    kt = torch.from_numpy(K2)[None, None].expand(1, 4, 30, 576)
+    vt = torch.from_numpy(K2[:, :512].copy())[None, None].expand(1, 4, 30, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / 24)[0, :, 0].numpy()
+    ok_sdpa = bool(np.allclose(Om, ref, atol=1e-10))
+    assert not (ok_closed and ok_sdpa)
