@@ -1,0 +1,181 @@
+"""Throughput of the sparse-MLA decode hot path on one MI355X.
+
+One step = the whole path for one batch: stable top-k per row over the indexer scores (with length
+clamping) -> canonical indices -> paged gather + MQA attention + split combine.  Workload: B=64
+decode rows, H=64 heads, top-k 2048, d_qk 576 (512 latent + 64 rope), d_v 512, bf16 KV in pages of
+64, context lengths uniform in [8192, 65536], random page tables.  Four independent (Q, scores) sets
+rotate over one 2.7 GB KV pool so a step's gathered set (151 MB) is not already cache-resident.
+
+Prints one JSON line.  `value` is rows/s of the whole step with every input resident in HBM;
+`roofline` reports the attention kernel's gathered-KV bandwidth against the 8 TB/s HBM peak;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same rows.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode rows/s + gathered-KV HBM GB/s (H=64, topk=2048, 1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+N_SETS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=128, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, n_rows):
+    """The oracle, as it is, on the first n_rows rows of the rotating sets (single BLAS thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.reference as O
+
+    kvh = wl.cache.kv.cpu().numpy()
+    bt = wl.cache.block_table.cpu().numpy()
+    done = 0
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for rs in wl.sets:
+            if done >= n_rows:
+                break
+            take = min(n_rows - done, rs.q.shape[0])
+            qb = rs.q[:take].contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+            sc = rs.scores[:take].cpu().numpy()
+            ln = rs.lengths[:take].cpu().numpy()
+            rq = rs.row_req[:take].cpu().numpy()
+            t0 = time.perf_counter()
+            O.decode_rows(qb, kvh, wl.cache.kv_dtype, bt, rq, sc, ln, wl.k, wl.scale)
+            t_total += time.perf_counter() - t0
+            done += take
+    return {"value": done / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows of the same workload (top-k + gather + attention, numpy fp64, 1 thread), "
+                      f"{t_total:.1f} s on {os.cpu_count()} host cores' machine"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
+              f"without any exchange, so the per-GPU figure is the one to read)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_mla_attention_topk_amd as smla
+    from sparse_mla_attention_topk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.decode_bf16(dev, n_sets=N_SETS)
+    B, H, k = wl.sets[0].q.shape[0], wl.H, wl.k
+    gathered = B * k * W.BF16_RECORD_BYTES            # every row has >= k candidates
+    flops = B * H * k * (576 + 512) * 2
+
+    ws = smla.attention_workspace(B, H, k, dev)
+    idx = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(N_SETS)]
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    def topk(i):
+        rs = wl.sets[i]
+        smla.topk_per_row(rs.scores, k, lengths=rs.lengths, out=idx[i])
+
+    def attn(i):
+        rs = wl.sets[i]
+        smla.sparse_mla_decode(rs.q, wl.cache.kv, wl.cache.block_table, idx[i], wl.scale, row_req=rs.row_req,
+                               out=out, lse=lse, workspace=ws)
+
+    for i in range(N_SETS):      # eager run first (also loads the kernels)
+        topk(i)
+        attn(i)
+    torch.cuda.synchronize()
+
+    if args.no_graph:
+        g_topk = [lambda i=i: topk(i) for i in range(N_SETS)]
+        g_attn = [lambda i=i: attn(i) for i in range(N_SETS)]
+    else:
+        g_topk, g_attn = [], []
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(s):
+            for i in range(N_SETS):
+                gt, ga = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gt, stream=s):
+                    topk(i)
+                with torch.cuda.graph(ga, stream=s):
+                    attn(i)
+                g_topk.append(gt.replay)
+                g_attn.append(ga.replay)
+        torch.cuda.current_stream(dev).wait_stream(s)
+        torch.cuda.synchronize()
+
+    for w in range(args.warmup):
+        g_topk[w % N_SETS]()
+        g_attn[w % N_SETS]()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for st in range(args.steps):
+        i = st % N_SETS
+        g_topk[i]()
+        ev[st][0].record()
+        g_attn[i]()
+        ev[st][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_begin.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    rows_per_s = B / (ms_step * 1e-3)
+    achieved = gathered / (attn_ms * 1e-3) / 1e9
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_rows > 0:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+
+    line = {
+        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "rows": B, "heads": H, "topk": k, "d_qk": 576, "d_v": 512,
+                   "page_block_size": 64, "kv": "bf16", "context": "uniform [8192, 65536]",
+                   "rotating_sets": N_SETS, "launch": "eager" if args.no_graph else "hip_graph_per_call"},
+        "gathered_kv_GBps": achieved,
+        "step_gathered_kv_GBps": gathered / (ms_step * 1e-3) / 1e9,
+        "attention_ms": attn_ms, "topk_and_gaps_ms": ms_step - attn_ms, "wall_s": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "sparse_mla_decode (attention + split combine)",
+                     "algorithmic_bytes_per_launch": gathered,
+                     "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

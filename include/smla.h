@@ -1,0 +1,160 @@
+/*
+ * smla.h — C ABI of the deterministic, batch-invariant sparse-MLA library for AMD MI355X (gfx950).
+ *
+ * Per query row the library
+ *   1. selects the top k of the row's indexer scores under a composite (score, index) order with a
+ *      stable tie-break                          [smla_topk_per_row]
+ *   2. emits the selected token positions in ascending order, padded with -1
+ *   3. gathers those latent-KV records from a paged cache
+ *   4. runs MQA attention in which every head reads the same 576-wide latent record
+ *      (512 latent + 64 rope; values are the first 512 entries), with one fixed reduction order
+ *                                                [smla_sparse_mla_decode, smla_sparse_mla_prefill_chunk]
+ * The result for a row never depends on the other rows of the call.
+ *
+ * Sources (pages by title, section):
+ *   - "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL" (vllm-project/vllm PR 54955),
+ *     sections "Deterministic sparse top-k" (composite score/index key, stable tie-break, canonical
+ *     index order before attention, persistent row-start buffers) and "Sparse MLA and FlashMLA"
+ *     (decode gathers the selected KV and runs the prefill attention path; prefill chunks each
+ *     request on its own; top-k width, gather capacity and workspaces come from model capacity;
+ *     length buffers are filled without a host sync).
+ *   - "[Bugfix] Make DSV4 sparse MLA work end-to-end for plain decode, MTP, and DSpark"
+ *     (vllm-project/vllm PR 51538), "What is fixed": lengths clamped to [0, stride] before any
+ *     decision, -1 padding of short rows, slot = block id * block size + offset, unsupported
+ *     shapes rejected at init with the missing parameter named.
+ *   - "[JJ] Preallocate DeepSeek V4 padded-query output" (local-inference-lab/vllm PR 671),
+ *     "Operation contract" / "Resulting behavior": caller-owned outputs, no hidden allocation,
+ *     shapes/dtypes/layouts validated before launch.
+ *
+ * Conventions for every entry point:
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library never allocates,
+ *     never frees and never synchronizes the host.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL means the null stream) and completes asynchronously.  Addresses may stay fixed across
+ *     HIP graph capture and replay; no call records a memset.
+ *   - Arguments are validated on the host before anything is enqueued.  On failure nothing is
+ *     enqueued, the status says which class of problem it is, and smla_last_error() names the
+ *     parameter and the supported values.
+ *   - Device-side values are guarded instead of trusted: lengths are clamped to [0, row_stride];
+ *     index entries < 0, request ids outside [0, num_reqs), positions past the block table and
+ *     page ids outside [0, num_pages) are treated as "no token" (they contribute nothing); nothing
+ *     is read outside the buffers described below.
+ *   - All offsets are 64-bit.
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent strides            */
+    SMLA_ERR_UNSUPPORTED = 2,   /* a shape parameter outside the compiled set (message names it) */
+    SMLA_ERR_WORKSPACE = 3,     /* workspace pointer missing or smaller than required            */
+    SMLA_ERR_ALIGNMENT = 4,     /* a pointer or stride violates the stated alignment             */
+    SMLA_ERR_CAPACITY = 5,      /* a size exceeds the capacity limits of this library            */
+    SMLA_ERR_HIP = 6            /* the HIP runtime reported an error while enqueueing            */
+} smla_status;
+
+typedef enum {
+    SMLA_KV_BF16 = 0,           /* record = 576 bf16 (1152 B): 512 latent then 64 rope           */
+    SMLA_KV_FP8_E4M3_G128 = 1   /* record = 656 B: 512 OCP e4m3fn codes | 4 fp32 scales (one per
+                                   128 latent entries, little endian) | 64 bf16 rope              */
+} smla_kv_dtype;
+
+/* Model capacity.  Workspace sizes derive from these numbers only, never from batch contents. */
+typedef struct {
+    int32_t max_rows;           /* most query rows one attention call carries (>= 1)              */
+    int32_t max_k;              /* largest top-k width                                            */
+    int32_t num_heads;          /* query heads H                                                  */
+    int32_t d_qk;               /* must be 576                                                    */
+    int32_t d_v;                /* must be 512                                                    */
+    int32_t page_block_size;    /* must be 64                                                     */
+    int64_t max_candidates;     /* longest score row (row_stride) top-k will see                  */
+    int32_t kv_dtype;           /* smla_kv_dtype                                                  */
+    int32_t reserved;           /* must be 0                                                      */
+} smla_capacity;
+
+/* Message for the last failing call on this host thread ("" if none).  Never NULL. */
+const char* smla_last_error(void);
+
+/* Library version string. */
+const char* smla_version(void);
+
+/* Init-time gate: SMLA_OK if the capacity is within what the compiled kernels support, else
+ * SMLA_ERR_UNSUPPORTED / SMLA_ERR_CAPACITY with the offending parameter and the supported set
+ * in smla_last_error().  Supported: num_heads a multiple of 16 in [16, 128]; d_qk 576; d_v 512;
+ * page_block_size 64; 1 <= max_k <= 16384; 1 <= max_candidates <= 2^31 - 1; max_rows >= 1. */
+smla_status smla_is_supported(const smla_capacity* cap);
+
+/* Workspace bytes the top-k and attention entry points need for this capacity (either output
+ * pointer may be NULL).  Workspaces must be 256-byte aligned.  A larger attention workspace lets
+ * one call carry more rows per launch; results do not depend on it. */
+smla_status smla_workspace_size(const smla_capacity* cap, size_t* topk_ws_bytes, size_t* attn_ws_bytes);
+
+/* A0, causal candidate counts of a prefill chunk:
+ *   lengths[t] = max(0, first_pos + t + 1), clamped to INT32_MAX, for t in [0, T).
+ * Query token t sits at position first_pos + t and may attend to positions 0..first_pos+t
+ * ("Negative indexer context lengths under MTP": never below 0).
+ * lengths: int32 [T] device buffer, 4-byte aligned.  T = 0 enqueues nothing. */
+smla_status smla_fill_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, void* stream);
+
+/* A1-A3, stable top-k with canonical order, one row per query row.
+ *   Row r's candidates are scores[off_r + j] for j in [0, L_r), where
+ *   off_r = row_offsets ? row_offsets[r] : r * row_stride   (element offsets, int64) and
+ *   L_r = clamp(lengths ? lengths[r] : row_stride, 0, row_stride).
+ *   Order: higher score first; equal scores (IEEE ==, so -0.0 == +0.0) by lower index; NaN after
+ *   every number, NaNs by lower index.  The first n_r = min(k, L_r) candidates in that order are
+ *   written to out_idx[r*k + 0 .. n_r) in ASCENDING index order, and out_idx[r*k + n_r .. k) = -1.
+ *   The result is a pure function of the row: bit-identical in any batch.
+ * scores: fp32, 4-byte aligned; row_offsets: int64 [rows] or NULL; lengths: int32 [rows] or NULL;
+ * out_idx: int32 [rows, k].  Requires 1 <= k <= 16384, 1 <= row_stride <= 2^31 - 1, rows >= 0.
+ * ws/ws_bytes: top-k workspace (may be NULL/0 when smla_workspace_size reports 0). */
+smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, int64_t row_stride,
+                              const int32_t* lengths, int32_t rows, int32_t k, int32_t* out_idx,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* A4-A11, sparse MLA attention over canonical indices (decode rows, or any mix of rows).
+ *   q:      bf16 [rows, H, 576], row r at q + r*q_row_stride elements (q_row_stride >= H*576,
+ *           multiple of 8); 16-byte aligned.
+ *   kv:     paged cache, [num_pages, 64, record] bytes per kv_dtype; 16-byte aligned.
+ *   block_table: int32 [num_reqs, bt_stride]; logical page p of request q is physical page
+ *           block_table[q*bt_stride + p].
+ *   row_req: int32 [rows] request id of each row, or NULL for "request 0".
+ *   idx:    int32 [rows, k] logical token positions (from smla_topk_per_row); entries < 0 skipped.
+ *   For row r and head h: s_j = softmax_scale * <q[r,h,:], K_j> over the 576 entries of each
+ *   listed token's record K_j; p = softmax over the listed tokens; out[r,h,:] = sum_j p_j K_j[0:512]
+ *   rounded to bf16 (RNE); lse[r,h] = natural-log log-sum-exp of s (fp32).  A row with no valid
+ *   token gets out = 0 and lse = -inf.  Slots are reduced in a fixed order that depends only on k:
+ *   the k slots are cut into ceil(k/512) splits, each split accumulates its tiles in slot order with
+ *   an fp32 online softmax, and the splits are combined in split order.
+ *   out: bf16 [rows, H, 512], 16-byte aligned; lse: fp32 [rows, H] or NULL.
+ *   ws: attention workspace (256-byte aligned) of at least the size smla_workspace_size reports for
+ *   a capacity with max_rows >= 1; rows beyond what it holds are processed in further launches.
+ * Requires H a multiple of 16 in [16, 128], 1 <= k <= 16384, rows >= 0, num_pages >= 1. */
+smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
+                                   int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                   int32_t num_reqs, const int32_t* row_req, const int32_t* idx,
+                                   int32_t rows, int32_t H, int32_t k, float softmax_scale,
+                                   void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill chunk of one request: T query rows that all read the request whose block table row is
+ * block_table_row (bt_len entries).  Same arithmetic and the same kernels as smla_sparse_mla_decode
+ * (row t of a chunk and the same row inside a mixed decode batch give bit-identical results). */
+smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, const void* kv,
+                                          int32_t kv_dtype, int64_t num_pages,
+                                          const int32_t* block_table_row, int64_t bt_len,
+                                          const int32_t* idx, int32_t T, int32_t H, int32_t k,
+                                          float softmax_scale, void* out, float* lse, void* ws,
+                                          size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

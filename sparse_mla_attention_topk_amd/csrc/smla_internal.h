@@ -1,0 +1,49 @@
+// Host-side launcher declarations shared between the C-ABI layer and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smla {
+
+// Geometry of the attention kernels (also used by the host to size workspaces).
+constexpr int kSplitSlots = 512;   // index slots reduced by one workgroup before the split combine
+constexpr int kHeadsPerBlock = 64; // heads handled by one workgroup (4 waves x 16)
+
+inline int attn_num_splits(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
+
+// Bytes of split partials per query row (0 when k fits one split).
+inline size_t attn_ws_bytes_per_row(int H, int k) {
+    const int S = attn_num_splits(k);
+    if (S <= 1) return 0;
+    return (size_t)S * (size_t)H * (size_t)(512 + 1) * sizeof(float);
+}
+
+struct AttnArgs {
+    const void* q;
+    int64_t q_row_stride;
+    const void* kv;
+    int kv_dtype;
+    int64_t num_pages;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int32_t num_reqs;
+    const int32_t* row_req;
+    const int32_t* idx;
+    int32_t rows;
+    int32_t H;
+    int32_t k;
+    float softmax_scale;
+    void* out;
+    float* lse;
+    void* ws;
+    size_t ws_bytes;
+};
+
+hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t row_stride,
+                       const int32_t* lengths, int32_t rows, int32_t k, int32_t* out, hipStream_t stream);
+hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,158 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host (before any HIP call) with a message naming the
+parameter."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mla_attention_topk_amd as smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "smla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return smla.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = _header_functions()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(declared) == sorted(smla.exported_symbols)
+
+
+def test_version_and_last_error(lib):
+    assert smla.version().startswith("smla")
+    assert isinstance(lib.smla_last_error(), bytes)
+
+
+def _cap(**kw):
+    base = dict(max_rows=64, max_k=2048, num_heads=64, max_candidates=65536)
+    base.update(kw)
+    return smla.Capacity.make(**base)
+
+
+def test_supported_capacity():
+    ok, msg = smla.is_supported(_cap())
+    assert ok, msg
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("num_heads", 8, "num_heads=8"),
+    ("num_heads", 72, "num_heads=72"),
+    ("num_heads", 256, "num_heads=256"),
+    ("d_qk", 512, "d_qk=512"),
+    ("d_v", 576, "d_v=576"),
+    ("page_block_size", 16, "page_block_size=16"),
+    ("max_k", 0, "max_k=0"),
+    ("max_k", 20000, "max_k=20000"),
+    ("max_candidates", 0, "max_candidates=0"),
+    ("max_rows", 0, "max_rows=0"),
+])
+def test_unsupported_capacity_names_the_parameter(field, value, needle):
+    cap = _cap()
+    setattr(cap, field, value)
+    ok, msg = smla.is_supported(cap)
+    assert not ok
+    assert needle in msg
+    if field in ("num_heads", "d_qk", "d_v", "page_block_size", "max_k"):
+        assert "supported" in msg
+
+
+def test_workspace_size_derives_from_capacity_only():
+    tk, at = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64))
+    assert tk == 0
+    assert at == 64 * 4 * 64 * 513 * 4          # rows x splits x heads x (512 + 1) fp32
+    _, at1 = smla.workspace_size(_cap(max_rows=1, max_k=512, num_heads=64))
+    assert at1 == 0                              # a single split needs no partials
+    _, at2 = smla.workspace_size(_cap(max_rows=3, max_k=513, num_heads=16))
+    assert at2 == 3 * 2 * 16 * 513 * 4
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_topk_validation(lib):
+    f = lib.smla_topk_per_row
+    st = f(_fake(0x1000), None, 100, None, 4, 0, _fake(0x2000), None, 0, None)
+    assert st == 2 and b"k=0" in lib.smla_last_error()
+    st = f(_fake(0x1000), None, 0, None, 4, 8, _fake(0x2000), None, 0, None)
+    assert st == 5 and b"row_stride=0" in lib.smla_last_error()
+    st = f(_fake(0x1000), None, 100, None, -1, 8, _fake(0x2000), None, 0, None)
+    assert st == 1 and b"rows=-1" in lib.smla_last_error()
+    st = f(None, None, 100, None, 4, 8, _fake(0x2000), None, 0, None)
+    assert st == 1 and b"scores is NULL" in lib.smla_last_error()
+    st = f(_fake(0x1002), None, 100, None, 4, 8, _fake(0x2000), None, 0, None)
+    assert st == 4 and b"scores" in lib.smla_last_error()
+    st = f(_fake(0x1000), _fake(0x3004), 100, None, 4, 8, _fake(0x2000), None, 0, None)
+    assert st == 4 and b"row_offsets" in lib.smla_last_error()
+    # zero rows is a valid no-op that touches nothing
+    assert f(None, None, 100, None, 0, 8, None, None, 0, None) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=0x10000, q_row_stride=64 * 576, kv=0x20000, kv_dtype=0, num_pages=10, bt=0x30000, bt_stride=4,
+             num_reqs=1, row_req=None, idx=0x40000, rows=2, H=64, k=2048, scale=1 / 24, out=0x50000, lse=None,
+             ws=0x60000, ws_bytes=1 << 30)
+    a.update(kw)
+    c = lambda v: None if v is None else _fake(v)
+    return lib.smla_sparse_mla_decode(c(a["q"]), a["q_row_stride"], c(a["kv"]), a["kv_dtype"], a["num_pages"],
+                                      c(a["bt"]), a["bt_stride"], a["num_reqs"], c(a["row_req"]), c(a["idx"]),
+                                      a["rows"], a["H"], a["k"], a["scale"], c(a["out"]), c(a["lse"]), c(a["ws"]),
+                                      a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(H=24), 2, b"num_heads=24"),
+    (dict(k=0), 2, b"k=0"),
+    (dict(kv_dtype=7), 2, b"kv_dtype=7"),
+    (dict(rows=-3), 1, b"rows=-3"),
+    (dict(num_pages=0), 1, b"num_pages=0"),
+    (dict(num_pages=1 << 40), 5, b"num_pages="),
+    (dict(scale=0.0), 1, b"softmax_scale"),
+    (dict(scale=float("nan")), 1, b"softmax_scale"),
+    (dict(q_row_stride=100), 1, b"q_row_stride=100"),
+    (dict(q=None), 1, b"q is NULL"),
+    (dict(idx=None), 1, b"idx is NULL"),
+    (dict(q=0x10008), 4, b"q must be 16-byte aligned"),
+    (dict(q_row_stride=64 * 576 + 4), 4, b"q_row_stride"),
+    (dict(out=0x50004), 4, b"out must be 16-byte aligned"),
+    (dict(ws=None), 3, b"ws is NULL"),
+    (dict(ws_bytes=100), 3, b"ws_bytes=100"),
+    (dict(ws=0x60010), 4, b"ws must be 256-byte aligned"),
+])
+def test_decode_validation(lib, kw, status, needle):
+    st = _decode(lib, **kw)
+    assert st == status, lib.smla_last_error()
+    assert needle in lib.smla_last_error()
+
+
+def test_decode_zero_rows_is_noop(lib):
+    assert _decode(lib, rows=0, q=None, idx=None, out=None) == 0
+
+
+def test_single_split_needs_no_workspace(lib):
+    # k <= 512 is one split: no workspace pointer needed; validation passes up to the launch, which is
+    # not reached here because rows=0.
+    assert _decode(lib, k=512, ws=None, ws_bytes=0, rows=0) == 0
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        smla.topk_per_row(torch.zeros((2, 8)), 2)

@@ -1,0 +1,141 @@
+"""GPU parity of sparse_mla_decode (and the top-k feeding it) against the fp64 oracle, plus
+bit-identity of a row alone vs in any batch."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as O
+import sparse_mla_attention_topk_amd as smla
+from sparse_mla_attention_topk_amd import workloads as W
+from tests.helpers import assert_attention_close, bf16_bits_np, bits_equal, kv_np, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(wl, rs, idx=None, row_req=None, q=None):
+    if idx is None:
+        idx = smla.topk_per_row(rs.scores, wl.k, lengths=rs.lengths)
+    q = rs.q if q is None else q
+    lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_decode(q, wl.cache.kv, wl.cache.block_table, idx, wl.scale,
+                                    row_req=rs.row_req if row_req is None else row_req, lse=lse)
+    torch.cuda.synchronize()
+    return idx, out, lse
+
+
+def _oracle_rows(wl, rs, rows, kv_host=None):
+    kvh = kv_np(wl.cache.kv) if kv_host is None else kv_host
+    return O.decode_rows(bf16_bits_np(rs.q), kvh, wl.cache.kv_dtype, wl.cache.block_table.cpu().numpy(),
+                         rs.row_req.cpu().numpy(), rs.scores.cpu().numpy(), rs.lengths.cpu().numpy(), wl.k,
+                         wl.scale, rows=rows)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return W.tiny_decode(DEV)
+
+
+@pytest.fixture(scope="module")
+def big():
+    log("[decode] building B=64 H=64 k=2048 bf16 workload")
+    wl = W.decode_bf16(DEV)
+    return wl, kv_np(wl.cache.kv)
+
+
+def test_tiny_decode_parity(tiny):
+    rs = tiny.sets[0]
+    idx, out, lse = _run(tiny, rs)
+    ref_idx, O_ref, lse_ref = _oracle_rows(tiny, rs, [0, 1])
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, "tiny")
+    log(f"[decode] tiny {st}")
+
+
+def test_full_size_decode_sampled_rows(big):
+    wl, kvh = big
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    rows = sample_rows(64, 8, 11)
+    ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, rows, kvh)
+    assert np.array_equal(idx.cpu().numpy()[rows], ref_idx)
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, "B64 H64 k2048")
+    log(f"[decode] full-size sampled {st}")
+
+
+def test_full_size_batch_invariance(big):
+    """Each row alone, the batch shuffled, and a repeat must reproduce the batch output bit for bit."""
+    wl, _ = big
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    for r in [0, 31, 63]:
+        _, o1, l1 = _run(wl, rs, idx=idx[r:r + 1].contiguous(), row_req=rs.row_req[r:r + 1].contiguous(),
+                         q=rs.q[r:r + 1].contiguous())
+        assert bits_equal(o1[0], out[r]) and bits_equal(l1[0], lse[r]), r
+    g = torch.Generator(device=DEV).manual_seed(3)
+    perm = torch.randperm(64, generator=g, device=DEV)
+    _, o2, l2 = _run(wl, rs, idx=idx[perm].contiguous(), row_req=rs.row_req[perm].contiguous(),
+                     q=rs.q[perm].contiguous())
+    assert bits_equal(o2, out[perm]) and bits_equal(l2, lse[perm])
+    sub = perm[:7]
+    _, o3, l3 = _run(wl, rs, idx=idx[sub].contiguous(), row_req=rs.row_req[sub].contiguous(),
+                     q=rs.q[sub].contiguous())
+    assert bits_equal(o3, out[sub]) and bits_equal(l3, lse[sub])
+    for _ in range(3):
+        _, o4, l4 = _run(wl, rs, idx=idx)
+        assert bits_equal(o4, out) and bits_equal(l4, lse)
+
+
+@pytest.mark.parametrize("H,k", [(16, 1), (16, 192), (32, 700), (48, 513), (64, 1024), (128, 2048), (64, 2500)])
+def test_heads_and_widths(H, k):
+    """Head counts 16..128 (two head blocks at 128) and widths that leave ragged tiles and splits."""
+    wl = W.decode_workload(f"hk_{H}_{k}", B=5, H=H, k=k, ctx_lo=max(1, k // 2), ctx_hi=3 * k + 70,
+                           kv_dtype=W.KV_BF16, seed=100 + H + k, device=DEV, score_kind="eighths")
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, list(range(5)))
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, f"H={H} k={k}")
+    log(f"[decode] H={H} k={k} {st}")
+
+
+def test_short_empty_and_invalid_slots():
+    """Rows with fewer candidates than k (-1 tail), an empty row, -1 holes in the middle, positions
+    past the block table, a bad request id: invalid slots contribute nothing; empty rows give 0/-inf."""
+    wl = W.decode_workload("edge", B=6, H=64, k=1024, ctx_lo=100, ctx_hi=3000, kv_dtype=W.KV_BF16, seed=77,
+                           device=DEV)
+    rs = wl.sets[0]
+    lens = rs.lengths.clone()
+    lens[0] = 0            # empty row
+    lens[1] = 37           # far fewer than k
+    lens[2] = 1000         # just under k
+    idx = smla.topk_per_row(rs.scores, wl.k, lengths=lens)
+    idx_h = idx.cpu().numpy().copy()
+    idx_h[3, 5:400:3] = -1                               # holes
+    idx_h[4, 10] = 10 ** 7                               # past the block table -> skipped
+    idx = torch.from_numpy(idx_h).to(DEV)
+    row_req = rs.row_req.clone()
+    row_req[5] = 999                                     # no such request -> empty row
+    _, out, lse = _run(wl, rs, idx=idx, row_req=row_req)
+    kvh = kv_np(wl.cache.kv)
+    bt = wl.cache.block_table.cpu().numpy()
+    idx_o = idx_h.copy()
+    idx_o[4, 10] = -1
+    idx_o[5, :] = -1
+    req = row_req.cpu().numpy().copy()
+    req[5] = 0
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(rs.q), kvh, W.KV_BF16, bt, req, idx_o, wl.scale)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, "edge rows")
+    assert (out[0].float() == 0).all() and torch.isneginf(lse[0]).all()
+    assert (out[5].float() == 0).all() and torch.isneginf(lse[5]).all()
+    log(f"[decode] edge {st}")
+
+
+def test_poisoned_pages_never_read():
+    """The cache's null page and the slots past each context are NaN; every output stays finite."""
+    wl = W.decode_workload("poison", B=8, H=32, k=256, ctx_lo=65, ctx_hi=700, kv_dtype=W.KV_BF16, seed=5,
+                           device=DEV)
+    rs = wl.sets[0]
+    _, out, lse = _run(wl, rs)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()

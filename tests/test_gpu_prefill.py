@@ -1,0 +1,91 @@
+"""Prefill chunk (4096 query tokens at positions 126976..131071 of a 131072-token context, causal)
+against the oracle on sampled rows, and bit-identity of those rows inside a mixed batch with 63
+decode rows."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as O
+import sparse_mla_attention_topk_amd as smla
+from sparse_mla_attention_topk_amd import workloads as W
+from tests.helpers import assert_attention_close, bf16_bits_np, bits_equal, kv_np, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def pf():
+    log("[prefill] building T=4096 ctx=131072 workload")
+    wl = W.prefill_chunk(DEV)
+    T = wl.q.shape[0]
+    lengths = smla.fill_causal_lengths(wl.first_pos, T, device=DEV)
+    idx = smla.topk_per_row(wl.scores, wl.k, lengths=lengths)
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_prefill_chunk(wl.q, wl.cache.kv, wl.cache.block_table[0].contiguous(), idx, wl.scale,
+                                           lse=lse)
+    torch.cuda.synchronize()
+    return wl, lengths, idx, out, lse
+
+
+def test_causal_lengths(pf):
+    wl, lengths, _, _, _ = pf
+    assert np.array_equal(lengths.cpu().numpy(), O.causal_lengths(wl.first_pos, wl.q.shape[0]))
+
+
+def test_prefill_sampled_rows_match_oracle(pf):
+    wl, lengths, idx, out, lse = pf
+    T = wl.q.shape[0]
+    rows = sorted(set(sample_rows(T, 24, 4) + [0, T - 1]))
+    scores_rows = wl.scores[rows].cpu().numpy()
+    ref_idx = O.topk_rows(scores_rows, lengths.cpu().numpy()[rows], wl.k)
+    assert np.array_equal(idx.cpu().numpy()[rows], ref_idx)
+    kvh = kv_np(wl.cache.kv)
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(wl.q[rows]), kvh, W.KV_BF16, wl.cache.block_table.cpu().numpy(),
+                                      [0] * len(rows), ref_idx, wl.scale)
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, "prefill")
+    log(f"[prefill] sampled {st}")
+
+
+def test_mixed_batch_bit_identical(pf):
+    """The prefill rows, rerun inside one batch with 63 decode rows at random positions (top-k and
+    attention both), give the same bits as the prefill-only run; the decode rows give the same bits
+    as a decode-only run."""
+    wl, lengths, idx, out, lse = pf
+    T = wl.q.shape[0]
+    dec = wl.decode
+    n_dec = dec.q.shape[0]
+    stride = wl.scores.shape[1]
+    # one score buffer holding the prefill rows followed by the decode rows
+    buf = torch.full((T + n_dec, stride), float("inf"), dtype=torch.float32, device=DEV)
+    buf[:T] = wl.scores
+    buf[T:, :dec.scores.shape[1]] = dec.scores
+    order = wl.mix_order.to(DEV)                        # mixed slot -> source row
+    offs = order.to(torch.int64) * stride
+    all_len = torch.cat([lengths, dec.lengths])
+    mlen = all_len[order].contiguous()
+    midx = smla.topk_per_row(buf, wl.k, lengths=mlen, row_offsets=offs, row_stride=stride)
+    all_q = torch.cat([wl.q, dec.q])
+    mq = all_q[order].contiguous()
+    all_req = torch.cat([torch.zeros(T, dtype=torch.int32, device=DEV), dec.row_req])
+    mreq = all_req[order].contiguous()
+    mlse = torch.empty((T + n_dec, wl.H), dtype=torch.float32, device=DEV)
+    mout, _ = smla.sparse_mla_decode(mq, wl.cache.kv, wl.cache.block_table, midx, wl.scale, row_req=mreq, lse=mlse)
+    # decode-only reference run
+    didx = smla.topk_per_row(dec.scores, wl.k, lengths=dec.lengths)
+    dlse = torch.empty((n_dec, wl.H), dtype=torch.float32, device=DEV)
+    dout, _ = smla.sparse_mla_decode(dec.q, wl.cache.kv, wl.cache.block_table, didx, wl.scale, row_req=dec.row_req,
+                                     lse=dlse)
+    torch.cuda.synchronize()
+    is_pf = order < T
+    src = order.clone()
+    pf_slots = torch.nonzero(is_pf).flatten()
+    dec_slots = torch.nonzero(~is_pf).flatten()
+    assert torch.equal(midx[pf_slots], idx[src[pf_slots]])
+    assert torch.equal(midx[dec_slots], didx[src[dec_slots] - T])
+    assert bits_equal(mout[pf_slots], out[src[pf_slots]])
+    assert bits_equal(mlse[pf_slots], lse[src[pf_slots]])
+    assert bits_equal(mout[dec_slots], dout[src[dec_slots] - T])
+    assert bits_equal(mlse[dec_slots], dlse[src[dec_slots] - T])
+    log(f"[prefill] mixed batch of {T + n_dec} rows bit-identical")

@@ -1,0 +1,119 @@
+"""GPU parity of topk_per_row against the oracle: bit-exact int32 indices (there is exactly one
+correct result), at the workload shapes and on edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as O
+import sparse_mla_attention_topk_amd as smla
+from sparse_mla_attention_topk_amd import workloads as W
+from tests.helpers import log, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _oracle(scores_cpu: np.ndarray, lengths, k, rows=None):
+    return O.topk_rows(scores_cpu, lengths, k, rows=rows)
+
+
+def _check(scores: torch.Tensor, lengths, k: int, rows=None, what=""):
+    log(f"[topk] {what}: {tuple(scores.shape)} k={k}")
+    got = smla.topk_per_row(scores, k, lengths=lengths)
+    torch.cuda.synchronize()
+    s_np = scores.cpu().numpy()
+    l_np = None if lengths is None else lengths.cpu().numpy()
+    sel = list(range(scores.shape[0])) if rows is None else rows
+    ref = _oracle(s_np, l_np, k, rows=sel)
+    g = got.cpu().numpy()[sel]
+    bad = np.nonzero((g != ref).any(axis=1))[0]
+    assert bad.size == 0, f"{what}: rows {[sel[i] for i in bad[:5]]} differ"
+
+
+def test_tiny_decode_scores_with_ties():
+    wl = W.tiny_decode(DEV)
+    rs = wl.sets[0]
+    _check(rs.scores, rs.lengths, wl.k, what="tiny eighths")
+
+
+def test_topk_alone_256_levels():
+    s = W.topk_levels(DEV)
+    _check(s, None, 2048, what="64x65536 levels=256")
+
+
+def test_decode_shape_rows():
+    g = torch.Generator(device=DEV).manual_seed(22)
+    lens = W.uniform_int(8192, 65536, 64, g, DEV).to(torch.int32)
+    s = torch.randn((64, 65536), generator=g, device=DEV)
+    W.poison_score_tails(s, lens)
+    _check(s, lens, 2048, what="64 rows L~U[8K,64K]")
+
+
+def test_fp8_decode_shape_rows_sampled():
+    g = torch.Generator(device=DEV).manual_seed(33)
+    lens = W.uniform_int(32768, 131072, 128, g, DEV).to(torch.int32)
+    s = torch.randn((128, 131072), generator=g, device=DEV)
+    W.poison_score_tails(s, lens)
+    _check(s, lens, 2048, rows=sample_rows(128, 48, 3), what="128 rows L~U[32K,128K]")
+
+
+@pytest.mark.parametrize("k", [1, 2, 63, 192, 256, 2000, 2048, 4096, 16384])
+def test_k_values_and_ragged_lengths(k):
+    g = torch.Generator(device=DEV).manual_seed(1000 + k)
+    R, stride = 24, 20000
+    lens = torch.tensor([0, -5, 1, k - 1, k, k + 1, 2 * k + 3, stride, stride + 99, 2**31 - 1, 777, 12345,
+                         19999, 5, 64, 65, 1023, 1024, 1025, 3000, 4097, 8191, 16385, 100], dtype=torch.int32)
+    lens = lens[:R].to(DEV)
+    s = torch.round(torch.randn((R, stride), generator=g, device=DEV) * 4) / 4     # ties
+    _check(s, lens, k, what=f"ragged k={k}")
+
+
+def test_special_values_rows():
+    g = torch.Generator(device=DEV).manual_seed(7)
+    R, L = 8, 5000
+    s = torch.randn((R, L), generator=g, device=DEV)
+    s[0] = 3.0                                                   # all equal
+    s[1, ::3] = float("nan")                                     # NaNs rank last
+    s[2, ::7] = float("inf"); s[2, 1::7] = float("-inf")         # infinities
+    s[3] = 0.0; s[3, ::2] = -0.0                                 # -0 == +0
+    s[4] = torch.arange(L, device=DEV, dtype=torch.float32)      # increasing
+    s[5] = -torch.arange(L, device=DEV, dtype=torch.float32)     # decreasing
+    s[6] = float("nan")                                          # all NaN
+    s[7, :] = torch.round(s[7] * 2) / 2
+    _check(s, None, 700, what="special values")
+
+
+def test_row_offsets_unaligned_and_shared_buffer():
+    """Rows addressed through arbitrary (unaligned) element offsets into one buffer, two rows
+    sharing storage, and a row repeated: all rows must match the oracle on their own slice."""
+    g = torch.Generator(device=DEV).manual_seed(9)
+    buf = torch.randn(300001, generator=g, device=DEV)
+    offs = torch.tensor([0, 1, 3, 12345, 12346, 250001, 3, 99999], dtype=torch.int64, device=DEV)
+    stride = 50000
+    lens = torch.tensor([50000, 49999, 300, 40000, 17, 50000, 300, 2049], dtype=torch.int32, device=DEV)
+    got = smla.topk_per_row(buf, 2048, lengths=lens, row_offsets=offs, row_stride=stride)
+    torch.cuda.synchronize()
+    ref = O.topk_rows(buf.cpu().numpy(), lens.cpu().numpy(), 2048, row_offsets=offs.cpu().numpy(),
+                      row_stride=stride)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_row_alone_equals_row_in_batch():
+    g = torch.Generator(device=DEV).manual_seed(5)
+    s = torch.round(torch.randn((16, 30000), generator=g, device=DEV) * 8) / 8
+    lens = torch.randint(0, 30001, (16,), generator=g, device=DEV, dtype=torch.int32)
+    full = smla.topk_per_row(s, 1024, lengths=lens)
+    for r in [0, 7, 15]:
+        alone = smla.topk_per_row(s[r:r + 1].contiguous(), 1024, lengths=lens[r:r + 1].contiguous())
+        assert torch.equal(alone[0], full[r])
+    perm = torch.randperm(16, generator=g, device=DEV)
+    shuffled = smla.topk_per_row(s[perm].contiguous(), 1024, lengths=lens[perm].contiguous())
+    assert torch.equal(shuffled, full[perm])
+
+
+def test_causal_lengths_match_oracle():
+    for first_pos, T in [(-2, 2), (98, 2), (126976, 4096), (0, 1), (-5000, 3000), (2**31 - 10, 20)]:
+        got = smla.fill_causal_lengths(first_pos, T, device=DEV).cpu().numpy()
+        ref = np.minimum(O.causal_lengths(first_pos, T), 2**31 - 1)
+        assert np.array_equal(got, ref), (first_pos, T)
