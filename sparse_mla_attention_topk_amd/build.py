@@ -36,6 +36,9 @@ def common_flags() -> list:
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         # keep packed-fp32 instructions out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in arch VGPRs: the rare online-softmax rescale then multiplies them in
+        # place, and Q (the other MFMA operand) stays in AGPRs
+        "-mllvm", "--amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
         "-Wall", "-Wno-unused-result",
     ]

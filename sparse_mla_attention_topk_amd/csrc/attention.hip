@@ -81,13 +81,36 @@ struct AttnParams {
     float* ws_lse;
 };
 
+// One direct-to-LDS 16-byte load: lane l's 16 bytes at `g` land at LDS byte lds_base + 16 l.  Issued
+// as inline assembly so that the compiler does not pair every later LDS read with a wait for all
+// outstanding loads; the kernel waits for these loads itself (wait_vmcnt before each barrier).
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// The running max of a head only moves when a tile's max exceeds it by more than this (log2
+// units); in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
+constexpr float kRescaleSlack = 8.f;
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier and the operand prefetch depths.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kQkAhead = 4;   // score steps (2 reads each) in flight ahead of their MFMAs
+constexpr int kPvAhead = 6;   // value dim-blocks (2 transposed reads each) in flight
+
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
     __shared__ uint32_t phys[kSplitSlots];
     __shared__ uint32_t tile_valid[kTilesPerSplit];
     __shared__ int s_first, s_last;
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     // Work item: consecutive items (the splits / head blocks of one row) go to the same XCD, since
     // workgroups are dispatched round-robin over the 8 XCDs.
@@ -140,23 +163,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) qv[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
     }
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qv[kk]));   // Q lives in AGPRs (MFMA B operand)
+    // Drain every compiler-visible global load here: inside the tile loop the only outstanding
+    // vector-memory operations are the tile loads, which the loop waits for explicitly.
+    wait_vmcnt<0>();
 
     // ---- A5: gather.  Wave w fills tile-local tokens [8w, 8w+8) of a stage: load i of lane l covers
-    // LDS bytes w*9216 + 1024 i + 16 l, i.e. token 8w + (64i + l) / 72, 16-byte position (64i + l) % 72.
-    auto issue_tile = [&](int tile, int stage) {
-        uint8_t* wbase = ring + stage * kStageBytes + wid * kWaveTileBytes;
+    // LDS bytes w*9216 + 1024 i + 16 l, i.e. token 8w + (64i + l) / 72, 16-byte position (64i + l) % 72,
+    // which holds the record's chunk swz_pos(position, swz_key(token)) (the swizzle is an involution).
+    const uint32_t ring_lds = lds_offset(ring);
+    const uint32_t wave_lds = ring_lds + (uint32_t)wid * kWaveTileBytes;
+    auto issue_tile = [&](int tile, int stage, int ln) {
+        const uint32_t m0 = wave_lds + (uint32_t)stage * kStageBytes;
+        const uint8_t* src[kLoadsPerWave];
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int qd = kWave * i + lane;
+        for (int i = 0; i < kLoadsPerWave; ++i) {   // all slot reads first: the asm below is a compiler barrier
+            const int qd = kWave * i + ln;
             const int tt = qd / 72;
-            const int pos = qd - 72 * tt;
             const int t = 8 * wid + tt;
             uint32_t ph = phys[tile * kTileTok + t];
-            if (ph == kNoToken) ph = dummy;
-            const int c = swz_pos(pos, swz_key(t));   // the swizzle is an involution
-            const uint8_t* src = p.kv + (int64_t)ph * kBf16Record + c * 16;
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(wbase + 1024 * i), 16, 0, 0);
+            ph = ph == kNoToken ? dummy : ph;
+            src[i] = p.kv + (uint64_t)ph * kBf16Record + 16u * (uint32_t)swz_pos(qd - 72 * tt, swz_key(t));
         }
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) dma_b128(src[i], m0 + 1024u * i);
     };
     // Zero this wave's records of invalid slots (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
@@ -172,23 +203,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         }
     };
 
-    float m_run = -INFINITY, l_run = 0.f;
+    // Per-lane LDS byte offsets inside a stage (computed in the loop):
+    //  score operand: token (lane & 15) of a 16-token block, chunk 4kk + g  ->  kb[kk & 3] + 256 (kk >> 2)
+    //  for kk < 16, kr[kk - 16] for the two rope steps.
+    //  transposed value reads: lane supplies row (token) 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3
+    //  of a 16-dim block, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1)  ->  vb[db & 7] + 256 (db >> 3).
+    const int g = lane >> 4;
+    float m_run = -INFINITY, l_run = 0.f;   // exp2-domain reference max and weight sum (this lane's tokens)
     f32x4_t oacc[32];
 #pragma unroll
     for (int d = 0; d < 32; ++d) oacc[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    // Per-lane LDS offsets.  Score operand: token (lane & 15) of a 16-token block, chunk 4kk + g.
-    const int g = lane >> 4;
-    const int fa = swz_key(lane & 15);
-    const int a_row = (lane & 15) * kBf16Record;
-    // Transposed value reads: lane supplies row (token) 4g + ((lane & 15) >> 2), dims 4(lane & 3)..+3
-    // of a 16-dim block, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1).
-    const int tv = 4 * g + ((lane & 15) >> 2);
-    const int fv = swz_key(tv);
-    const int v_row = tv * kBf16Record + 8 * (lane & 1);
-    const int v_half = (lane >> 1) & 1;
-
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
+    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t, lane);
 
     for (int it = 0; it < ntiles; ++it) {
         const int stage = it % kStages;
@@ -199,56 +225,77 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         zero_invalid(it, stage);
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();   // tile `it` visible; every wave is done with tile it-1
-        if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        // Per-lane constants are recomputed every tile from an opaque copy of the lane id: keeping them
+        // live across the loop would leave no registers for operand prefetch.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages, ln);
         if (!has_heads) continue;
+        const int g = ln >> 4;
+        const int fa = swz_key(ln & 15);
+        const int tv = 4 * g + ((ln & 15) >> 2);
+        const int fv = swz_key(tv);
+        uint32_t kb[4], kr[2], vb[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kb[j] = (ln & 15) * kBf16Record + 16 * ((4 * j + g) ^ fa);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) kr[j] = (ln & 15) * kBf16Record + 16 * (64 + ((4 * j + g) ^ (fa & 7)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vb[j] = tv * kBf16Record + 8 * (ln & 1) + 16 * ((2 * j + ((ln >> 1) & 1)) ^ fv);
 
         const uint8_t* sb = ring + stage * kStageBytes;
         const uint32_t vmask = tile_valid[it];
 
-        // ---- A7: scores, two 16-token blocks ----
-        f32x4_t sacc[2];
+        // ---- A7: scores S^T[32 tok x 16 heads] as two 16-token blocks ----
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* rp = sb + tb * 16 * kBf16Record + a_row;
-#pragma unroll
-            for (int kk = 0; kk < 18; ++kk) {
-                const int c = 4 * kk + g;
-                const bf16x8_t a = *(const bf16x8_t*)(rp + 16 * swz_pos(c, fa));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[kk], acc, 0, 0, 0);
-            }
-            sacc[tb] = acc;
+        for (int kk = 0; kk < 18; ++kk) {
+            const uint32_t off = kk < 16 ? kb[kk & 3] + 256u * (kk >> 2) : kr[kk - 16];
+            const bf16x8_t a0 = *(const bf16x8_t*)(sb + off);
+            const bf16x8_t a1 = *(const bf16x8_t*)(sb + off + 16 * kBf16Record);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
         }
+        // Schedule: operand reads run kQkAhead steps ahead of the MFMAs that consume them.
+#pragma unroll
+        for (int i = 0; i < kQkAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 18 - kQkAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kQkAhead, 0);
 
         // ---- A8: online softmax (lane: head lane & 15, tokens 16tb + 4g + i) ----
         float sv[8];
         float mt = -INFINITY;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * tb + 4 * g + i;
-                const float x = ((vmask >> tok) & 1u) ? sacc[tb][i] * p.scale_log2 : -INFINITY;
-                sv[4 * tb + i] = x;
-                mt = fmaxf(mt, x);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = ((vmask >> (4 * g + i)) & 1u) ? s0[i] * p.scale_log2 : -INFINITY;
+            const float x1 = ((vmask >> (16 + 4 * g + i)) & 1u) ? s1[i] * p.scale_log2 : -INFINITY;
+            sv[i] = x0;
+            sv[4 + i] = x1;
+            mt = fmaxf(mt, fmaxf(x0, x1));
+        }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        float psum = 0.f;
+        // The reference max moves only if this tile's max exceeds it by more than the slack; the
+        // decision is a function of the row's own scores, so it is identical in every batch.
+        if (mt > m_run + kRescaleSlack) {
+            const float alpha = exp2f(m_run - mt);   // 0 while nothing has been accumulated
+            m_run = mt;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < 32; ++d) {
+                oacc[d][0] *= alpha; oacc[d][1] *= alpha; oacc[d][2] *= alpha; oacc[d][3] *= alpha;
+            }
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float pw[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             pw[j] = exp2f(sv[j] - m_use);
-            psum += pw[j];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) {
-            oacc[d][0] *= alpha; oacc[d][1] *= alpha; oacc[d][2] *= alpha; oacc[d][3] *= alpha;
+            l_run += pw[j];
         }
         union { bf16x8_t v; uint32_t u[4]; } pb;
         pb.u[0] = pack_bf16x2(pw[0], pw[1]);
@@ -257,20 +304,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         pb.u[3] = pack_bf16x2(pw[6], pw[7]);
 
         // ---- A9: O^T += V^T P^T over 32 dim blocks ----
-        const uint8_t* vp0 = sb + v_row;
-        const uint8_t* vp1 = vp0 + 16 * kBf16Record;
 #pragma unroll
         for (int db = 0; db < 32; ++db) {
-            const int off = 16 * ((2 * db + v_half) ^ fv);
+            const uint8_t* vp = sb + vb[db & 7] + 256u * (db >> 3);
             union { bf16x8_t v; i16x4_t h[2]; } va;
-            va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp0 + off));
-            va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp1 + off));
+            va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
+            va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb.v, oacc[db], 0, 0, 0);
         }
+#pragma unroll
+        for (int i = 0; i < kPvAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 32 - kPvAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
     }
 
     // ---- A10: epilogue (lane: head h0 + (lane & 15), dims 16db + 4g + i) ----
     if (!has_heads) return;
+    // Lanes of one head share m_run (the tile max is reduced over them), so their sums add directly.
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot = l_tot + __shfl_xor(l_tot, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
