@@ -40,7 +40,7 @@ def common_flags() -> list:
         # place, and Q (the other MFMA operand) stays in AGPRs
         "-mllvm", "--amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
-        "-Wall", "-Wno-unused-result",
+        "-Wall", "-Wno-unused-result", "-Wno-inline-asm",
     ]
 
 

@@ -10,27 +10,35 @@
 //
 // Work decomposition.  One workgroup (4 waves) owns one (row, split, 64-head block).  A split is
 // 512 consecutive index slots; the number of splits depends on k only, so the reduction order of a
-// row never depends on the batch.  Wave w owns heads [16w, 16w+16) of the block and keeps
-//   * Q for its 16 heads in VGPRs (the B operand of the score MFMA, 18 x bf16x8),
-//   * the output accumulator O^T [512 dims x 16 heads] in 32 MFMA tiles (AGPRs),
-//   * a running max / sum per head (exp2 domain).
-// The split's slots are processed in tiles of 32 tokens through a 4-stage LDS ring: each wave
-// gathers 8 token records per tile with direct-to-LDS 16-byte loads (global_load_lds_dwordx4), so
-// three tiles are in flight while one is consumed.  Records are stored unpadded (1152 B) with the
-// 16-byte chunks of token t XOR-swizzled by f(t); the swizzle makes both operand reads below
-// bank-conflict free.
-//   scores:  S^T[16 tok x 16 heads] = K[16 tok x 576] . Q^T   (A = K rows from LDS via ds_read_b128)
-//   values:  O^T[16 dims x 16 heads] += V^T[16 dims x 32 tok] . P^T[32 tok x 16 heads]
-//            (A = V^T via ds_read_b64_tr_b16 transposed LDS reads, B = P straight from the score
-//             accumulators: the S^T layout already puts a head's 8 token weights in one lane)
-// Softmax is an fp32 online softmax in the exp2 domain, tiles in slot order.  A split that is not
-// the only one writes its normalized partial (O_s, lse_s) to the workspace and a combine kernel
-// merges the splits of a row in split order.  Nothing uses floating-point atomics.
+// row never depends on the batch.  The split's slots are processed in tiles of 32 tokens through a
+// 4-stage LDS ring: each wave gathers 8 token records per tile with direct-to-LDS 16-byte loads
+// (global_load_lds_dwordx4), so three tiles are in flight while one is consumed.  Records are
+// stored unpadded (1152 B); the 16-byte chunks of tile-local token t are XOR-swizzled with
+// f(t) = (t >> 1) & 7, the mapping measured to keep both operand read patterns below free of LDS
+// bank conflicts on gfx950.
+//
+// Waves pair up on 32 heads.  Wave w computes scores for its own 16 heads with Q in AGPRs:
+//   S^T[16 tok x 16 heads] = K[16 tok x 576] . Q^T        (A = K rows via ds_read_b128)
+// keeps the online-softmax state of those heads, and publishes its bf16 weights P (one 16-byte
+// fragment per lane) to its partner through LDS.  Each wave then accumulates the values for BOTH
+// head blocks of the pair over one half of the 512 value dims:
+//   O^T[16 dims x 16 heads] += V^T[16 dims x 32 tok] . P^T[32 tok x 16 heads]
+// (A = V^T via ds_read_b64_tr_b16 transposed LDS reads, shared by the two head blocks), so every
+// transposed read feeds two MFMAs.  The S^T accumulator layout already holds a head's token
+// weights in the B-operand layout of the value MFMA, so no register transpose is needed.
+//
+// Softmax is an fp32 online softmax in the exp2 domain, tiles in slot order.  A head's reference
+// max only moves when a tile's max exceeds it by more than 2^8 (a decision that depends on the
+// row's own scores only), so the accumulators are rescaled rarely.  A split that is not the only
+// one writes its normalized partial (O_s, lse_s) to the workspace and a combine kernel merges the
+// splits of a row in split order.  Nothing uses floating-point atomics.
 //
 // Invalid slots (index < 0, request/page out of range) load a valid dummy record, are zeroed in
 // LDS after arrival and get score -inf, so every wave issues exactly the same number of
 // direct-to-LDS loads per tile and the vmcnt bookkeeping below stays exact.
 #include <math.h>
+
+#include <type_traits>
 
 #include "smla_device.h"
 #include "smla_internal.h"
@@ -50,14 +58,9 @@ constexpr uint32_t kNoToken = 0xffffffffu;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Swizzle key of tile-local token t: bits (t2, t0, t1, t3) -> (b0, b1, b2, b3).  Chunk c of the
-// token's record sits at 16-byte position c ^ f (c < 64) or 64 + ((c - 64) ^ (f & 7)) (rope part).
-__device__ __forceinline__ int swz_key(int t) {
-    return ((t & 1) << 1) | ((t & 2) << 1) | ((t >> 2) & 1) | (t & 8);
-}
-__device__ __forceinline__ int swz_pos(int c, int f) {
-    return c < 64 ? (c ^ f) : (64 + ((c - 64) ^ (f & 7)));
-}
+// Swizzle of tile-local token t: chunk c of the record sits at 16-byte position c ^ f(t).  f < 8, so
+// every chunk stays inside its aligned group of 8 (the 64 latent chunks and the 8 rope chunks alike).
+__device__ __forceinline__ int swz_key(int t) { return (t >> 1) & 7; }
 
 struct AttnParams {
     const uint16_t* q;
@@ -93,21 +96,47 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// The running max of a head only moves when a tile's max exceeds it by more than this (log2
-// units); in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
+// max over lanes l, l^16, l^32, l^48 (the four lanes holding one head's tokens)
+__device__ __forceinline__ float head_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float w = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// sum over the same four lanes, in an order every one of them reproduces bit for bit
+__device__ __forceinline__ float head_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);    // lanes l < 32: v_l + v_{l+32}
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 b2;
+    union { b2 v; uint32_t u; } r;
+    r.v = __builtin_convertvector((f2){lo, hi}, b2);   // v_cvt_pk_bf16_f32, round to nearest even
+    return r.u;
+}
+
+// A head's reference max only moves when a tile's max exceeds it by more than this (log2 units);
+// in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
 
 // Instruction-group masks of __builtin_amdgcn_sched_group_barrier and the operand prefetch depths.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr int kQkAhead = 4;   // score steps (2 reads each) in flight ahead of their MFMAs
-constexpr int kPvAhead = 6;   // value dim-blocks (2 transposed reads each) in flight
+constexpr int kQkAhead = 3;   // score steps (2 reads each) in flight ahead of their MFMAs
+constexpr int kPvAhead = 4;   // value dim-blocks (2 transposed reads each) in flight
 
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
     __shared__ uint32_t phys[kSplitSlots];
     __shared__ uint32_t tile_valid[kTilesPerSplit];
-    __shared__ int s_first, s_last;
+    __shared__ __attribute__((aligned(16))) uint32_t pfrag[kAttnWaves][kWave * 4];   // P fragments
+    __shared__ float xalpha[kAttnWaves][16];    // per-head rescale factor of the current tile
+    __shared__ float xsum[kAttnWaves][16];      // per-head weight sums at the end
+    __shared__ int s_first, s_last, s_rescale;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -123,6 +152,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     const int rloc = rs / p.n_splits;
     const int64_t row = (int64_t)p.row0 + rloc;
 
+    // Heads: wave w scores heads hown .. hown+16; its pair (w, w^1) shares heads hpair .. hpair+32;
+    // for the values, wave w covers dims dim0 .. dim0+256 of both head blocks of the pair.
+    const int hown = hb * kHeadsPerBlock + wid * 16;
+    const int hpair = hb * kHeadsPerBlock + (wid >> 1) * 32;
+    const int dim0 = (wid & 1) * 256;
+    const bool own_ok = hown < p.H;
+    const bool blk0_ok = hpair < p.H;          // head block hpair .. +16
+    const bool blk1_ok = hpair + 16 < p.H;     // head block hpair+16 .. +32
+
+    // ---- Q (B operand of the score MFMA): lane holds head (lane & 15), dims 32kk + 8(lane >> 4) .. +8
+    bf16x8_t qv[18];
+    if (own_ok) {
+        const uint16_t* qrow = p.q + row * p.q_row_stride + (int64_t)(hown + (lane & 15)) * kDqk + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) qv[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+    }
+
     // ---- A4: translate this split's slots to physical token records ----
     const int slot0 = split * kSplitSlots;
     const int nslots = min(kSplitSlots, p.k - slot0);
@@ -131,60 +177,64 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     if (tid == 0) { s_first = kSplitSlots; s_last = -1; }
     if (tid < kTilesPerSplit) tile_valid[tid] = 0u;
     __syncthreads();
-    for (int j = tid; j < kSplitSlots; j += kAttnThreads) {
+    int32_t pos[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int j = tid + r * kAttnThreads;
+        const int jc = j < nslots ? j : 0;   // unconditional loads (clamped), so both are in flight together
+        pos[r] = p.idx[row * p.k + slot0 + jc];
+        if (!(j < nslots && req_ok)) pos[r] = -1;
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int j = tid + r * kAttnThreads;
         uint32_t ph = kNoToken;
-        if (j < nslots && req_ok) {
-            const int32_t pos = p.idx[row * p.k + slot0 + j];
-            if (pos >= 0) {
-                const int64_t lp = pos >> 6;
-                if (lp < p.bt_stride) {
-                    const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
-                    if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(pos & (kPage - 1));
-                }
-            }
+        const int64_t lp = pos[r] >> 6;
+        if (pos[r] >= 0 && lp < p.bt_stride) {
+            const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
+            if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(pos[r] & (kPage - 1));
         }
         phys[j] = ph;
-        if (ph != kNoToken) {
-            atomicMin(&s_first, j);
-            atomicMax(&s_last, j);
-            atomicOr(&tile_valid[j / kTileTok], 1u << (j % kTileTok));
+        const uint64_t vb = __ballot(ph != kNoToken);
+        if (lane == 0 && vb) {
+            const int jw = j - lane;    // first slot of this wave's 64
+            atomicMin(&s_first, jw + (int)__builtin_ctzll(vb));
+            atomicMax(&s_last, jw + 63 - (int)__builtin_clzll(vb));
+            atomicOr(&tile_valid[jw / kTileTok], (uint32_t)vb);
+            atomicOr(&tile_valid[jw / kTileTok + 1], (uint32_t)(vb >> 32));
         }
     }
-    __syncthreads();
-    const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
-    const uint32_t dummy = s_last < 0 ? 0u : phys[s_first];
-
-    // ---- Q (B operand of the score MFMA): lane holds head (lane & 15), dims 32kk + 8(lane >> 4) .. +8
-    const int h0 = hb * kHeadsPerBlock + wid * 16;
-    const bool has_heads = h0 < p.H;
-    bf16x8_t qv[18];
-    if (has_heads) {
-        const uint16_t* qrow = p.q + row * p.q_row_stride + (int64_t)(h0 + (lane & 15)) * kDqk + 8 * (lane >> 4);
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qv[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qv[kk]));   // Q lives in AGPRs (MFMA B operand)
     // Drain every compiler-visible global load here: inside the tile loop the only outstanding
     // vector-memory operations are the tile loads, which the loop waits for explicitly.
     wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qv[kk]));   // Q lives in AGPRs (MFMA B operand)
+    const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
+    const uint32_t dummy = s_last < 0 ? 0u : phys[s_first];
 
     // ---- A5: gather.  Wave w fills tile-local tokens [8w, 8w+8) of a stage: load i of lane l covers
-    // LDS bytes w*9216 + 1024 i + 16 l, i.e. token 8w + (64i + l) / 72, 16-byte position (64i + l) % 72,
-    // which holds the record's chunk swz_pos(position, swz_key(token)) (the swizzle is an involution).
-    const uint32_t ring_lds = lds_offset(ring);
-    const uint32_t wave_lds = ring_lds + (uint32_t)wid * kWaveTileBytes;
-    auto issue_tile = [&](int tile, int stage, int ln) {
+    // LDS bytes w*9216 + 1024 i + 16 l, i.e. token t = 8w + (64i + l) / 72 at 16-byte position
+    // (64i + l) % 72, which holds the record's chunk position ^ f(t).
+    uint32_t dtok[kLoadsPerWave], doff[kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int qd = kWave * i + lane;
+        const int tt = qd / 72;
+        const int t = 8 * wid + tt;
+        dtok[i] = 4u * (uint32_t)t;
+        doff[i] = 16u * (uint32_t)((qd - 72 * tt) ^ swz_key(t));
+    }
+    const uint32_t wave_lds = lds_offset(ring) + (uint32_t)wid * kWaveTileBytes;
+    auto issue_tile = [&](int tile, int stage) {
         const uint32_t m0 = wave_lds + (uint32_t)stage * kStageBytes;
+        const uint8_t* phys_tile = (const uint8_t*)phys + tile * kTileTok * 4;
         const uint8_t* src[kLoadsPerWave];
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {   // all slot reads first: the asm below is a compiler barrier
-            const int qd = kWave * i + ln;
-            const int tt = qd / 72;
-            const int t = 8 * wid + tt;
-            uint32_t ph = phys[tile * kTileTok + t];
+            uint32_t ph = *(const uint32_t*)(phys_tile + dtok[i]);
             ph = ph == kNoToken ? dummy : ph;
-            src[i] = p.kv + (uint64_t)ph * kBf16Record + 16u * (uint32_t)swz_pos(qd - 72 * tt, swz_key(t));
+            src[i] = p.kv + (uint64_t)ph * kBf16Record + doff[i];
         }
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) dma_b128(src[i], m0 + 1024u * i);
@@ -203,18 +253,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         }
     };
 
-    // Per-lane LDS byte offsets inside a stage (computed in the loop):
-    //  score operand: token (lane & 15) of a 16-token block, chunk 4kk + g  ->  kb[kk & 3] + 256 (kk >> 2)
-    //  for kk < 16, kr[kk - 16] for the two rope steps.
-    //  transposed value reads: lane supplies row (token) 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3
-    //  of a 16-dim block, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1)  ->  vb[db & 7] + 256 (db >> 3).
+    // Per-lane LDS byte offsets inside a stage.
+    //  score operand: token (lane & 15) (+16 for the second block), chunk 4kk + g -> ka[kk & 1] + 128 (kk >> 1)
+    //  transposed value reads: lane supplies token 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3 of a
+    //  16-dim block db, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1) -> vb[db & 3] + 128 (db >> 2)
     const int g = lane >> 4;
-    float m_run = -INFINITY, l_run = 0.f;   // exp2-domain reference max and weight sum (this lane's tokens)
-    f32x4_t oacc[32];
+    uint32_t ka[2], vb[4];
+    {
+        const int lr = lane & 15;
+        const int fa = swz_key(lr);
+        const int tv = 4 * g + (lr >> 2);
+        const int fv = swz_key(tv);
 #pragma unroll
-    for (int d = 0; d < 32; ++d) oacc[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) ka[j] = lr * kBf16Record + 16 * ((4 * j + g) ^ fa);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vb[j] = tv * kBf16Record + 8 * (lane & 1) + 16 * ((2 * j + ((lane >> 1) & 1)) ^ fv);
+    }
 
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t, lane);
+    float m_run = -INFINITY, l_run = 0.f;   // own heads: exp2-domain reference max, weight sum (lane's tokens)
+    f32x4_t oacc[2][16];                    // [head block of the pair][16-dim block of this wave's half]
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int d = 0; d < 16; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
 
     for (int it = 0; it < ntiles; ++it) {
         const int stage = it % kStages;
@@ -225,131 +288,155 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         zero_invalid(it, stage);
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();   // tile `it` visible; every wave is done with tile it-1
-        // Per-lane constants are recomputed every tile from an opaque copy of the lane id: keeping them
-        // live across the loop would leave no registers for operand prefetch.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages, ln);
-        if (!has_heads) continue;
-        const int g = ln >> 4;
-        const int fa = swz_key(ln & 15);
-        const int tv = 4 * g + ((ln & 15) >> 2);
-        const int fv = swz_key(tv);
-        uint32_t kb[4], kr[2], vb[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kb[j] = (ln & 15) * kBf16Record + 16 * ((4 * j + g) ^ fa);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) kr[j] = (ln & 15) * kBf16Record + 16 * (64 + ((4 * j + g) ^ (fa & 7)));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vb[j] = tv * kBf16Record + 8 * (ln & 1) + 16 * ((2 * j + ((ln >> 1) & 1)) ^ fv);
-
+        if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        // Every wave passes both barriers of every tile, whether or not its heads exist.
         const uint8_t* sb = ring + stage * kStageBytes;
         const uint32_t vmask = tile_valid[it];
 
-        // ---- A7: scores S^T[32 tok x 16 heads] as two 16-token blocks ----
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        // ---- A7 + A8: scores and online softmax of this wave's own 16 heads ----
+        if (own_ok) {
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-            const uint32_t off = kk < 16 ? kb[kk & 3] + 256u * (kk >> 2) : kr[kk - 16];
-            const bf16x8_t a0 = *(const bf16x8_t*)(sb + off);
-            const bf16x8_t a1 = *(const bf16x8_t*)(sb + off + 16 * kBf16Record);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
-        }
-        // Schedule: operand reads run kQkAhead steps ahead of the MFMAs that consume them.
+            for (int kk = 0; kk < 18; ++kk) {
+                const uint8_t* ap = sb + ka[kk & 1] + 128 * (kk >> 1);
+                const bf16x8_t a0 = *(const bf16x8_t*)(ap);
+                const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < kQkAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            for (int i = 0; i < kQkAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
-        for (int i = 0; i < 18 - kQkAhead; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kQkAhead, 0);
+            for (int i = 0; i < 18 - kQkAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kQkAhead, 0);
 
-        // ---- A8: online softmax (lane: head lane & 15, tokens 16tb + 4g + i) ----
-        float sv[8];
-        float mt = -INFINITY;
+            // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
+            float sv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = ((vmask >> (4 * g + i)) & 1u) ? s0[i] * p.scale_log2 : -INFINITY;
-            const float x1 = ((vmask >> (16 + 4 * g + i)) & 1u) ? s1[i] * p.scale_log2 : -INFINITY;
-            sv[i] = x0;
-            sv[4 + i] = x1;
-            mt = fmaxf(mt, fmaxf(x0, x1));
+            for (int i = 0; i < 4; ++i) { sv[i] = s0[i] * p.scale_log2; sv[4 + i] = s1[i] * p.scale_log2; }
+            if (vmask != 0xffffffffu) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (!((vmask >> (4 * g + i)) & 1u)) sv[i] = -INFINITY;
+                    if (!((vmask >> (16 + 4 * g + i)) & 1u)) sv[4 + i] = -INFINITY;
+                }
+            }
+            float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mt = head_max(mt);
+            float alpha = 1.f;
+            if (mt > m_run + kRescaleSlack) {     // same decision in all four lanes of the head
+                alpha = __builtin_amdgcn_exp2f(m_run - mt);   // 0 while nothing has been accumulated
+                m_run = mt;
+                l_run *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            float pw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pw[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
+                l_run += pw[j];
+            }
+            uint4 pf;
+            pf.x = pack_bf16x2_hw(pw[0], pw[1]);
+            pf.y = pack_bf16x2_hw(pw[2], pw[3]);
+            pf.z = pack_bf16x2_hw(pw[4], pw[5]);
+            pf.w = pack_bf16x2_hw(pw[6], pw[7]);
+            *(uint4*)&pfrag[wid][4 * lane] = pf;
+            if (lane < 16) xalpha[wid][lane] = alpha;
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // The reference max moves only if this tile's max exceeds it by more than the slack; the
-        // decision is a function of the row's own scores, so it is identical in every batch.
-        if (mt > m_run + kRescaleSlack) {
-            const float alpha = exp2f(m_run - mt);   // 0 while nothing has been accumulated
-            m_run = mt;
-            l_run *= alpha;
+        wait_lgkmcnt0();                 // s_barrier does not wait for LDS writes by itself
+        __builtin_amdgcn_s_barrier();   // P fragments and rescale factors of both waves published
+        if (!blk0_ok) continue;          // no head of this pair exists (uniform across the pair)
+
+        // ---- A9: O^T += V^T P^T for both head blocks of the pair over this wave's 256 dims ----
+        const int w0 = wid & ~1;
+        float a_blk[2];
+        a_blk[0] = blk0_ok ? xalpha[w0][lane & 15] : 1.f;
+        a_blk[1] = blk1_ok ? xalpha[w0 + 1][lane & 15] : 1.f;
+        bf16x8_t pb[2];
+        pb[0] = *(const bf16x8_t*)&pfrag[w0][4 * lane];
+        pb[1] = *(const bf16x8_t*)&pfrag[w0 + 1][4 * lane];
 #pragma unroll
-            for (int d = 0; d < 32; ++d) {
-                oacc[d][0] *= alpha; oacc[d][1] *= alpha; oacc[d][2] *= alpha; oacc[d][3] *= alpha;
+        for (int b = 0; b < 2; ++b) {
+            if (a_blk[b] != 1.f) {   // rare: a reference max moved (exact 1.0 otherwise)
+#pragma unroll
+                for (int d = 0; d < 16; ++d) {
+                    oacc[b][d][0] *= a_blk[b]; oacc[b][d][1] *= a_blk[b];
+                    oacc[b][d][2] *= a_blk[b]; oacc[b][d][3] *= a_blk[b];
+                }
             }
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float pw[8];
+        const uint8_t* vp0 = sb + 128 * (dim0 / 64);
+        // Two copies of the value loop (both head blocks / first block only) keep the branch out of it.
+        auto value_pass = [&](auto both_blocks) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            pw[j] = exp2f(sv[j] - m_use);
-            l_run += pw[j];
-        }
-        union { bf16x8_t v; uint32_t u[4]; } pb;
-        pb.u[0] = pack_bf16x2(pw[0], pw[1]);
-        pb.u[1] = pack_bf16x2(pw[2], pw[3]);
-        pb.u[2] = pack_bf16x2(pw[4], pw[5]);
-        pb.u[3] = pack_bf16x2(pw[6], pw[7]);
-
-        // ---- A9: O^T += V^T P^T over 32 dim blocks ----
+            for (int d = 0; d < 16; ++d) {   // dim block within this wave's half
+                const uint8_t* vp = vp0 + vb[d & 3] + 128 * (d >> 2);
+                union { bf16x8_t v; i16x4_t h[2]; } va;
+                va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
+                va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
+                oacc[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[0], oacc[0][d], 0, 0, 0);
+                if constexpr (decltype(both_blocks)::value)
+                    oacc[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[1], oacc[1][d], 0, 0, 0);
+            }
+            constexpr int kM = decltype(both_blocks)::value ? 2 : 1;
 #pragma unroll
-        for (int db = 0; db < 32; ++db) {
-            const uint8_t* vp = sb + vb[db & 7] + 256u * (db >> 3);
-            union { bf16x8_t v; i16x4_t h[2]; } va;
-            va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
-            va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb.v, oacc[db], 0, 0, 0);
-        }
+            for (int i = 0; i < kPvAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
-        for (int i = 0; i < kPvAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 32 - kPvAhead; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
+            for (int i = 0; i < 16 - kPvAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, kM, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kM * kPvAhead, 0);
+        };
+        if (blk1_ok) value_pass(std::true_type{});
+        else value_pass(std::false_type{});
     }
 
-    // ---- A10: epilogue (lane: head h0 + (lane & 15), dims 16db + 4g + i) ----
-    if (!has_heads) return;
-    // Lanes of one head share m_run (the tile max is reduced over them), so their sums add directly.
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot = l_tot + __shfl_xor(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    const int head = h0 + (lane & 15);
-    if (p.n_splits == 1) {
-        uint16_t* orow = p.out + (row * p.H + head) * (int64_t)kDv + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 32; ++db) {
-            uint2 w;
-            w.x = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
-            w.y = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
-            *(uint2*)(orow + 16 * db) = w;
+    // ---- A10: epilogue.  Own heads: total weight and LSE; both blocks: normalize and write ----
+    const float l_tot = head_sum(l_run);
+    if (own_ok && lane < 16) xsum[wid][lane] = l_tot;
+    __syncthreads();
+    if (!blk0_ok) return;
+    if (own_ok && lane < 16) {
+        const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        const int64_t hix = row * p.H + hown + lane;
+        if (p.n_splits == 1) {
+            if (p.lse) p.lse[hix] = lse_v;
+        } else {
+            p.ws_lse[((int64_t)rloc * p.n_splits + split) * p.H + hown + lane] = lse_v;
         }
-        if (lane < 16 && p.lse) p.lse[row * p.H + head] = lse_v;
-    } else {
-        const int64_t part = ((int64_t)rloc * p.n_splits + split) * p.H + head;
-        float* wo = p.ws_o + part * kDv + 4 * g;
+    }
+    const int w0 = wid & ~1;
 #pragma unroll
-        for (int db = 0; db < 32; ++db) {
-            f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
-            *(f32x4_t*)(wo + 16 * db) = v;
+    for (int b = 0; b < 2; ++b) {
+        if (b == 1 && !blk1_ok) break;
+        const float lt = xsum[w0 + b][lane & 15];
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int head = hpair + 16 * b + (lane & 15);
+        if (p.n_splits == 1) {
+            uint16_t* orow = p.out + (row * p.H + head) * (int64_t)kDv + dim0 + 4 * g;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) {
+                uint2 w;
+                w.x = pack_bf16x2_hw(oacc[b][d][0] * inv, oacc[b][d][1] * inv);
+                w.y = pack_bf16x2_hw(oacc[b][d][2] * inv, oacc[b][d][3] * inv);
+                *(uint2*)(orow + 16 * d) = w;
+            }
+        } else {
+            const int64_t part = ((int64_t)rloc * p.n_splits + split) * p.H + head;
+            float* wo = p.ws_o + part * kDv + dim0 + 4 * g;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) {
+                f32x4_t v = {oacc[b][d][0] * inv, oacc[b][d][1] * inv, oacc[b][d][2] * inv, oacc[b][d][3] * inv};
+                *(f32x4_t*)(wo + 16 * d) = v;
+            }
         }
-        if (lane < 16) p.ws_lse[part] = lse_v;
     }
 }
 
@@ -381,8 +468,8 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
     }
     const int64_t orow = ((int64_t)row0 + rloc) * H + head;
     uint2 w;
-    w.x = pack_bf16x2(acc[0], acc[1]);
-    w.y = pack_bf16x2(acc[2], acc[3]);
+    w.x = pack_bf16x2_hw(acc[0], acc[1]);
+    w.y = pack_bf16x2_hw(acc[2], acc[3]);
     *(uint2*)(out + orow * kDv + d) = w;
     if (d == 0 && lse) lse[orow] = LSE;
 }
