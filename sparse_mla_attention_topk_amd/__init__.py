@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "SmlaError", "KV_BF16", "KV_FP8", "Capacity", "library_path", "load_library", "exported_symbols",
-    "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row",
+    "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row", "topk_workspace",
     "sparse_mla_decode", "sparse_mla_prefill_chunk",
 ]
 
@@ -148,8 +148,12 @@ def fill_causal_lengths(first_pos: int, T: int, out: Optional[torch.Tensor] = No
 def topk_per_row(scores: torch.Tensor, k: int, lengths: Optional[torch.Tensor] = None,
                  row_offsets: Optional[torch.Tensor] = None, row_stride: Optional[int] = None,
                  rows: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
     """Stable top-k of each row, ascending indices, -1 padded: int32 [rows, k].
+
+    ``workspace`` (uint8, 256-byte aligned) lets few long rows split over several workgroups; when
+    None one is allocated if the split applies, unless ``split`` is False (then no workspace is
+    passed and every row is one workgroup).  The result is the same either way.
 
     ``scores`` is fp32; either 2-D [rows, stride] (row r at r*stride) or any contiguous buffer
     addressed through ``row_offsets`` (int64 element offsets) with ``row_stride`` entries per row.
@@ -175,6 +179,8 @@ def topk_per_row(scores: torch.Tensor, k: int, lengths: Optional[torch.Tensor] =
     _require(out, "out", torch.int32, scores.device)
     if out.numel() < rows * k:
         raise ValueError("out is smaller than rows*k")
+    if workspace is None and split:
+        workspace = topk_workspace(rows, k, row_stride, scores.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.smla_topk_per_row(_ptr(scores), _ptr(row_offsets), int(row_stride), _ptr(lengths), int(rows), int(k),
                                  _ptr(out), _ptr(workspace), ws_bytes, _stream(scores.device)))
@@ -198,6 +204,15 @@ def _kv_dtype_of(kv: torch.Tensor, kv_dtype: Optional[int]) -> int:
     if kv_dtype is not None:
         return int(kv_dtype)
     return KV_BF16 if kv.shape[-1] == 1152 else KV_FP8
+
+
+def topk_workspace(rows: int, k: int, row_stride: int, device) -> Optional[torch.Tensor]:
+    """A top-k workspace that lets `rows` rows of `row_stride` candidates split over several
+    workgroups (None when that split does not apply)."""
+    tk, _ = workspace_size(Capacity.make(max(1, rows), k, 16, int(row_stride)))
+    if tk == 0:
+        return None
+    return torch.empty(tk, dtype=torch.uint8, device=device)
 
 
 def attention_workspace(rows: int, H: int, k: int, device) -> Optional[torch.Tensor]:

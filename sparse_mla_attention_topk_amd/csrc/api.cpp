@@ -138,7 +138,11 @@ smla_status smla_is_supported(const smla_capacity* cap) {
 smla_status smla_workspace_size(const smla_capacity* cap, size_t* topk_ws_bytes, size_t* attn_ws_bytes) {
     smla_status st = smla_is_supported(cap);
     if (st != SMLA_OK) return st;
-    if (topk_ws_bytes) *topk_ws_bytes = 0;
+    if (topk_ws_bytes) {
+        const size_t per_row = smla::topk_ws_bytes_per_row(cap->max_candidates, cap->max_k);
+        const size_t rows = cap->max_rows < 255 ? (size_t)cap->max_rows : 255;   // the chunked path serves < 256 rows
+        *topk_ws_bytes = per_row * rows;
+    }
     if (attn_ws_bytes) {
         const size_t per_row = smla::attn_ws_bytes_per_row(cap->num_heads, cap->max_k);
         *attn_ws_bytes = per_row * (size_t)cap->max_rows;
@@ -157,8 +161,6 @@ smla_status smla_fill_causal_lengths(int64_t first_pos, int32_t T, int32_t* leng
 smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, int64_t row_stride,
                               const int32_t* lengths, int32_t rows, int32_t k, int32_t* out_idx, void* ws,
                               size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     smla_status st;
     if ((st = check_k(k, "k")) != SMLA_OK) return st;
     if (rows < 0) return fail(SMLA_ERR_INVALID_ARG, "rows=%d must be >= 0", rows);
@@ -172,7 +174,9 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
     if (!aligned(out_idx, 4)) return fail(SMLA_ERR_ALIGNMENT, "out_idx must be 4-byte aligned");
     if (row_offsets && !aligned(row_offsets, 8)) return fail(SMLA_ERR_ALIGNMENT, "row_offsets must be 8-byte aligned");
     if (lengths && !aligned(lengths, 4)) return fail(SMLA_ERR_ALIGNMENT, "lengths must be 4-byte aligned");
-    return hip_status(smla::launch_topk(scores, row_offsets, row_stride, lengths, rows, k, out_idx, (hipStream_t)stream),
+    if (ws && !aligned(ws, 256)) return fail(SMLA_ERR_ALIGNMENT, "ws must be 256-byte aligned");
+    return hip_status(smla::launch_topk(scores, row_offsets, row_stride, lengths, rows, k, out_idx, ws,
+                                        ws ? ws_bytes : 0, (hipStream_t)stream),
                       "topk_per_row");
 }
 

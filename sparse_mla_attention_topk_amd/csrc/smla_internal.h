@@ -41,8 +41,11 @@ struct AttnArgs {
     size_t ws_bytes;
 };
 
+// Top-k workspace bytes per row for the chunked path (0: the row is processed by one workgroup).
+size_t topk_ws_bytes_per_row(int64_t row_stride, int32_t k);
 hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t row_stride,
-                       const int32_t* lengths, int32_t rows, int32_t k, int32_t* out, hipStream_t stream);
+                       const int32_t* lengths, int32_t rows, int32_t k, int32_t* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 

@@ -30,49 +30,55 @@ constexpr int kTopkWaves = kTopkThreads / kWave;   // 16
 constexpr int kTopkUnroll = 16;                     // elements per thread per chunk
 constexpr int64_t kTopkChunk = (int64_t)kTopkThreads * kTopkUnroll;
 
+// Score source: a selection runs over positions j in [0, L) of a row; at(j) is the score, index(j)
+// the index written to the output for it.
+struct DirectScores {                 // a contiguous row
+    const float* __restrict__ s;
+    __device__ __forceinline__ float at(int64_t j) const { return s[j]; }
+    __device__ __forceinline__ int32_t index(int64_t j) const { return (int32_t)j; }
+};
+// Number of set bits of a wave mask below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16 lanes, then the row
+// broadcasts carry the running totals across rows (DPP, no LDS traffic).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Exclusive prefix sum of v over the 1024 threads of the block, in thread order.
-// `scratch` holds at least kTopkWaves + 1 words of LDS.  Ends with a barrier.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+// `scratch` holds at least kTopkWaves words of LDS.  Ends with a barrier.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        uint32_t y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == kWave - 1) scratch[wid] = x;
     __syncthreads();
-    if (wid == 0) {
-        uint32_t w = lane < kTopkWaves ? scratch[lane] : 0u;
-        uint32_t z = w;
-#pragma unroll
-        for (int off = 1; off < kTopkWaves; off <<= 1) {
-            uint32_t y = __shfl_up(z, off, kWave);
-            if (lane >= off) z += y;
-        }
-        if (lane < kTopkWaves) scratch[lane] = z - w;
-        if (lane == kTopkWaves - 1) scratch[kTopkWaves] = z;
-    }
+    const uint32_t w = lane < kTopkWaves ? scratch[lane] : 0u;
+    const uint32_t z = wave_inclusive_scan(w);       // every wave scans the 16 wave totals itself
+    const uint32_t before = __shfl(z - w, wid);       // exclusive prefix of this wave's total
+    *total = __shfl(z, kTopkWaves - 1);
     __syncthreads();
-    uint32_t r = scratch[wid] + x - v;
-    *total = scratch[kTopkWaves];
-    __syncthreads();
-    return r;
+    return before + x - v;
 }
 
 // Keys of the chunk's candidates base + u*1024 + threadIdx.x (0 past the end).  Every load is
 // issued unconditionally (index clamped into the row) and the values are pinned before use, so
 // all loads of the chunk are in flight together instead of each waiting behind its own branch.
-__device__ __forceinline__ void load_keys(const float* __restrict__ s, int64_t L, int64_t base, uint32_t* key) {
+template <class Src>
+__device__ __forceinline__ void load_keys(const Src& src, int64_t L, int64_t base, uint32_t* key) {
     float v[kTopkUnroll];
 #pragma unroll
     for (int u = 0; u < kTopkUnroll; ++u) {
         const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
-        v[u] = s[j < L ? j : L - 1];
+        v[u] = src.at(j < L ? j : L - 1);
     }
 #pragma unroll
     for (int u = 0; u < kTopkUnroll; ++u) asm volatile("" ::"v"(v[u]));
@@ -85,15 +91,15 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ s, int64_t L
 
 // Histogram of the BITS-bit digit below the DEPTH leading key bits, over the candidates whose
 // leading DEPTH bits equal `prefix`.
-template <int DEPTH, int BITS>
-__device__ void digit_histogram(const float* __restrict__ s, int64_t L, uint32_t prefix, uint32_t* hist) {
+template <int DEPTH, int BITS, class Src>
+__device__ __forceinline__ void digit_histogram(const Src& src, int64_t L, uint32_t prefix, uint32_t* hist) {
     constexpr int kBins = 1 << BITS;
     constexpr int kShift = 32 - DEPTH - BITS;
     for (int i = threadIdx.x; i < kBins; i += kTopkThreads) hist[i] = 0u;
     __syncthreads();
     for (int64_t base = 0; base < L; base += kTopkChunk) {
         uint32_t key[kTopkUnroll];
-        load_keys(s, L, base, key);
+        load_keys(src, L, base, key);
 #pragma unroll
         for (int u = 0; u < kTopkUnroll; ++u) {
             const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
@@ -108,7 +114,7 @@ __device__ void digit_histogram(const float* __restrict__ s, int64_t L, uint32_t
 // Finds the digit d holding the need-th largest candidate: above = #candidates with a larger digit,
 // above < need <= above + hist[d].  Results land in res[0..2] = {d, above, hist[d]}.
 template <int BITS>
-__device__ void find_digit(const uint32_t* hist, uint32_t need, uint32_t* scratch, uint32_t* res) {
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, uint32_t* scratch, uint32_t* res) {
     constexpr int kBins = 1 << BITS;
     constexpr int kPer = kBins >= kTopkThreads ? kBins / kTopkThreads : 1;
     uint32_t h[kPer];
@@ -134,183 +140,247 @@ __device__ void find_digit(const uint32_t* hist, uint32_t need, uint32_t* scratc
     __syncthreads();
 }
 
-// LDS capacities of the two-pass path.
-constexpr int kMaskWords = 4096;     // candidate bitmasks cover rows of up to 131072 candidates
-constexpr int kCandCap = 6144;       // boundary-bucket candidates resolved in LDS
+// LDS capacity of the filtered path.
+constexpr int kCandCap = 12288;      // candidates passing the filter, resolved in LDS
+constexpr int kSampleLog2 = 12;      // 4096 sampled candidates, 4 per thread
 
 // Block-wide exclusive scan of a 64-bit value (two 32-bit scans).
-__device__ uint64_t block_exclusive_scan64(uint32_t a, uint32_t b, uint32_t* scratch, uint32_t* ta, uint32_t* tb) {
+__device__ __forceinline__ uint64_t block_exclusive_scan64(uint32_t a, uint32_t b, uint32_t* scratch, uint32_t* ta,
+                                                           uint32_t* tb) {
     const uint32_t ea = block_exclusive_scan(a, scratch, ta);
     const uint32_t eb = block_exclusive_scan(b, scratch, tb);
     return ((uint64_t)ea << 32) | eb;
 }
 
-// Ordered emission from two LDS bitmasks over [0, L): every `gt` candidate is selected, and the first
-// `need` `eq` candidates in index order.  Output slot = #selected candidates with a smaller index.
-__device__ void emit_from_masks(const uint32_t* gtw, const uint32_t* eqw, int64_t L, uint32_t need, int32_t n,
-                                int32_t* __restrict__ o, uint32_t* scratch) {
-    const int W = (int)((L + 31) >> 5);
-    const int per = (W + kTopkThreads - 1) / kTopkThreads;
-    const int w0 = threadIdx.x * per;
-    const int w1 = min(W, w0 + per);
-    uint32_t cg = 0, ce = 0;
-    for (int w = w0; w < w1; ++w) {
-        cg += __popc(gtw[w]);
-        ce += __popc(eqw[w]);
+// The smallest value whose key has top-12 digit d (d >= 8): for every non-NaN v, v >= value <=>
+// score_key(v) >= d << 20.  Digits below 8 hold only -inf and NaN keys and have no such value.
+__device__ __forceinline__ float digit_floor_value(uint32_t d) {
+    const uint32_t key = d << 20;
+    return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
+// Slot layout of the filtered path.  A row is processed in chunks of U * 1024 positions; in a chunk
+// starting at `base`, wave w owns the U * 64 consecutive positions from base + w * U * 64, and lane l
+// holds position base + w * U * 64 + u * 64 + l in slot u.  Listing candidates chunk by chunk, wave
+// by wave, slot by slot and lane by lane therefore lists them in ascending position order.
+// Rows of up to 65536 positions are one chunk of 64 slots held in registers (read once); longer
+// rows stream in chunks of 16 slots and are read twice.
+constexpr int kResidentU = 64;
+constexpr int64_t kResident = (int64_t)kResidentU * kTopkThreads;   // 65536
+constexpr int kStreamU = 16;
+constexpr int32_t kStreamChunk = kStreamU * kTopkThreads;            // 16384
+// one (chunk, wave) count per thread: rows of up to 64 chunks
+constexpr int64_t kFilterMax = (int64_t)(kTopkThreads / kTopkWaves) * kStreamChunk;   // 1048576
+
+template <int U>
+__device__ __forceinline__ int32_t slot_pos(int32_t base, int u) {
+    return base + (int32_t)(threadIdx.x / kWave) * (U * kWave) + u * kWave + (int32_t)(threadIdx.x & (kWave - 1));
+}
+
+// Loads the U slots of the chunk at `base`.  Positions at or beyond L hold NaN, which passes no
+// threshold test.  Every load is issued before any wait, and the values become opaque register
+// contents, so the compiler cannot re-load them at later uses.
+template <int U, class Src>
+__device__ __forceinline__ void load_slots(const Src& src, int32_t L, int32_t base, float* v) {
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int g = 0; g < U; g += kTopkUnroll) {
+        const bool live = slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) < L;   // uniform in the wave
+#pragma unroll
+        for (int u = g; u < g + kTopkUnroll; ++u) {
+            const int32_t j = slot_pos<U>(base, u);
+            v[u] = live ? src.at(j < L ? j : L - 1) : qnan;
+        }
     }
-    uint32_t tg, te;
-    const uint64_t ex = block_exclusive_scan64(cg, ce, scratch, &tg, &te);
-    uint32_t gt_before = (uint32_t)(ex >> 32), eq_before = (uint32_t)ex;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t mg = gtw[w], me = eqw[w];
-        uint32_t both = mg | me;
-        while (both) {
-            const int b = __ffs(both) - 1;
-            both &= both - 1;
-            const int32_t j = (w << 5) + b;
-            uint32_t dst = 0xffffffffu;
-            if ((mg >> b) & 1u) {
-                dst = gt_before + (eq_before < need ? eq_before : need);
-                ++gt_before;
-            } else {
-                if (eq_before < need) dst = gt_before + eq_before;
-                ++eq_before;
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (slot_pos<U>(base, u) >= L) v[u] = qnan;
+}
+
+// Number of this wave's slots with v >= tf (uniform in the wave).
+template <int U>
+__device__ __forceinline__ uint32_t wave_count_ge(const float* v, int32_t L, int32_t base, float tf) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int g = 0; g < U; g += kTopkUnroll) {
+        if (slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) >= L) break;   // uniform in the wave
+#pragma unroll
+        for (int u = g; u < g + kTopkUnroll; ++u) c += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(v[u] >= tf));
+    }
+    return c;
+}
+
+// Appends this wave's slots with v >= tf (value bits, position) to the LDS list from offset `pos`
+// (uniform in the wave), in slot-then-lane order.  With GUARD, slots at or beyond kCandCap are
+// never written (the streaming path re-reads the row, so its counts are not taken on faith).
+template <int U, bool GUARD>
+__device__ __forceinline__ void wave_append_ge(const float* v, int32_t L, int32_t base, float tf, uint32_t pos,
+                                               uint32_t* cbits, uint32_t* cidx) {
+#pragma unroll
+    for (int g = 0; g < U; g += kTopkUnroll) {
+        if (slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) >= L) break;   // uniform in the wave
+#pragma unroll
+        for (int u = g; u < g + kTopkUnroll; ++u) {
+            const bool pred = v[u] >= tf;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+            if (pred) {
+                const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos));
+                if (!GUARD || p < (uint32_t)kCandCap) {
+                    cbits[p] = __float_as_uint(v[u]);
+                    cidx[p] = (uint32_t)slot_pos<U>(base, u);
+                }
             }
-            if (dst < (uint32_t)n) o[dst] = j;
+            pos += (uint32_t)__popcll(m);
         }
     }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ scores,
-                                                                 const int64_t* __restrict__ row_offsets,
-                                                                 int64_t row_stride,
-                                                                 const int32_t* __restrict__ lengths,
-                                                                 int32_t k, int32_t* __restrict__ out) {
-    __shared__ uint32_t hist[1 << 12];
-    __shared__ uint32_t scratch[kTopkWaves + 2];
-    __shared__ uint32_t res[3];
-    __shared__ uint32_t tbl[kTopkUnroll * kTopkWaves];
-    __shared__ uint32_t gtw[kMaskWords], eqw[kMaskWords];
-    __shared__ uint32_t cand_key[kCandCap], cand_idx[kCandCap];
-    __shared__ uint32_t ncand;
+// LDS of one selecting workgroup.
+struct TopkShared {
+    uint32_t hist[1 << 12];
+    uint32_t scratch[kTopkWaves + 2];
+    uint32_t res[3];
+    uint32_t tbl[kTopkUnroll * kTopkWaves];
+    uint32_t wcnt[kTopkThreads];             // per-wave candidate counts, then list offsets
+    uint32_t cand_key[kCandCap], cand_idx[kCandCap];
+};
 
-    const int row = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int64_t len = lengths ? (int64_t)lengths[row] : row_stride;
-    const int64_t L = len < 0 ? 0 : (len > row_stride ? row_stride : len);   // clamp before any decision
-    const int64_t off = row_offsets ? row_offsets[row] : (int64_t)row * row_stride;
-    const float* __restrict__ s = scores + off;
-    int32_t* __restrict__ o = out + (int64_t)row * k;
-    const int32_t n = (int32_t)(L < (int64_t)k ? L : (int64_t)k);
+// Filter threshold from the four sampled values per thread: a value tf such that, judging by the
+// sample, about 1.25 n + 4 sigma candidates of the row have v >= tf.  Returns false when the sample
+// offers none.  Every workgroup that samples the same row at the same positions derives the same tf.
+__device__ __forceinline__ bool sample_threshold(const float* sv, int64_t L, int32_t n, uint32_t* hist,
+                                                 uint32_t* scratch, uint32_t* res, float* tf) {
+    for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicAdd(&hist[score_key(sv[i]) >> 20], 1u);
+    __syncthreads();
+    const float expect = (float)n * (float)(1 << kSampleLog2) / (float)L;
+    const uint32_t want = (uint32_t)(1.25f * expect + 4.f * sqrtf(expect) + 8.f);
+    if (want >= (uint32_t)(1 << kSampleLog2)) return false;
+    find_digit<12>(hist, want, scratch, res);
+    if (res[0] < 8u) return false;
+    *tf = digit_floor_value(res[0]);
+    return true;
+}
 
-    if ((int64_t)n == L) {   // every candidate is selected (also L == 0)
-        for (int i = threadIdx.x; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
-        return;
+// Sampled positions: four per thread, spread evenly over the row.
+template <class Src>
+__device__ __forceinline__ void load_sample(const Src& src, int64_t L, float* sv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = src.at(((int64_t)(threadIdx.x * 4 + i) * L) >> kSampleLog2);
+}
+
+// Rows that go through a candidate filter (decided from L and k alone).
+__device__ __forceinline__ bool filter_eligible(int64_t L, int32_t n) {
+    return L > kCandCap && L <= kFilterMax && n <= kCandCap;
+}
+
+// Finishes a selection from the candidate list sm.cand_key (value bits) / sm.cand_idx (positions),
+// entries [0, total), which holds every selected candidate, in ascending position order, with
+// n <= total <= kCandCap: radix selection of the n-th key, then the output slot of each selected
+// candidate is the number of selected candidates before it in the list.
+template <class Src>
+__device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int32_t n, int32_t k,
+                                             int32_t* __restrict__ o, TopkShared& sm) {
+    uint32_t* hist = sm.hist;
+    uint32_t* scratch = sm.scratch;
+    uint32_t* res = sm.res;
+    uint32_t* cand_key = sm.cand_key;
+    uint32_t* cand_idx = sm.cand_idx;
+    // ---- radix selection of the n-th key among the listed candidates ----
+    for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+    __syncthreads();
+    const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
+    const uint32_t c0 = threadIdx.x * per;
+    const uint32_t c1 = c0 + per < total ? c0 + per : total;
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t key = score_key(__uint_as_float(cand_key[c]));
+        cand_key[c] = key;
+        atomicAdd(&hist[key >> 20], 1u);
     }
+    __syncthreads();
+    find_digit<12>(hist, (uint32_t)n, scratch, res);
+    uint32_t p = res[0];
+    uint32_t need = (uint32_t)n - res[1];
+    int shift = 20;
+    if (need != res[2]) {
+        for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+        __syncthreads();
+        for (uint32_t c = c0; c < c1; ++c)
+            if ((cand_key[c] >> 20) == p) atomicAdd(&hist[(cand_key[c] >> 8) & 0xfffu], 1u);
+        __syncthreads();
+        find_digit<12>(hist, need, scratch, res);
+        p = (p << 12) | res[0];
+        need -= res[1];
+        shift = 8;
+        if (need != res[2]) {
+            for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0u;
+            __syncthreads();
+            for (uint32_t c = c0; c < c1; ++c)
+                if ((cand_key[c] >> 8) == p) atomicAdd(&hist[cand_key[c] & 0xffu], 1u);
+            __syncthreads();
+            find_digit<8>(hist, need, scratch, res);
+            p = (p << 8) | res[0];
+            need -= res[1];
+            shift = 0;
+        }
+    }
+    // ---- emission: selected are the keys above the boundary value p and the first `need`
+    // (in list, i.e. position, order) equal to it; a selected candidate's output slot is the
+    // number of selected candidates before it in the list ----
+    uint32_t ng = 0, ne = 0;
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t hi = cand_key[c] >> shift;
+        ng += hi > p ? 1u : 0u;
+        ne += hi == p ? 1u : 0u;
+    }
+    uint32_t tg, te;
+    const uint64_t ex = block_exclusive_scan64(ng, ne, scratch, &tg, &te);
+    uint32_t gb = (uint32_t)(ex >> 32), eb = (uint32_t)ex;
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t hi = cand_key[c] >> shift;
+        uint32_t dst = 0xffffffffu;
+        if (hi > p) {
+            dst = gb + (eb < need ? eb : need);
+            ++gb;
+        } else if (hi == p) {
+            if (eb < need) dst = gb + eb;
+            ++eb;
+        }
+        if (dst < (uint32_t)n) o[dst] = src.index((int64_t)cand_idx[c]);
+    }
+    for (int i = n + threadIdx.x; i < k; i += kTopkThreads) o[i] = -1;
+}
 
-    // ---- pass 1: histogram of the top 12 key bits ----
+// General selection, any row: radix passes over the row, then an ordered compaction that rereads it.
+template <class Src>
+__device__ __forceinline__ void select_general(const Src& src, int64_t L, int32_t n, int32_t k,
+                                               int32_t* __restrict__ o, TopkShared& sm) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    uint32_t* hist = sm.hist;
+    uint32_t* scratch = sm.scratch;
+    uint32_t* res = sm.res;
+    uint32_t* tbl = sm.tbl;
     uint32_t need = (uint32_t)n;
-    digit_histogram<0, 12>(s, L, 0u, hist);
+    digit_histogram<0, 12>(src, L, 0u, hist);
     find_digit<12>(hist, need, scratch, res);
     uint32_t prefix = res[0];
     need -= res[1];
     uint32_t cnt = res[2];
-
-    const bool masks_fit = L <= (int64_t)kMaskWords * 32;
-    if (masks_fit && (need == cnt || cnt <= (uint32_t)kCandCap)) {
-        // ---- pass 2: bitmask of candidates above the boundary bucket; the bucket itself is either
-        // taken whole (eq mask) or gathered into LDS for an exact resolution ----
-        const bool take_all = need == cnt;
-        const int W = (int)((L + 31) >> 5);
-        for (int w = threadIdx.x; w < W; w += kTopkThreads) { gtw[w] = 0u; eqw[w] = 0u; }
-        if (threadIdx.x == 0) ncand = 0u;
-        __syncthreads();
-        for (int64_t base = 0; base < L; base += kTopkChunk) {
-            uint32_t key[kTopkUnroll];
-#pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) {
-                const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
-                key[u] = j < L ? score_key(s[j < L ? j : L - 1]) : 0u;   // unconditional load: all in flight
-            }
-#pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) {
-                const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
-                const uint32_t hi = key[u] >> 20;
-                const bool ok = j < L;
-                const uint64_t gm = __ballot(ok && hi > prefix);
-                const bool in_bucket = ok && hi == prefix;
-                if (take_all) {
-                    const uint64_t em = __ballot(in_bucket);
-                    if (lane == 0 && base + (int64_t)u * kTopkThreads + wid * kWave < L) {
-                        const int w = (int)((base + (int64_t)u * kTopkThreads + wid * kWave) >> 5);
-                        gtw[w] = (uint32_t)gm;
-                        eqw[w] = (uint32_t)em;
-                        if (w + 1 < W) { gtw[w + 1] = (uint32_t)(gm >> 32); eqw[w + 1] = (uint32_t)(em >> 32); }
-                    }
-                } else {
-                    if (lane == 0 && base + (int64_t)u * kTopkThreads + wid * kWave < L) {
-                        const int w = (int)((base + (int64_t)u * kTopkThreads + wid * kWave) >> 5);
-                        gtw[w] = (uint32_t)gm;
-                        if (w + 1 < W) gtw[w + 1] = (uint32_t)(gm >> 32);
-                    }
-                    if (in_bucket) {
-                        const uint32_t slot = atomicAdd(&ncand, 1u);   // < cnt <= kCandCap (same data as pass 1)
-                        if (slot < (uint32_t)kCandCap) {
-                            cand_key[slot] = key[u];
-                            cand_idx[slot] = (uint32_t)j;
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        if (!take_all) {
-            // ---- resolve the bucket in LDS: radix select on the remaining 20 key bits ----
-            const uint32_t nc = ncand < (uint32_t)kCandCap ? ncand : (uint32_t)kCandCap;
-            for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-            __syncthreads();
-            for (uint32_t c = threadIdx.x; c < nc; c += kTopkThreads) atomicAdd(&hist[(cand_key[c] >> 8) & 0xfffu], 1u);
-            __syncthreads();
-            find_digit<12>(hist, need, scratch, res);
-            uint32_t p2 = (prefix << 12) | res[0];
-            need -= res[1];
-            int shift = 8;
-            if (need != res[2]) {
-                for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0u;
-                __syncthreads();
-                for (uint32_t c = threadIdx.x; c < nc; c += kTopkThreads)
-                    if ((cand_key[c] >> 8) == p2) atomicAdd(&hist[cand_key[c] & 0xffu], 1u);
-                __syncthreads();
-                find_digit<8>(hist, need, scratch, res);
-                p2 = (p2 << 8) | res[0];
-                need -= res[1];
-                shift = 0;
-            }
-            for (uint32_t c = threadIdx.x; c < nc; c += kTopkThreads) {
-                const uint32_t hi = cand_key[c] >> shift;
-                const uint32_t j = cand_idx[c];
-                if (hi > p2) atomicOr(&gtw[j >> 5], 1u << (j & 31));
-                else if (hi == p2) atomicOr(&eqw[j >> 5], 1u << (j & 31));
-            }
-            __syncthreads();
-        }
-        emit_from_masks(gtw, eqw, L, need, n, o, scratch);
-        for (int i = n + threadIdx.x; i < k; i += kTopkThreads) o[i] = -1;
-        return;
-    }
-
-    // ---- general path (rows longer than the LDS masks, or a huge boundary bucket): further radix
-    // passes over the row, then an ordered compaction that rereads it ----
     int depth = 12;
     if (need != cnt) {
-        digit_histogram<12, 12>(s, L, prefix, hist);
+        digit_histogram<12, 12>(src, L, prefix, hist);
         find_digit<12>(hist, need, scratch, res);
         prefix = (prefix << 12) | res[0];
         need -= res[1];
         cnt = res[2];
         depth = 24;
         if (need != cnt) {
-            digit_histogram<24, 8>(s, L, prefix, hist);
+            digit_histogram<24, 8>(src, L, prefix, hist);
             find_digit<8>(hist, need, scratch, res);
             prefix = (prefix << 8) | res[0];
             need -= res[1];
@@ -324,7 +394,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     for (int64_t base = 0; base < L; base += kTopkChunk) {
         uint64_t gtm[kTopkUnroll], eqm[kTopkUnroll];
         uint32_t key[kTopkUnroll];
-        load_keys(s, L, base, key);
+        load_keys(src, L, base, key);
 #pragma unroll
         for (int u = 0; u < kTopkUnroll; ++u) {
             const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
@@ -349,7 +419,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
             uint32_t dst = 0xffffffffu;
             if ((gtm[u] >> lane) & 1ull) dst = gt_before + (eq_before < need ? eq_before : need);
             else if (((eqm[u] >> lane) & 1ull) && eq_before < need) dst = gt_before + eq_before;
-            if (dst < (uint32_t)n) o[dst] = (int32_t)j;   // always true; guards the buffer regardless
+            if (dst < (uint32_t)n) o[dst] = src.index(j);   // always true; guards the buffer regardless
         }
         gt_run += tot >> 16;
         eq_run += tot & 0xffffu;
@@ -358,13 +428,265 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     for (int i = n + threadIdx.x; i < k; i += kTopkThreads) o[i] = -1;
 }
 
+// Selects the min(k, L) best positions of `src` and writes their indices (src.index) to o[0 .. n),
+// ascending, then -1 to o[n .. k), in one workgroup.
+//
+// Filtered path: a threshold value tf is taken from a fixed sample of the row such that roughly
+// 1.25 n candidates satisfy v >= tf, and the row is counted against it.  If at least n and at most
+// kCandCap candidates pass, every selected candidate is among them (a candidate below tf, or NaN,
+// is preceded by all those at or above tf), so the selection is finished on that short list.  The
+// sample only decides how fast the row goes; if the count check fails the row takes the general
+// path, with the same result.  Rows of at most kCandCap candidates list all of them.
+template <class Src>
+__device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k, int32_t* __restrict__ o,
+                                            TopkShared& sm) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int32_t n = (int32_t)(L < (int64_t)k ? L : (int64_t)k);
+
+    if ((int64_t)n == L) {   // every candidate is selected (also L == 0)
+        for (int i = threadIdx.x; i < k; i += kTopkThreads) o[i] = i < n ? src.index(i) : -1;
+        return;
+    }
+    if (L <= kCandCap) {
+        const int32_t L32 = (int32_t)L;
+        float v[kResidentU];
+        load_slots<kResidentU>(src, L32, 0, v);
+#pragma unroll
+        for (int u = 0; u < kResidentU; ++u) {
+            const int32_t j = slot_pos<kResidentU>(0, u);
+            if (j < L32) {
+                sm.cand_key[j] = __float_as_uint(v[u]);
+                sm.cand_idx[j] = (uint32_t)j;
+            }
+        }
+        resolve_list(src, (uint32_t)L32, n, k, o, sm);
+        return;
+    }
+    if (filter_eligible(L, n)) {   // uniform
+        const int32_t L32 = (int32_t)L;
+        const bool resident = L <= kResident;
+        float v[kResidentU];
+        float sv[4];
+        load_sample(src, L, sv);
+        if (resident) load_slots<kResidentU>(src, L32, 0, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(sv[i]));
+        float tf = 0.f;
+        if (sample_threshold(sv, L, n, sm.hist, sm.scratch, sm.res, &tf)) {
+            const int nch = resident ? 1 : (L32 + kStreamChunk - 1) / kStreamChunk;
+            if (resident) {
+                const uint32_t c = wave_count_ge<kResidentU>(v, L32, 0, tf);
+                if (lane == 0) sm.wcnt[wid] = c;
+            } else {
+                for (int ch = 0; ch < nch; ++ch) {
+                    float cv[kStreamU];
+                    load_slots<kStreamU>(src, L32, ch * kStreamChunk, cv);
+                    const uint32_t c = wave_count_ge<kStreamU>(cv, L32, ch * kStreamChunk, tf);
+                    if (lane == 0) sm.wcnt[ch * kTopkWaves + wid] = c;
+                }
+            }
+            __syncthreads();
+            uint32_t total;
+            const uint32_t mine = (int)threadIdx.x < nch * kTopkWaves ? sm.wcnt[threadIdx.x] : 0u;
+            const uint32_t before = block_exclusive_scan(mine, sm.scratch, &total);
+            if ((int)threadIdx.x < nch * kTopkWaves) sm.wcnt[threadIdx.x] = before;
+            __syncthreads();
+            if (total >= (uint32_t)n && total <= (uint32_t)kCandCap) {   // uniform
+                if (resident) {
+                    wave_append_ge<kResidentU, false>(v, L32, 0, tf, sm.wcnt[wid], sm.cand_key, sm.cand_idx);
+                } else {
+                    for (int ch = 0; ch < nch; ++ch) {
+                        float cv[kStreamU];
+                        load_slots<kStreamU>(src, L32, ch * kStreamChunk, cv);
+                        wave_append_ge<kStreamU, true>(cv, L32, ch * kStreamChunk, tf, sm.wcnt[ch * kTopkWaves + wid],
+                                                       sm.cand_key, sm.cand_idx);
+                    }
+                }
+                __syncthreads();
+                resolve_list(src, total, n, k, o, sm);
+                return;
+            }
+        }
+        __syncthreads();
+    }
+    select_general(src, L, n, k, o, sm);
+}
+
+__device__ __forceinline__ int64_t clamped_length(const int32_t* lengths, int row, int64_t row_stride) {
+    const int64_t len = lengths ? (int64_t)lengths[row] : row_stride;
+    return len < 0 ? 0 : (len > row_stride ? row_stride : len);   // clamp before any decision
+}
+
+// One workgroup per row.
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ scores,
+                                                                 const int64_t* __restrict__ row_offsets,
+                                                                 int64_t row_stride,
+                                                                 const int32_t* __restrict__ lengths,
+                                                                 int32_t k, int32_t* __restrict__ out) {
+    __shared__ TopkShared sm;
+    const int row = blockIdx.x;
+    const int64_t L = clamped_length(lengths, row, row_stride);
+    const int64_t off = row_offsets ? row_offsets[row] : (int64_t)row * row_stride;
+    select_topk(DirectScores{scores + off}, L, k, out + (int64_t)row * k, sm);
+}
+
+// ---- few long rows: the filter pass split over the row's chunks of kStreamChunk positions ----
+// Per row, the workspace holds kSplitHeader bytes of chunk counts, then for each chunk a list of up
+// to kCandCap (value bits, position) pairs.  Every chunk workgroup derives the same threshold from
+// the same sample of the row, and lists its candidates in position order; the select kernel
+// concatenates the lists in chunk order, which is position order, and finishes the row exactly as
+// the one-workgroup filtered path does.  Rows whose filter fails (a chunk reports kFilterFailed, or
+// the total is out of range) are selected by the general path in the select kernel.
+constexpr size_t kSplitHeader = 256;
+constexpr int kMaxSplitChunks = 16;
+constexpr int kMinSplitChunks = 8;
+constexpr uint32_t kFilterFailed = 0xffffffffu;
+
+__host__ __device__ __forceinline__ size_t split_row_bytes(int nch) {
+    return kSplitHeader + (size_t)nch * kCandCap * sizeof(uint2);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* __restrict__ scores,
+                                                                   const int64_t* __restrict__ row_offsets,
+                                                                   int64_t row_stride,
+                                                                   const int32_t* __restrict__ lengths, int32_t k,
+                                                                   int32_t nch, unsigned char* __restrict__ ws) {
+    __shared__ uint32_t hist[1 << 12];
+    __shared__ uint32_t scratch[kTopkWaves + 2];
+    __shared__ uint32_t res[3];
+    __shared__ uint32_t wcnt[kTopkWaves];
+    const int row = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int64_t L = clamped_length(lengths, row, row_stride);
+    const int32_t n = (int32_t)(L < (int64_t)k ? L : (int64_t)k);
+    if ((int64_t)n == L || !filter_eligible(L, n)) return;   // uniform; the select kernel takes the row whole
+    unsigned char* rws = ws + (size_t)row * split_row_bytes(nch);
+    uint32_t* counts = (uint32_t*)rws;
+    uint2* list = (uint2*)(rws + kSplitHeader) + (size_t)c * kCandCap;
+    const int32_t L32 = (int32_t)L;
+    const int32_t base = c * kStreamChunk;
+    if (base >= L32) {
+        if (threadIdx.x == 0) counts[c] = 0u;
+        return;
+    }
+    const DirectScores src{scores + (row_offsets ? row_offsets[row] : (int64_t)row * row_stride)};
+    float sv[4], v[kStreamU];
+    load_sample(src, L, sv);
+    load_slots<kStreamU>(src, L32, base, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(sv[i]));
+    float tf = 0.f;
+    if (!sample_threshold(sv, L, n, hist, scratch, res, &tf)) {
+        if (threadIdx.x == 0) counts[c] = kFilterFailed;
+        return;
+    }
+    const uint32_t wc = wave_count_ge<kStreamU>(v, L32, base, tf);
+    if (lane == 0) wcnt[wid] = wc;
+    __syncthreads();
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan(threadIdx.x < kTopkWaves ? wcnt[threadIdx.x] : 0u, scratch, &total);
+    if (threadIdx.x < kTopkWaves) wcnt[threadIdx.x] = before;
+    __syncthreads();
+    if (threadIdx.x == 0) counts[c] = total;
+    if (total > (uint32_t)kCandCap) return;   // uniform; the row's total is then out of range too
+    uint32_t pos = wcnt[wid];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        const bool pred = v[u] >= tf;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+        if (pred) {
+            const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos));
+            list[p] = make_uint2(__float_as_uint(v[u]), (uint32_t)slot_pos<kStreamU>(base, u));   // p < total
+        }
+        pos += (uint32_t)__popcll(m);
+    }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* __restrict__ scores,
+                                                                   const int64_t* __restrict__ row_offsets,
+                                                                   int64_t row_stride,
+                                                                   const int32_t* __restrict__ lengths, int32_t k,
+                                                                   int32_t nch, const unsigned char* __restrict__ ws,
+                                                                   int32_t* __restrict__ out) {
+    __shared__ TopkShared sm;
+    const int row = blockIdx.x;
+    const int64_t L = clamped_length(lengths, row, row_stride);
+    const int32_t n = (int32_t)(L < (int64_t)k ? L : (int64_t)k);
+    const DirectScores src{scores + (row_offsets ? row_offsets[row] : (int64_t)row * row_stride)};
+    int32_t* o = out + (int64_t)row * k;
+    if ((int64_t)n < L && filter_eligible(L, n)) {   // uniform
+        const unsigned char* rws = ws + (size_t)row * split_row_bytes(nch);
+        const uint32_t* counts = (const uint32_t*)rws;
+        const uint2* lists = (const uint2*)(rws + kSplitHeader);
+        const int used = (int)((L + kStreamChunk - 1) / kStreamChunk);   // chunks the filter kernel ran
+        if ((int)threadIdx.x < used) sm.wcnt[threadIdx.x] = counts[threadIdx.x];
+        __syncthreads();
+        uint32_t total = 0;
+        bool ok = true;
+        for (int c = 0; c < used; ++c) {
+            const uint32_t cc = sm.wcnt[c];
+            if (cc == kFilterFailed || cc > (uint32_t)kCandCap) ok = false;
+            else total += cc;
+        }
+        ok = ok && total >= (uint32_t)n && total <= (uint32_t)kCandCap;   // uniform
+        if (ok) {
+            uint32_t off = 0;
+            for (int c = 0; c < used; ++c) {
+                const uint32_t cc = sm.wcnt[c];
+                for (uint32_t i = threadIdx.x; i < cc; i += kTopkThreads) {
+                    const uint2 e = lists[(size_t)c * kCandCap + i];
+                    sm.cand_key[off + i] = e.x;
+                    sm.cand_idx[off + i] = e.y;
+                }
+                off += cc;
+            }
+            __syncthreads();
+            resolve_list(src, total, n, k, o, sm);
+            return;
+        }
+        __syncthreads();
+        select_general(src, L, n, k, o, sm);
+        return;
+    }
+    select_topk(src, L, k, o, sm);
+}
+
+size_t topk_ws_bytes_per_row(int64_t row_stride, int32_t k) {
+    (void)k;
+    const int64_t nch = (row_stride + kStreamChunk - 1) / kStreamChunk;
+    if (nch < kMinSplitChunks || nch > kMaxSplitChunks) return 0;
+    return split_row_bytes((int)nch);
+}
+
 hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t row_stride,
-                       const int32_t* lengths, int32_t rows, int32_t k, int32_t* out, hipStream_t stream) {
+                       const int32_t* lengths, int32_t rows, int32_t k, int32_t* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
     if (rows == 0) return hipSuccess;
+    const size_t per_row = topk_ws_bytes_per_row(row_stride, k);
+    // Few very long rows leave most of the GPU idle at one workgroup per row, each streaming its row
+    // twice: split the filter pass over the rows' chunks when the workspace allows.  Measured on
+    // 64 rows of 65536 candidates the split is slower (its fixed costs are paid twice), so it starts
+    // at rows of 8 chunks.  The result is identical either way.
+    const int nch = (int)((row_stride + kStreamChunk - 1) / kStreamChunk);
+    if (per_row > 0 && nch >= kMinSplitChunks && rows < 256 && ws && ws_bytes >= per_row) {
+        const int per_batch = (int)min((size_t)rows, ws_bytes / per_row);
+        for (int r0 = 0; r0 < rows; r0 += per_batch) {
+            const int nr = min(per_batch, rows - r0);
+            const int64_t* ro = row_offsets ? row_offsets + r0 : nullptr;
+            const float* sc = row_offsets ? scores : scores + (int64_t)r0 * row_stride;
+            const int32_t* ln = lengths ? lengths + r0 : nullptr;
+            hipLaunchKernelGGL(topk_filter_kernel, dim3(nr * nch), dim3(kTopkThreads), 0, stream, sc, ro, row_stride,
+                               ln, k, nch, (unsigned char*)ws);
+            hipLaunchKernelGGL(topk_select_kernel, dim3(nr), dim3(kTopkThreads), 0, stream, sc, ro, row_stride, ln, k,
+                               nch, (const unsigned char*)ws, out + (int64_t)r0 * k);
+        }
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_offsets,
                        row_stride, lengths, k, out);
     return hipGetLastError();
 }
+
 
 // ---- A0: causal lengths ----
 __global__ __launch_bounds__(256) void causal_lengths_kernel(int64_t first_pos, int32_t T, int32_t* lengths) {

@@ -117,3 +117,48 @@ def test_causal_lengths_match_oracle():
         got = smla.fill_causal_lengths(first_pos, T, device=DEV).cpu().numpy()
         ref = np.minimum(O.causal_lengths(first_pos, T), 2**31 - 1)
         assert np.array_equal(got, ref), (first_pos, T)
+
+
+@pytest.mark.parametrize("stride", [114689, 131072, 200003, 262144])
+def test_chunked_rows_equal_single_workgroup_rows(stride):
+    """Few long rows are split into 16384-wide chunks and merged; the result must equal both the
+    oracle and the one-workgroup-per-row path, including selections that straddle chunks, ties
+    across chunk borders and rows shorter than k."""
+    g = torch.Generator(device=DEV).manual_seed(stride)
+    k = 2048
+    lens = [0, 1, k - 1, k, k + 1, 16383, 16384, 16385, 16384 + k, stride - 1, stride, stride + 5,
+            (stride * 3) // 4, 40000, 9000, 2**31 - 1]
+    R = len(lens)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    s = torch.round(torch.randn((R, stride), generator=g, device=DEV) * 2) / 2       # heavy ties
+    s[0:4] = 1.0                                            # all equal: the first k indices win
+    s[4, 16384 - 1000:] = 50.0                              # winners straddle the first chunk border
+    s[5, ::5] = float("nan")
+    s[6, -k:] = float("inf")
+    log(f"[topk] chunked stride={stride}")
+    split = smla.topk_per_row(s, k, lengths=lens_t)
+    whole = smla.topk_per_row(s, k, lengths=lens_t, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(split, whole)
+    ref = _oracle(s.cpu().numpy(), lens_t.cpu().numpy(), k)
+    g_np = split.cpu().numpy()
+    bad = np.nonzero((g_np != ref).any(axis=1))[0]
+    assert bad.size == 0, f"rows {bad[:5].tolist()} differ"
+
+
+def test_chunked_path_with_row_offsets_and_small_workspace():
+    """Rows given by offsets into one buffer; a workspace holding two rows runs several launches."""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    stride, k, R = 131072, 512, 7
+    buf = torch.randn(R * stride + 13, generator=g, device=DEV)
+    offs = torch.tensor([13 + r * stride - (r % 3) for r in range(R)], dtype=torch.int64, device=DEV)
+    lens = torch.tensor([stride, 100000, 513, 512, 16385, 131071, 20000], dtype=torch.int32, device=DEV)
+    per_row = smla.topk_workspace(1, k, stride, DEV).numel()
+    ws = torch.empty(2 * per_row + 100, dtype=torch.uint8, device=DEV)
+    got = smla.topk_per_row(buf, k, lengths=lens, row_offsets=offs, row_stride=stride, rows=R, workspace=ws)
+    whole = smla.topk_per_row(buf, k, lengths=lens, row_offsets=offs, row_stride=stride, rows=R, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(got, whole)
+    b = buf.cpu().numpy()
+    ref = O.topk_rows(b, lens.cpu().numpy(), k, row_offsets=offs.cpu().numpy(), row_stride=stride)
+    assert np.array_equal(got.cpu().numpy(), ref)
