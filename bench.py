@@ -30,7 +30,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=128, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")

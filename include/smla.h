@@ -19,7 +19,7 @@
  *     request on its own; top-k width, gather capacity and workspaces come from model capacity;
  *     length buffers are filled without a host sync).
  *   - "[Bugfix] Make DSV4 sparse MLA work end-to-end for plain decode, MTP, and DSpark"
- *     (vllm-project/vllm PR 51538), "What is fixed": lengths clamped to [0, stride] before any
+ *     (vllm-project/vllm PR 51538), section "Purpose": lengths clamped to [0, stride] before any
  *     decision, -1 padding of short rows, slot = block id * block size + offset, unsupported
  *     shapes rejected at init with the missing parameter named.
  *   - "[JJ] Preallocate DeepSeek V4 padded-query output" (local-inference-lab/vllm PR 671),

@@ -19,7 +19,7 @@ Sources (pages as titled; sections named):
   FlashMLA": decode gathers KV for the selected tokens and runs the same sparse
   attention as prefill; prefill chunks each request on its own.
 * "[Bugfix] Make DSV4 sparse MLA work end-to-end for plain decode, MTP, and
-  DSpark" (vllm-project/vllm PR 51538), "What is fixed", items "Negative
+  DSpark" (vllm-project/vllm PR 51538), section "Purpose", items "Negative
   indexer context lengths under MTP" and "Top-k kernels hardened against
   out-of-range lengths": lengths are clamped to [0, row stride] before any
   decision; rows with fewer candidates than k are padded with -1.  Item

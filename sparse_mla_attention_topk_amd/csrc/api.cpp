@@ -5,7 +5,7 @@
 // buffer.  Unsupported shapes are hard errors, never a fallback to another numeric path
 // ("[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", "Fused activation and FP8
 // quantization": missing support is an error; "[Bugfix] Make DSV4 sparse MLA work end-to-end ...",
-// "What is fixed", item "SM120 gate": reject at init and name the required shape).
+// section "Purpose", item "SM120 gate": reject at init and name the required shape).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>

@@ -3,7 +3,7 @@
 // What is computed (MQA over a shared latent; the decode path gathers the selected KV and runs the
 // same sparse attention as prefill: "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL",
 // section "Sparse MLA and FlashMLA"; slot = block id * block size + offset: "[Bugfix] Make DSV4
-// sparse MLA work end-to-end ...", "What is fixed", item "Graph replay and draft KV"):
+// sparse MLA work end-to-end ...", section "Purpose", item "Graph replay and draft KV"):
 //   s[h, j] = scale * <q[h, 0:576], K_j[0:576]>,  p = softmax_j(s),  out[h] = sum_j p[h, j] K_j[0:512]
 //   lse[h] = log sum_j exp(s[h, j])
 // for the tokens j listed in the row's index slots (entries < 0 skipped).

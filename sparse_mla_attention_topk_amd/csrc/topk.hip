@@ -2,7 +2,8 @@
 //
 // Method (deterministic sparse top-k of "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff
 // RL", section "Deterministic sparse top-k"; length clamping and -1 padding of "[Bugfix] Make DSV4
-// sparse MLA work end-to-end ...", "What is fixed"):
+// sparse MLA work end-to-end ...", section "Purpose", items "Negative indexer context lengths under
+// MTP" and "Top-k kernels hardened against out-of-range lengths"):
 //   * every score becomes an order-preserving 32-bit key (score_key); the composite order is
 //     (key descending, index ascending), so the n = min(k, L) selected candidates are exactly
 //       { j : key_j > T } U { the first `need` indices j with key_j == T }
