@@ -140,6 +140,8 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
  *   out: bf16 [rows, H, 512], 16-byte aligned; lse: fp32 [rows, H] or NULL.
  *   ws: attention workspace (256-byte aligned) of at least the size smla_workspace_size reports for
  *   a capacity with max_rows >= 1; rows beyond what it holds are processed in further launches.
+ *   It holds the bf16 split partials and their fp32 LSEs (k > 512 only); calls that share a
+ *   workspace must be ordered on one stream.
  * Requires H a multiple of 16 in [16, 128], 1 <= k <= 16384, rows >= 0, num_pages >= 1. */
 smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                    int64_t num_pages, const int32_t* block_table, int64_t bt_stride,

@@ -216,11 +216,12 @@ def topk_workspace(rows: int, k: int, row_stride: int, device) -> Optional[torch
 
 
 def attention_workspace(rows: int, H: int, k: int, device) -> Optional[torch.Tensor]:
-    """A workspace big enough for `rows` rows in one launch (None if k needs none)."""
+    """A zeroed workspace big enough for `rows` rows in one launch (None if k needs none).  The
+    library keeps its arrival counters at zero between calls, so it can be reused as is."""
     _, nbytes = workspace_size(Capacity.make(max(1, rows), k, H, 1))
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, idx: torch.Tensor,

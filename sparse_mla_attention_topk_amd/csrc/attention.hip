@@ -8,34 +8,37 @@
 //   lse[h] = log sum_j exp(s[h, j])
 // for the tokens j listed in the row's index slots (entries < 0 skipped).
 //
-// Work decomposition.  One workgroup (4 waves) owns one (row, split, 64-head block).  A split is
-// 512 consecutive index slots; the number of splits depends on k only, so the reduction order of a
-// row never depends on the batch.  The split's slots are processed in tiles of 32 tokens through a
-// 4-stage LDS ring: each wave gathers 8 token records per tile with direct-to-LDS 16-byte loads
-// (global_load_lds_dwordx4), so three tiles are in flight while one is consumed.  Records are
-// stored unpadded (1152 B); the 16-byte chunks of tile-local token t are XOR-swizzled with
-// f(t) = (t >> 1) & 7, the mapping measured to keep both operand read patterns below free of LDS
-// bank conflicts on gfx950.
+// Work decomposition.  One workgroup of 16 waves owns one (row, split, 64-head block) and is the only
+// workgroup on its CU.  A split is 512 consecutive index slots; the number of splits depends on k
+// only, so the reduction order of a row never depends on the batch.  The split's slots are processed
+// in tiles of 32 tokens through a 3-stage LDS ring.  The gather of a tile (36 loads of 1 KB, direct
+// to LDS with global_load_lds_dwordx4) is spread over all 16 waves: the rate at which random records
+// arrive grows with the number of waves per CU issuing loads, measured on MI355X.  Records are stored
+// unpadded (1152 B); the 16-byte chunks of tile-local token t are XOR-swizzled with f(t) = (t >> 1) & 7,
+// the mapping measured to keep the operand reads below free of LDS bank conflicts on gfx950.
 //
-// Waves pair up on 32 heads.  Wave w computes scores for its own 16 heads with Q in AGPRs:
-//   S^T[16 tok x 16 heads] = K[16 tok x 576] . Q^T        (A = K rows via ds_read_b128)
-// keeps the online-softmax state of those heads, and publishes its bf16 weights P (one 16-byte
-// fragment per lane) to its partner through LDS.  Each wave then accumulates the values for BOTH
-// head blocks of the pair over one half of the 512 value dims:
-//   O^T[16 dims x 16 heads] += V^T[16 dims x 32 tok] . P^T[32 tok x 16 heads]
-// (A = V^T via ds_read_b64_tr_b16 transposed LDS reads, shared by the two head blocks), so every
-// transposed read feeds two MFMAs.  The S^T accumulator layout already holds a head's token
-// weights in the B-operand layout of the value MFMA, so no register transpose is needed.
+// Roles (at most 128 registers per wave at 16 waves per CU):
+//   score waves 0..7:  wave (hb, half) computes the partial scores of heads hb*16 .. +16 over dims
+//                      288*half .. +288 for the tile's 32 tokens with Q in AGPRs:
+//                        S^T[16 tok x 16 heads] += K[16 tok x 32 dims] . Q^T    (A = K rows, ds_read_b128)
+//                      The second halves publish their partials through LDS; the first halves add them
+//                      (first half + second half, always in this order), keep the online-softmax state
+//                      of their 16 heads and publish the bf16 weights P and the rescale factors.
+//   value waves 8..15: wave 8 + v accumulates dims 64v .. +64 of all 64 heads:
+//                        O^T[16 dims x 16 heads] += V^T[16 dims x 32 tok] . P^T[32 tok x 16 heads]
+//                      (A = V^T via ds_read_b64_tr_b16 transposed reads, each feeding 4 head blocks).
+//   The S^T accumulator layout already holds a head's token weights in the B-operand layout of the
+//   value MFMA, so no register transpose is needed.
 //
 // Softmax is an fp32 online softmax in the exp2 domain, tiles in slot order.  A head's reference
 // max only moves when a tile's max exceeds it by more than 2^8 (a decision that depends on the
-// row's own scores only), so the accumulators are rescaled rarely.  A split that is not the only
-// one writes its normalized partial (O_s, lse_s) to the workspace and a combine kernel merges the
-// splits of a row in split order.  Nothing uses floating-point atomics.
+// row's own scores only), so the accumulators are rescaled rarely.  When a row has several splits,
+// each writes its normalized partial (O_s rounded to bf16, lse_s in fp32) to the workspace, and a
+// combine kernel merges the splits of a row in split order.  Nothing uses floating-point atomics.
 //
 // Invalid slots (index < 0, request/page out of range) load a valid dummy record, are zeroed in
-// LDS after arrival and get score -inf, so every wave issues exactly the same number of
-// direct-to-LDS loads per tile and the vmcnt bookkeeping below stays exact.
+// LDS after arrival and get score -inf, so every wave issues the same number of direct-to-LDS loads
+// for every tile and the vmcnt bookkeeping below stays exact.
 #include <math.h>
 
 #include <type_traits>
@@ -45,15 +48,16 @@
 
 namespace smla {
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 16;
+constexpr int kAttnThreads = kAttnWaves * kWave;               // 1024
+constexpr int kScoreWaves = 8;
 constexpr int kTileTok = 32;
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 constexpr int kTilesPerSplit = kSplitSlots / kTileTok;         // 16
 constexpr int kStageBytes = kTileTok * kBf16Record;             // 36864
-constexpr int kWaveTileBytes = kStageBytes / kAttnWaves;        // 9216: 8 records per wave
-constexpr int kLoadsPerWave = kWaveTileBytes / (16 * kWave);    // 9 direct-to-LDS loads per tile
-static_assert(kLoadsPerWave * 16 * kWave == kWaveTileBytes, "tile must split into whole wave loads");
+constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-LDS loads of 1 KB per tile
+static_assert(kTileLoads * 16 * kWave == kStageBytes, "tile must split into whole wave loads");
+constexpr int kMaxLoadsPerWave = (kTileLoads + kAttnWaves - 1) / kAttnWaves;   // 3 (waves 0..3), else 2
 constexpr uint32_t kNoToken = 0xffffffffu;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -80,8 +84,8 @@ struct AttnParams {
     int32_t row0;
     uint16_t* out;
     float* lse;
-    float* ws_o;
-    float* ws_lse;
+    uint16_t* ws_o;      // bf16 [rows][splits][H][512] split partials
+    float* ws_lse;       // fp32 [rows][splits][H]
 };
 
 // One direct-to-LDS 16-byte load: lane l's 16 bytes at `g` land at LDS byte lds_base + 16 l.  Issued
@@ -123,50 +127,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
 // in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
 
-// Instruction-group masks of __builtin_amdgcn_sched_group_barrier and the operand prefetch depths.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kQkAhead = 3;   // score steps (2 reads each) in flight ahead of their MFMAs
-constexpr int kPvAhead = 4;   // value dim-blocks (2 transposed reads each) in flight
-
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
     __shared__ uint32_t phys[kSplitSlots];
     __shared__ uint32_t tile_valid[kTilesPerSplit];
-    __shared__ __attribute__((aligned(16))) uint32_t pfrag[kAttnWaves][kWave * 4];   // P fragments
-    __shared__ float xalpha[kAttnWaves][16];    // per-head rescale factor of the current tile
-    __shared__ float xsum[kAttnWaves][16];      // per-head weight sums at the end
-    __shared__ int s_first, s_last, s_rescale;
+    __shared__ __attribute__((aligned(16))) f32x4_t xs[4][2][kWave];        // second-half partial scores
+    __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][kWave * 4];   // P fragments per head block
+    __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
+    __shared__ float xsum[4][16];      // per-head weight sums at the end
+    __shared__ int s_first, s_last;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane >> 4;
 
     // Work item: consecutive items (the splits / head blocks of one row) go to the same XCD, since
     // workgroups are dispatched round-robin over the 8 XCDs.
     const int nwg = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3, per = nwg >> 3, rem = nwg & 7;
     const int item = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int hb = item % p.n_hblocks;
+    const int hb_item = item % p.n_hblocks;
     const int rs = item / p.n_hblocks;
     const int split = rs % p.n_splits;
     const int rloc = rs / p.n_splits;
     const int64_t row = (int64_t)p.row0 + rloc;
+    const int head0 = hb_item * kHeadsPerBlock;
+    const int nhb = min(4, (p.H - head0) / 16);   // valid 16-head blocks of this item (H % 16 == 0)
 
-    // Heads: wave w scores heads hown .. hown+16; its pair (w, w^1) shares heads hpair .. hpair+32;
-    // for the values, wave w covers dims dim0 .. dim0+256 of both head blocks of the pair.
-    const int hown = hb * kHeadsPerBlock + wid * 16;
-    const int hpair = hb * kHeadsPerBlock + (wid >> 1) * 32;
-    const int dim0 = (wid & 1) * 256;
-    const bool own_ok = hown < p.H;
-    const bool blk0_ok = hpair < p.H;          // head block hpair .. +16
-    const bool blk1_ok = hpair + 16 < p.H;     // head block hpair+16 .. +32
+    const bool is_score = wid < kScoreWaves;
+    const int shb = wid & 3, half = (wid >> 2) & 1;   // score waves: head block, dim half
+    const int vdim0 = 64 * (wid - kScoreWaves);      // value waves: first of their 64 dims
+    const bool score_ok = is_score && shb < nhb;
 
-    // ---- Q (B operand of the score MFMA): lane holds head (lane & 15), dims 32kk + 8(lane >> 4) .. +8
-    bf16x8_t qv[18];
-    if (own_ok) {
-        const uint16_t* qrow = p.q + row * p.q_row_stride + (int64_t)(hown + (lane & 15)) * kDqk + 8 * (lane >> 4);
+    // ---- Q slice (B operand of the score MFMA): lane holds head (lane & 15), dims 288 half + 32 kk + 8 g .. +8
+    bf16x8_t qv[9];
+    if (score_ok) {
+        const uint16_t* qrow = p.q + row * p.q_row_stride + (int64_t)(head0 + shb * 16 + (lane & 15)) * kDqk +
+                               288 * half + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) qv[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+        for (int kk = 0; kk < 9; ++kk) qv[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 9; ++kk) qv[kk] = (bf16x8_t){};
     }
 
     // ---- A4: translate this split's slots to physical token records ----
@@ -177,31 +179,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     if (tid == 0) { s_first = kSplitSlots; s_last = -1; }
     if (tid < kTilesPerSplit) tile_valid[tid] = 0u;
     __syncthreads();
-    int32_t pos[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int j = tid + r * kAttnThreads;
-        const int jc = j < nslots ? j : 0;   // unconditional loads (clamped), so both are in flight together
-        pos[r] = p.idx[row * p.k + slot0 + jc];
-        if (!(j < nslots && req_ok)) pos[r] = -1;
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int j = tid + r * kAttnThreads;
+    if (tid < kSplitSlots) {
+        const int j = tid;
+        int32_t pos = p.idx[row * p.k + slot0 + (j < nslots ? j : 0)];
+        if (!(j < nslots && req_ok)) pos = -1;
         uint32_t ph = kNoToken;
-        const int64_t lp = pos[r] >> 6;
-        if (pos[r] >= 0 && lp < p.bt_stride) {
+        const int64_t lp = pos >> 6;
+        if (pos >= 0 && lp < p.bt_stride) {
             const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
-            if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(pos[r] & (kPage - 1));
+            if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(pos & (kPage - 1));
         }
         phys[j] = ph;
-        const uint64_t vb = __ballot(ph != kNoToken);
-        if (lane == 0 && vb) {
+        const uint64_t vbits = __ballot(ph != kNoToken);
+        if (lane == 0 && vbits) {
             const int jw = j - lane;    // first slot of this wave's 64
-            atomicMin(&s_first, jw + (int)__builtin_ctzll(vb));
-            atomicMax(&s_last, jw + 63 - (int)__builtin_clzll(vb));
-            atomicOr(&tile_valid[jw / kTileTok], (uint32_t)vb);
-            atomicOr(&tile_valid[jw / kTileTok + 1], (uint32_t)(vb >> 32));
+            atomicMin(&s_first, jw + (int)__builtin_ctzll(vbits));
+            atomicMax(&s_last, jw + 63 - (int)__builtin_clzll(vbits));
+            atomicOr(&tile_valid[jw / kTileTok], (uint32_t)vbits);
+            atomicOr(&tile_valid[jw / kTileTok + 1], (uint32_t)(vbits >> 32));
         }
     }
     // Drain every compiler-visible global load here: inside the tile loop the only outstanding
@@ -209,46 +204,50 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     wait_vmcnt<0>();
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qv[kk]));   // Q lives in AGPRs (MFMA B operand)
+    for (int kk = 0; kk < 9; ++kk) asm volatile("" : "+v"(qv[kk]));   // opaque: Q is never re-loaded
     const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
     const uint32_t dummy = s_last < 0 ? 0u : phys[s_first];
 
-    // ---- A5: gather.  Wave w fills tile-local tokens [8w, 8w+8) of a stage: load i of lane l covers
-    // LDS bytes w*9216 + 1024 i + 16 l, i.e. token t = 8w + (64i + l) / 72 at 16-byte position
-    // (64i + l) % 72, which holds the record's chunk position ^ f(t).
-    uint32_t dtok[kLoadsPerWave], doff[kLoadsPerWave];
+    // ---- A5: gather.  Load instruction i (0..35) of a tile covers stage bytes 1024 i .. +1024; wave w
+    // issues i = w, w + 16 and (waves 0..3) w + 32.  Lane l of instruction i moves 16-byte chunk
+    // Q = 64 i + l: token t = Q / 72 at 16-byte position Q % 72, which holds the record's chunk
+    // position ^ f(t).
+    const int nload = wid < kTileLoads - 2 * kAttnWaves ? 3 : 2;   // uniform in the wave
+    uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int qd = kWave * i + lane;
-        const int tt = qd / 72;
-        const int t = 8 * wid + tt;
-        dtok[i] = 4u * (uint32_t)t;
-        doff[i] = 16u * (uint32_t)((qd - 72 * tt) ^ swz_key(t));
+    for (int r = 0; r < kMaxLoadsPerWave; ++r) {
+        const int i = wid + kAttnWaves * r;
+        const int qd = kWave * (i < kTileLoads ? i : 0) + lane;
+        const int t = qd / 72;
+        dtok[r] = 4u * (uint32_t)t;
+        doff[r] = 16u * (uint32_t)((qd - 72 * t) ^ swz_key(t));
     }
-    const uint32_t wave_lds = lds_offset(ring) + (uint32_t)wid * kWaveTileBytes;
+    const uint32_t ring_lds = lds_offset(ring);
     auto issue_tile = [&](int tile, int stage) {
-        const uint32_t m0 = wave_lds + (uint32_t)stage * kStageBytes;
         const uint8_t* phys_tile = (const uint8_t*)phys + tile * kTileTok * 4;
-        const uint8_t* src[kLoadsPerWave];
+        const uint8_t* src[kMaxLoadsPerWave];
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) {   // all slot reads first: the asm below is a compiler barrier
-            uint32_t ph = *(const uint32_t*)(phys_tile + dtok[i]);
+        for (int r = 0; r < kMaxLoadsPerWave; ++r) {   // all slot reads first: the asm below is a compiler barrier
+            uint32_t ph = *(const uint32_t*)(phys_tile + dtok[r]);
             ph = ph == kNoToken ? dummy : ph;
-            src[i] = p.kv + (uint64_t)ph * kBf16Record + doff[i];
+            src[r] = p.kv + (uint64_t)ph * kBf16Record + doff[r];
         }
-#pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) dma_b128(src[i], m0 + 1024u * i);
+        const uint32_t m0 = ring_lds + (uint32_t)stage * kStageBytes + 1024u * (uint32_t)wid;
+        dma_b128(src[0], m0);
+        dma_b128(src[1], m0 + 1024u * kAttnWaves);
+        if (nload == 3) dma_b128(src[2], m0 + 2048u * kAttnWaves);
     };
-    // Zero this wave's records of invalid slots (after their dummy data has landed).
+    // Zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
-        const uint32_t wbits = (tile_valid[tile] >> (8 * wid)) & 0xffu;
-        if (wbits != 0xffu) {
-            uint8_t* wbase = ring + stage * kStageBytes + wid * kWaveTileBytes;
+        const uint32_t vm = tile_valid[tile];
+        if (vm != 0xffffffffu) {
+            uint8_t* sbase = ring + stage * kStageBytes;
 #pragma unroll
-            for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int qd = kWave * i + lane;
-                const int tt = qd / 72;
-                if (!((wbits >> tt) & 1u)) *(uint4*)(wbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
+            for (int r = 0; r < kMaxLoadsPerWave; ++r) {
+                if (r < nload) {
+                    const int qd = kWave * (wid + kAttnWaves * r) + lane;
+                    if (!((vm >> (qd / 72)) & 1u)) *(uint4*)(sbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
+                }
             }
         }
     };
@@ -257,7 +256,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     //  score operand: token (lane & 15) (+16 for the second block), chunk 4kk + g -> ka[kk & 1] + 128 (kk >> 1)
     //  transposed value reads: lane supplies token 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3 of a
     //  16-dim block db, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1) -> vb[db & 3] + 128 (db >> 2)
-    const int g = lane >> 4;
     uint32_t ka[2], vb[4];
     {
         const int lr = lane & 15;
@@ -270,207 +268,225 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         for (int j = 0; j < 4; ++j) vb[j] = tv * kBf16Record + 8 * (lane & 1) + 16 * ((2 * j + ((lane >> 1) & 1)) ^ fv);
     }
 
-    float m_run = -INFINITY, l_run = 0.f;   // own heads: exp2-domain reference max, weight sum (lane's tokens)
-    f32x4_t oacc[2][16];                    // [head block of the pair][16-dim block of this wave's half]
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int d = 0; d < 16; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
 
-    for (int it = 0; it < ntiles; ++it) {
+    // Start of tile `it`, common to both roles: wait for this wave's loads of the tile, zero its
+    // invalid chunks, make the tile visible (first barrier) and start the load of tile it+2 into the
+    // stage every wave finished with in tile it-1.
+    auto tile_top = [&](int it) {
         const int stage = it % kStages;
-        const int ahead = min(kStages - 2, ntiles - 1 - it);   // tiles issued after `it`
-        if (ahead >= 2) wait_vmcnt<2 * kLoadsPerWave>();
-        else if (ahead == 1) wait_vmcnt<kLoadsPerWave>();
-        else wait_vmcnt<0>();
+        if (it + 1 < ntiles) {   // tile it+1 stays in flight
+            if (nload == 3) wait_vmcnt<3>();
+            else wait_vmcnt<2>();
+        } else {
+            wait_vmcnt<0>();
+        }
         zero_invalid(it, stage);
         wait_lgkmcnt0();
-        __builtin_amdgcn_s_barrier();   // tile `it` visible; every wave is done with tile it-1
+        __builtin_amdgcn_s_barrier();
         if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
-        // Every wave passes both barriers of every tile, whether or not its heads exist.
-        const uint8_t* sb = ring + stage * kStageBytes;
-        const uint32_t vmask = tile_valid[it];
+        return (const uint8_t*)(ring + stage * kStageBytes);
+    };
 
-        // ---- A7 + A8: scores and online softmax of this wave's own 16 heads ----
-        if (own_ok) {
+    // The two roles run separate loops with the same three barriers per tile, so the registers of
+    // one role (Q, the score accumulators) and of the other (the output accumulators) can share storage.
+    float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
+    if (is_score) {
+        for (int it = 0; it < ntiles; ++it) {
+            const uint8_t* sb = tile_top(it);
+            // ---- A7: partial scores over this wave's half of the dims ----
             f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            if (score_ok) {
 #pragma unroll
-            for (int kk = 0; kk < 18; ++kk) {
-                const uint8_t* ap = sb + ka[kk & 1] + 128 * (kk >> 1);
-                const bf16x8_t a0 = *(const bf16x8_t*)(ap);
-                const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+                for (int kk = 0; kk < 9; ++kk) {
+                    const int kg = 9 * half + kk;      // kk step over the full 576 dims
+                    const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
+                    const bf16x8_t a0 = *(const bf16x8_t*)(ap);
+                    const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+                }
+                if (half) {
+                    xs[shb][0][lane] = s0;
+                    xs[shb][1][lane] = s1;
+                }
             }
-#pragma unroll
-            for (int i = 0; i < kQkAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-#pragma unroll
-            for (int i = 0; i < 18 - kQkAhead; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kQkAhead, 0);
+            wait_lgkmcnt0();                 // s_barrier does not wait for LDS writes by itself
+            __builtin_amdgcn_s_barrier();   // second-half partials published
 
-            // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
-            float sv[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { sv[i] = s0[i] * p.scale_log2; sv[4 + i] = s1[i] * p.scale_log2; }
-            if (vmask != 0xffffffffu) {
+            // ---- A8: online softmax of the first-half waves' 16 heads ----
+            if (score_ok && !half) {
+                const f32x4_t t0 = xs[shb][0][lane], t1 = xs[shb][1][lane];
+                const uint32_t vmask = tile_valid[it];
+                // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
+                float sv[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (!((vmask >> (4 * g + i)) & 1u)) sv[i] = -INFINITY;
-                    if (!((vmask >> (16 + 4 * g + i)) & 1u)) sv[4 + i] = -INFINITY;
+                    sv[i] = (s0[i] + t0[i]) * p.scale_log2;
+                    sv[4 + i] = (s1[i] + t1[i]) * p.scale_log2;
                 }
-            }
-            float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            mt = head_max(mt);
-            float alpha = 1.f;
-            if (mt > m_run + kRescaleSlack) {     // same decision in all four lanes of the head
-                alpha = __builtin_amdgcn_exp2f(m_run - mt);   // 0 while nothing has been accumulated
-                m_run = mt;
-                l_run *= alpha;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-            float pw[8];
+                if (vmask != 0xffffffffu) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pw[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
-                l_run += pw[j];
+                    for (int i = 0; i < 4; ++i) {
+                        if (!((vmask >> (4 * g + i)) & 1u)) sv[i] = -INFINITY;
+                        if (!((vmask >> (16 + 4 * g + i)) & 1u)) sv[4 + i] = -INFINITY;
+                    }
+                }
+                float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+                mt = head_max(mt);
+                float alpha = 1.f;
+                if (mt > m_run + kRescaleSlack) {     // same decision in all four lanes of the head
+                    alpha = __builtin_amdgcn_exp2f(m_run - mt);   // 0 while nothing has been accumulated
+                    m_run = mt;
+                    l_run *= alpha;
+                }
+                const float m_use = m_run == -INFINITY ? 0.f : m_run;
+                float pw[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pw[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
+                    l_run += pw[j];
+                }
+                uint4 pf;
+                pf.x = pack_bf16x2_hw(pw[0], pw[1]);
+                pf.y = pack_bf16x2_hw(pw[2], pw[3]);
+                pf.z = pack_bf16x2_hw(pw[4], pw[5]);
+                pf.w = pack_bf16x2_hw(pw[6], pw[7]);
+                *(uint4*)&pfrag[shb][4 * lane] = pf;
+                if (lane < 16) xalpha[shb][lane] = alpha;
+            } else if (!half && shb >= nhb) {   // head block beyond H: zero weights
+                *(uint4*)&pfrag[shb][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+                if (lane < 16) xalpha[shb][lane] = 1.f;
             }
-            uint4 pf;
-            pf.x = pack_bf16x2_hw(pw[0], pw[1]);
-            pf.y = pack_bf16x2_hw(pw[2], pw[3]);
-            pf.z = pack_bf16x2_hw(pw[4], pw[5]);
-            pf.w = pack_bf16x2_hw(pw[6], pw[7]);
-            *(uint4*)&pfrag[wid][4 * lane] = pf;
-            if (lane < 16) xalpha[wid][lane] = alpha;
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
         }
-        wait_lgkmcnt0();                 // s_barrier does not wait for LDS writes by itself
-        __builtin_amdgcn_s_barrier();   // P fragments and rescale factors of both waves published
-        if (!blk0_ok) continue;          // no head of this pair exists (uniform across the pair)
+        // ---- A10 (score waves): total weight and LSE of the first halves' heads ----
+        const float l_tot = head_sum(l_run);
+        if (score_ok && !half && lane < 16) xsum[shb][lane] = l_tot;
+        __syncthreads();
+        if (score_ok && !half && lane < 16) {
+            const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            const int head = head0 + shb * 16 + lane;
+            if (p.n_splits == 1) {
+                if (p.lse) p.lse[row * p.H + head] = lse_v;
+            } else {
+                p.ws_lse[((int64_t)rloc * p.n_splits + split) * p.H + head] = lse_v;
+            }
+        }
+    } else {
+        f32x4_t oacc[4][4];                 // [head block][16-dim block of the wave's 64 dims]
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < ntiles; ++it) {
+            const uint8_t* sb = tile_top(it);
+            __builtin_amdgcn_s_barrier();   // second-half partials published
+            __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
 
-        // ---- A9: O^T += V^T P^T for both head blocks of the pair over this wave's 256 dims ----
-        const int w0 = wid & ~1;
-        float a_blk[2];
-        a_blk[0] = blk0_ok ? xalpha[w0][lane & 15] : 1.f;
-        a_blk[1] = blk1_ok ? xalpha[w0 + 1][lane & 15] : 1.f;
-        bf16x8_t pb[2];
-        pb[0] = *(const bf16x8_t*)&pfrag[w0][4 * lane];
-        pb[1] = *(const bf16x8_t*)&pfrag[w0 + 1][4 * lane];
+            // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims ----
+            float a_blk[4];
+            bf16x8_t pb[4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (a_blk[b] != 1.f) {   // rare: a reference max moved (exact 1.0 otherwise)
+            for (int b = 0; b < 4; ++b) {
+                a_blk[b] = xalpha[b][lane & 15];
+                pb[b] = *(const bf16x8_t*)&pfrag[b][4 * lane];
+            }
 #pragma unroll
-                for (int d = 0; d < 16; ++d) {
-                    oacc[b][d][0] *= a_blk[b]; oacc[b][d][1] *= a_blk[b];
-                    oacc[b][d][2] *= a_blk[b]; oacc[b][d][3] *= a_blk[b];
+            for (int b = 0; b < 4; ++b) {
+                if (a_blk[b] != 1.f) {   // rare: a reference max moved (exact 1.0 otherwise)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        oacc[b][d][0] *= a_blk[b]; oacc[b][d][1] *= a_blk[b];
+                        oacc[b][d][2] *= a_blk[b]; oacc[b][d][3] *= a_blk[b];
+                    }
                 }
             }
-        }
-        const uint8_t* vp0 = sb + 128 * (dim0 / 64);
-        // Two copies of the value loop (both head blocks / first block only) keep the branch out of it.
-        auto value_pass = [&](auto both_blocks) {
+            const uint8_t* vp0 = sb + 128 * (vdim0 / 64);
 #pragma unroll
-            for (int d = 0; d < 16; ++d) {   // dim block within this wave's half
-                const uint8_t* vp = vp0 + vb[d & 3] + 128 * (d >> 2);
+            for (int d = 0; d < 4; ++d) {   // 16-dim block within this wave's 64 dims
+                const uint8_t* vp = vp0 + vb[d];
                 union { bf16x8_t v; i16x4_t h[2]; } va;
                 va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
                 va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
-                oacc[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[0], oacc[0][d], 0, 0, 0);
-                if constexpr (decltype(both_blocks)::value)
-                    oacc[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[1], oacc[1][d], 0, 0, 0);
-            }
-            constexpr int kM = decltype(both_blocks)::value ? 2 : 1;
 #pragma unroll
-            for (int i = 0; i < kPvAhead; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-#pragma unroll
-            for (int i = 0; i < 16 - kPvAhead; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, kM, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+                for (int b = 0; b < 4; ++b)
+                    oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[b], oacc[b][d], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kM * kPvAhead, 0);
-        };
-        if (blk1_ok) value_pass(std::true_type{});
-        else value_pass(std::false_type{});
-    }
-
-    // ---- A10: epilogue.  Own heads: total weight and LSE; both blocks: normalize and write ----
-    const float l_tot = head_sum(l_run);
-    if (own_ok && lane < 16) xsum[wid][lane] = l_tot;
-    __syncthreads();
-    if (!blk0_ok) return;
-    if (own_ok && lane < 16) {
-        const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-        const int64_t hix = row * p.H + hown + lane;
-        if (p.n_splits == 1) {
-            if (p.lse) p.lse[hix] = lse_v;
-        } else {
-            p.ws_lse[((int64_t)rloc * p.n_splits + split) * p.H + hown + lane] = lse_v;
         }
-    }
-    const int w0 = wid & ~1;
+        // ---- A10 (value waves): wait for the weight sums, normalize and write ----
+        __syncthreads();
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (b == 1 && !blk1_ok) break;
-        const float lt = xsum[w0 + b][lane & 15];
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int head = hpair + 16 * b + (lane & 15);
-        if (p.n_splits == 1) {
-            uint16_t* orow = p.out + (row * p.H + head) * (int64_t)kDv + dim0 + 4 * g;
+        for (int b = 0; b < 4; ++b) {
+            if (b >= nhb) break;
+            const float lt = xsum[b][lane & 15];
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const int head = head0 + 16 * b + (lane & 15);
+            uint16_t* orow = p.n_splits == 1
+                                 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * g
+                                 : p.ws_o + (((int64_t)rloc * p.n_splits + split) * p.H + head) * kDv + vdim0 + 4 * g;
 #pragma unroll
-            for (int d = 0; d < 16; ++d) {
+            for (int d = 0; d < 4; ++d) {
                 uint2 w;
                 w.x = pack_bf16x2_hw(oacc[b][d][0] * inv, oacc[b][d][1] * inv);
                 w.y = pack_bf16x2_hw(oacc[b][d][2] * inv, oacc[b][d][3] * inv);
                 *(uint2*)(orow + 16 * d) = w;
-            }
-        } else {
-            const int64_t part = ((int64_t)rloc * p.n_splits + split) * p.H + head;
-            float* wo = p.ws_o + part * kDv + dim0 + 4 * g;
-#pragma unroll
-            for (int d = 0; d < 16; ++d) {
-                f32x4_t v = {oacc[b][d][0] * inv, oacc[b][d][1] * inv, oacc[b][d][2] * inv, oacc[b][d][3] * inv};
-                *(f32x4_t*)(wo + 16 * d) = v;
             }
         }
     }
 }
 
 // A11: merge the splits of each row in split order:  LSE = m + log sum_s e^(lse_s - m),
-// out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16.  One thread per (row, head, 4 dims).
-__global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ ws_o,
+// out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16.  64 threads per (row, head), 8 dims each.
+__global__ __launch_bounds__(256) void split_combine_kernel(const uint16_t* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse, int S, int H,
                                                             int row0, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
-    const int pairs = H / 2;
-    const int rloc = blockIdx.x / pairs;
-    const int head = (blockIdx.x % pairs) * 2 + (threadIdx.x >> 7);
-    const int d = 4 * (threadIdx.x & 127);
+    const int hq = H / 4;
+    const int rloc = blockIdx.x / hq;
+    const int head = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
+    const int d = 8 * (threadIdx.x & 63);
     const float* ls = ws_lse + (int64_t)rloc * S * H + head;
     float m = -INFINITY;
     for (int s = 0; s < S; ++s) m = fmaxf(m, ls[(int64_t)s * H]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float LSE = -INFINITY;
     if (m != -INFINITY) {
         float tot = 0.f;
         for (int s = 0; s < S; ++s) tot += expf(ls[(int64_t)s * H] - m);
         LSE = m + logf(tot);
         const float inv = 1.f / tot;
-        for (int s = 0; s < S; ++s) {
-            const float w = expf(ls[(int64_t)s * H] - m) * inv;
-            const f32x4_t o = *(const f32x4_t*)(ws_o + (((int64_t)rloc * S + s) * H + head) * kDv + d);
-            acc[0] += w * o[0]; acc[1] += w * o[1]; acc[2] += w * o[2]; acc[3] += w * o[3];
+        constexpr int kGroup = 4;   // splits whose loads are in flight together
+        for (int s0 = 0; s0 < S; s0 += kGroup) {
+            uint4 v[kGroup];
+            float w[kGroup];
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const int s = s0 + j < S ? s0 + j : S - 1;   // loads stay unconditional (clamped)
+                w[j] = s0 + j < S ? expf(ls[(int64_t)s * H] - m) * inv : 0.f;
+                v[j] = *(const uint4*)(ws_o + (((int64_t)rloc * S + s) * H + head) * kDv + d);
+            }
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += w[j] * __uint_as_float(wd[e] << 16);
+                    acc[2 * e + 1] += w[j] * __uint_as_float(wd[e] & 0xffff0000u);
+                }
+            }
         }
     }
     const int64_t orow = ((int64_t)row0 + rloc) * H + head;
-    uint2 w;
-    w.x = pack_bf16x2_hw(acc[0], acc[1]);
-    w.y = pack_bf16x2_hw(acc[2], acc[3]);
-    *(uint2*)(out + orow * kDv + d) = w;
+    uint4 o;
+    o.x = pack_bf16x2_hw(acc[0], acc[1]);
+    o.y = pack_bf16x2_hw(acc[2], acc[3]);
+    o.z = pack_bf16x2_hw(acc[4], acc[5]);
+    o.w = pack_bf16x2_hw(acc[6], acc[7]);
+    *(uint4*)(out + orow * kDv + d) = o;
     if (d == 0 && lse) lse[orow] = LSE;
 }
 
@@ -503,14 +519,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     for (int row0 = 0; row0 < a.rows; row0 += rows_per_launch) {
         const int n = min(rows_per_launch, a.rows - row0);
         p.row0 = row0;
-        p.ws_o = (float*)a.ws;
-        p.ws_lse = per_row > 0 ? (float*)a.ws + (size_t)n * p.n_splits * a.H * kDv : nullptr;
+        // Workspace regions for a launch of rows_per_launch rows: partials, then LSEs.
+        p.ws_o = per_row > 0 ? (uint16_t*)a.ws : nullptr;
+        p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch * attn_ws_o_bytes_per_row(a.H, a.k))
+                               : nullptr;
         const int grid = n * p.n_splits * p.n_hblocks;
         hipLaunchKernelGGL(sparse_mla_bf16_kernel, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.n_splits > 1) {
-            hipLaunchKernelGGL(split_combine_kernel, dim3(n * (a.H / 2)), dim3(256), 0, stream, p.ws_o, p.ws_lse,
+            hipLaunchKernelGGL(split_combine_kernel, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o, p.ws_lse,
                                p.n_splits, a.H, row0, p.out, p.lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;

@@ -13,11 +13,13 @@ constexpr int kHeadsPerBlock = 64; // heads handled by one workgroup (4 waves x 
 
 inline int attn_num_splits(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
 
-// Bytes of split partials per query row (0 when k fits one split).
+// Workspace of the attention entry points, per query row (0 when k fits one split): the bf16
+// partial outputs of every (split, head), then their fp32 LSEs.
+inline size_t attn_ws_o_bytes_per_row(int H, int k) { return (size_t)attn_num_splits(k) * H * 512 * 2; }
+inline size_t attn_ws_lse_bytes_per_row(int H, int k) { return (size_t)attn_num_splits(k) * H * 4; }
 inline size_t attn_ws_bytes_per_row(int H, int k) {
-    const int S = attn_num_splits(k);
-    if (S <= 1) return 0;
-    return (size_t)S * (size_t)H * (size_t)(512 + 1) * sizeof(float);
+    if (attn_num_splits(k) <= 1) return 0;
+    return attn_ws_o_bytes_per_row(H, k) + attn_ws_lse_bytes_per_row(H, k);
 }
 
 struct AttnArgs {

@@ -80,11 +80,11 @@ def test_workspace_size_derives_from_capacity_only():
     tk_many, _ = smla.workspace_size(_cap(max_rows=4096, max_k=512, num_heads=64, max_candidates=120000))
     assert tk_many == 255 * (256 + 8 * 12288 * 8)   # the split serves calls of fewer than 256 rows
     _, at = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=65536))
-    assert at == 64 * 4 * 64 * 513 * 4          # rows x splits x heads x (512 + 1) fp32
+    assert at == 64 * 4 * 64 * (512 * 2 + 4)    # rows x splits x heads x (bf16 partial + fp32 LSE)
     _, at1 = smla.workspace_size(_cap(max_rows=1, max_k=512, num_heads=64))
     assert at1 == 0                              # a single split needs no partials
     _, at2 = smla.workspace_size(_cap(max_rows=3, max_k=513, num_heads=16))
-    assert at2 == 3 * 2 * 16 * 513 * 4
+    assert at2 == 3 * 2 * 16 * (512 * 2 + 4)
 
 
 P = ctypes.c_void_p
