@@ -215,10 +215,10 @@ def topk_workspace(rows: int, k: int, row_stride: int, device) -> Optional[torch
     return torch.empty(tk, dtype=torch.uint8, device=device)
 
 
-def attention_workspace(rows: int, H: int, k: int, device) -> Optional[torch.Tensor]:
+def attention_workspace(rows: int, H: int, k: int, device, kv_dtype: int = KV_BF16) -> Optional[torch.Tensor]:
     """A zeroed workspace big enough for `rows` rows in one launch (None if k needs none).  The
     library keeps its arrival counters at zero between calls, so it can be reused as is."""
-    _, nbytes = workspace_size(Capacity.make(max(1, rows), k, H, 1))
+    _, nbytes = workspace_size(Capacity.make(max(1, rows), k, H, 1, kv_dtype=kv_dtype))
     if nbytes == 0:
         return None
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -247,7 +247,7 @@ def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tens
         _require(row_req, "row_req", torch.int32, dev)
     out, lse = _attn_outputs(rows, H, dev, out, lse)
     if workspace is None:
-        workspace = attention_workspace(rows, H, k, dev)
+        workspace = attention_workspace(rows, H, k, dev, _kv_dtype_of(kv, kv_dtype))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     bt2 = block_table if block_table.dim() == 2 else block_table.view(1, -1)
     _check(lib.smla_sparse_mla_decode(_ptr(q), q.stride(0), _ptr(kv), _kv_dtype_of(kv, kv_dtype), kv.shape[0],
@@ -274,7 +274,7 @@ def sparse_mla_prefill_chunk(q: torch.Tensor, kv: torch.Tensor, block_table_row:
     k = idx.shape[-1]
     out, lse = _attn_outputs(T, H, dev, out, lse)
     if workspace is None:
-        workspace = attention_workspace(T, H, k, dev)
+        workspace = attention_workspace(T, H, k, dev, _kv_dtype_of(kv, kv_dtype))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.smla_sparse_mla_prefill_chunk(_ptr(q), q.stride(0), _ptr(kv), _kv_dtype_of(kv, kv_dtype), kv.shape[0],
                                              _ptr(block_table_row), block_table_row.numel(), _ptr(idx), T, H, k,

@@ -51,9 +51,9 @@ smla_status check_k(int32_t k, const char* name) {
 }
 
 smla_status check_kv_dtype(int32_t d) {
-    if (d != SMLA_KV_BF16)
-        return fail(SMLA_ERR_UNSUPPORTED,
-                    "kv_dtype=%d is not supported by this build; supported: %d (SMLA_KV_BF16)", d, (int)SMLA_KV_BF16);
+    if (d != SMLA_KV_BF16 && d != SMLA_KV_FP8_E4M3_G128)
+        return fail(SMLA_ERR_UNSUPPORTED, "kv_dtype=%d is not supported; supported: %d (SMLA_KV_BF16), %d (SMLA_KV_FP8_E4M3_G128)",
+                    d, (int)SMLA_KV_BF16, (int)SMLA_KV_FP8_E4M3_G128);
     return SMLA_OK;
 }
 
@@ -97,7 +97,7 @@ smla_status check_attention(const void* q, int64_t q_row_stride, const void* kv,
     if (!aligned(block_table, 4)) return fail(SMLA_ERR_ALIGNMENT, "block_table must be 4-byte aligned");
     if (!aligned(idx, 4)) return fail(SMLA_ERR_ALIGNMENT, "idx must be 4-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(SMLA_ERR_ALIGNMENT, "lse must be 4-byte aligned");
-    const size_t per_row = smla::attn_ws_bytes_per_row(H, k);
+    const size_t per_row = smla::attn_ws_bytes_per_row(H, k, kv_dtype);
     if (per_row > 0) {
         if (!ws) return fail(SMLA_ERR_WORKSPACE, "ws is NULL but k=%d needs %zu workspace bytes per row", k, per_row);
         if (!aligned(ws, 256)) return fail(SMLA_ERR_ALIGNMENT, "ws must be 256-byte aligned");
@@ -144,7 +144,7 @@ smla_status smla_workspace_size(const smla_capacity* cap, size_t* topk_ws_bytes,
         *topk_ws_bytes = per_row * rows;
     }
     if (attn_ws_bytes) {
-        const size_t per_row = smla::attn_ws_bytes_per_row(cap->num_heads, cap->max_k);
+        const size_t per_row = smla::attn_ws_bytes_per_row(cap->num_heads, cap->max_k, cap->kv_dtype);
         *attn_ws_bytes = per_row * (size_t)cap->max_rows;
     }
     return ok();

@@ -58,6 +58,14 @@ constexpr int kStageBytes = kTileTok * kBf16Record;             // 36864
 constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-LDS loads of 1 KB per tile
 static_assert(kTileLoads * 16 * kWave == kStageBytes, "tile must split into whole wave loads");
 constexpr int kMaxLoadsPerWave = (kTileLoads + kAttnWaves - 1) / kAttnWaves;   // 3 (waves 0..3), else 2
+// FP8 records: [512 e4m3 codes | 4 fp32 scales, one per 128 latent dims | 64 bf16 rope] = 656 B,
+// 41 chunks of 16 B.  A tile's 1312 chunks take 21 loads of 1 KB, the last with 32 active lanes.
+
+constexpr int kFp8Chunks = kFp8Record / 16;                           // 41
+constexpr int kFp8StageBytes = kTileTok * kFp8Record;                 // 20992
+constexpr int kFp8TileChunks = kTileTok * kFp8Chunks;                 // 1312
+constexpr int kFp8TileLoads = (kFp8TileChunks + kWave - 1) / kWave;   // 21
+static_assert(kFp8StageBytes % 16 == 0, "FP8 stages must stay 16-byte aligned");
 constexpr uint32_t kNoToken = 0xffffffffu;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -84,7 +92,7 @@ struct AttnParams {
     int32_t row0;
     uint16_t* out;
     float* lse;
-    uint16_t* ws_o;      // bf16 [rows][splits][H][512] split partials
+    void* ws_o;          // [rows][splits][H][512] split partials: bf16 (bf16 cache) or fp32 (FP8 cache)
     float* ws_lse;       // fp32 [rows][splits][H]
 };
 
@@ -123,16 +131,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
     return r.u;
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
+    typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
+    union { h2 v; uint32_t u; } r;
+    r.v = __builtin_convertvector((f2){lo, hi}, h2);   // round to nearest even
+    return r.u;
+}
+
+// Two bf16 values holding small integers times powers of two (e4m3 codes) -> the same two values in
+// fp16 (exact: every e4m3 value is an fp16 value, so the truncating conversion does not round).
+__device__ __forceinline__ uint32_t bf16x2_code_to_f16x2(uint32_t w) {
+    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.f, 0.f)) v; uint32_t u; } r;
+    r.v = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    return r.u;
+}
+
 // A head's reference max only moves when a tile's max exceeds it by more than this (log2 units);
 // in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
 
-__global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
+// KV_FP8: the ring holds FP8 records, and every tile is first expanded into one bf16 tile with the
+// layout of the bf16 path: the e4m3 codes exactly (every e4m3 value is a bf16 value), the rope copied,
+// and the four fp32 group scales of each token into a small table.  The scales are applied in fp32:
+// the score waves keep one partial per 128-dim scale group and sum scale x partial; the softmax
+// publishes, for every group, the weights times that group's scales rounded to fp16, and a value
+// wave, whose 64 dims lie in one group, runs the value product in fp16 (the codes are exact in fp16
+// too) with that group's weights.  At the magnitudes these scales produce, rounding the scaled
+// values, or the scaled weights, to bf16 costs far more accuracy than the fp16 weights.
+template <bool KV_FP8>
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
+    constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + kStageBytes : kStages * kStageBytes;
+    constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
+    constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
     __shared__ uint32_t phys[kSplitSlots];
     __shared__ uint32_t tile_valid[kTilesPerSplit];
     __shared__ __attribute__((aligned(16))) f32x4_t xs[4][2][kWave];        // second-half partial scores
-    __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][kWave * 4];   // P fragments per head block
+    // P fragments per head block; FP8: one set per scale group (weights times the group's scales)
+    __shared__ __attribute__((aligned(16))) uint32_t pfrag[KV_FP8 ? 4 : 1][4][kWave * 4];
+    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? kTileTok : 1][4];   // FP8: scales of the tile's tokens
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     __shared__ float xsum[4][16];      // per-head weight sums at the end
     __shared__ int s_first, s_last;
@@ -208,21 +248,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
     const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
     const uint32_t dummy = s_last < 0 ? 0u : phys[s_first];
 
-    // ---- A5: gather.  Load instruction i (0..35) of a tile covers stage bytes 1024 i .. +1024; wave w
-    // issues i = w, w + 16 and (waves 0..3) w + 32.  Lane l of instruction i moves 16-byte chunk
-    // Q = 64 i + l: token t = Q / 72 at 16-byte position Q % 72, which holds the record's chunk
-    // position ^ f(t).
-    const int nload = wid < kTileLoads - 2 * kAttnWaves ? 3 : 2;   // uniform in the wave
+    // ---- A5: gather.  Load instruction i of a tile covers stage bytes 1024 i .. +1024; wave w issues
+    // i = w, w + 16, w + 32 (those below the tile's count: 36 for bf16, 21 for FP8).  Lane l of
+    // instruction i moves 16-byte chunk Q = 64 i + l of the stage.  bf16: token t = Q / 72 at 16-byte
+    // position Q % 72, which holds the record's chunk position ^ f(t).  FP8: token t = Q / 41, chunk
+    // Q % 41 in place; chunks past the tile (Q >= 1312, lanes 32..63 of load 20) are not loaded.
+    constexpr int kLoads = KV_FP8 ? kFp8TileLoads : kTileLoads;
+    const int nload = (wid < kLoads ? 1 : 0) + (wid + kAttnWaves < kLoads ? 1 : 0) +
+                      (wid + 2 * kAttnWaves < kLoads ? 1 : 0);   // loads of this wave per tile (uniform)
     uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
 #pragma unroll
     for (int r = 0; r < kMaxLoadsPerWave; ++r) {
         const int i = wid + kAttnWaves * r;
-        const int qd = kWave * (i < kTileLoads ? i : 0) + lane;
-        const int t = qd / 72;
-        dtok[r] = 4u * (uint32_t)t;
-        doff[r] = 16u * (uint32_t)((qd - 72 * t) ^ swz_key(t));
+        const int qd = kWave * (i < kLoads ? i : 0) + lane;
+        if (KV_FP8) {
+            const int qc = qd < kFp8TileChunks ? qd : kFp8TileChunks - 1;
+            const int t = qc / kFp8Chunks;
+            dtok[r] = 4u * (uint32_t)t;
+            doff[r] = 16u * (uint32_t)(qc - kFp8Chunks * t);
+        } else {
+            const int t = qd / 72;
+            dtok[r] = 4u * (uint32_t)t;
+            doff[r] = 16u * (uint32_t)((qd - 72 * t) ^ swz_key(t));
+        }
     }
     const uint32_t ring_lds = lds_offset(ring);
+    const bool half_load = KV_FP8 && wid + kAttnWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
     auto issue_tile = [&](int tile, int stage) {
         const uint8_t* phys_tile = (const uint8_t*)phys + tile * kTileTok * 4;
         const uint8_t* src[kMaxLoadsPerWave];
@@ -230,14 +281,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
         for (int r = 0; r < kMaxLoadsPerWave; ++r) {   // all slot reads first: the asm below is a compiler barrier
             uint32_t ph = *(const uint32_t*)(phys_tile + dtok[r]);
             ph = ph == kNoToken ? dummy : ph;
-            src[r] = p.kv + (uint64_t)ph * kBf16Record + doff[r];
+            src[r] = p.kv + (uint64_t)ph * kRecBytes + doff[r];
         }
-        const uint32_t m0 = ring_lds + (uint32_t)stage * kStageBytes + 1024u * (uint32_t)wid;
-        dma_b128(src[0], m0);
-        dma_b128(src[1], m0 + 1024u * kAttnWaves);
-        if (nload == 3) dma_b128(src[2], m0 + 2048u * kAttnWaves);
+        const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)wid;
+        if (!KV_FP8) {
+            dma_b128(src[0], m0);
+            dma_b128(src[1], m0 + 1024u * kAttnWaves);
+            if (nload == 3) dma_b128(src[2], m0 + 2048u * kAttnWaves);
+        } else {
+            if (nload == 1) {
+                dma_b128(src[0], m0);
+            } else if (!half_load) {
+                dma_b128(src[0], m0);
+                dma_b128(src[1], m0 + 1024u * kAttnWaves);
+            } else {
+                dma_b128(src[0], m0);
+                if (lane < kFp8TileChunks - kWave * (kFp8TileLoads - 1)) dma_b128(src[1], m0 + 1024u * kAttnWaves);
+            }
+        }
     };
-    // Zero this wave's chunks of invalid tokens (after their dummy data has landed).
+    // bf16: zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
         const uint32_t vm = tile_valid[tile];
         if (vm != 0xffffffffu) {
@@ -249,6 +312,46 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
                     if (!((vm >> (qd / 72)) & 1u)) *(uint4*)(sbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
                 }
             }
+        }
+    };
+    // FP8 (A6): expand the stage's records into the bf16 tile, done by the 512 threads of the score
+    // waves (the value waves hold their accumulators).  Unit u (tid and tid + 512) converts codes
+    // 16c .. 16c+15 of token t = u / 32 (c = u % 32) into bf16 chunks 2c, 2c+1 and, for c % 8 == 0,
+    // stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.  Invalid
+    // tokens become zeros (codes, rope and scales).
+    uint8_t* const btile = ring + kStages * kFp8StageBytes;
+    auto dequant_tile = [&](int tile, int stage) {
+        const uint8_t* st = ring + stage * kFp8StageBytes;
+        const uint32_t vm = tile_valid[tile];
+        // Invalid tokens are cleared with a bit mask (a select between vectors would go through
+        // scratch memory, whose wait would also wait for the tile loads in flight).
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int u = tid + 512 * h;
+            const int t = u >> 5, c = u & 31;
+            const uint32_t keep = 0u - ((vm >> t) & 1u);
+            const int f = swz_key(t);
+            const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
+            if ((c & 7) == 0) tscale[t][c >> 3] = keep ? *(const float*)(st + t * kFp8Record + 512 + 4 * (c >> 3)) : 0.f;
+            uint8_t* dst = btile + t * kBf16Record;
+            // codes 0..7 of the chunk -> bf16 chunk 2c, codes 8..15 -> bf16 chunk 2c+1 (exact)
+            auto expand = [&](uint32_t w0, uint32_t w1) {
+                const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+                const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+                const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+                const auto g2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+                return make_uint4(pack_bf16x2_hw(a[0], a[1]) & keep, pack_bf16x2_hw(b[0], b[1]) & keep,
+                                  pack_bf16x2_hw(e[0], e[1]) & keep, pack_bf16x2_hw(g2[0], g2[1]) & keep);
+            };
+            *(uint4*)(dst + 16 * ((2 * c) ^ f)) = expand(codes.x, codes.y);
+            *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) = expand(codes.z, codes.w);
+        }
+        if (tid < kTileTok * 8) {
+            const int rt = tid >> 3, j = tid & 7;
+            const uint32_t keep = 0u - ((vm >> rt) & 1u);
+            uint4 r = *(const uint4*)(st + rt * kFp8Record + 528 + 16 * j);
+            r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
+            *(uint4*)(btile + rt * kBf16Record + 16 * ((64 + j) ^ swz_key(rt))) = r;
         }
     };
 
@@ -270,41 +373,86 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
 
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
 
-    // Start of tile `it`, common to both roles: wait for this wave's loads of the tile, zero its
-    // invalid chunks, make the tile visible (first barrier) and start the load of tile it+2 into the
-    // stage every wave finished with in tile it-1.
-    auto tile_top = [&](int it) {
+    // Start of tile `it`, common to both roles: wait for this wave's loads of the tile, make the tile
+    // visible (first barrier) and start the load of tile it+2 into the stage every wave finished
+    // with in tile it-1.  bf16: invalid tokens are zeroed in the stage before the barrier.  FP8: the
+    // stage is expanded into the bf16 tile after it (the previous tile's bf16 data is no longer read),
+    // followed by a second barrier.
+    auto tile_top = [&](int it, auto expands) {
         const int stage = it % kStages;
         if (it + 1 < ntiles) {   // tile it+1 stays in flight
             if (nload == 3) wait_vmcnt<3>();
-            else wait_vmcnt<2>();
+            else if (nload == 2) wait_vmcnt<2>();
+            else wait_vmcnt<1>();
         } else {
             wait_vmcnt<0>();
         }
-        zero_invalid(it, stage);
+        if (!KV_FP8) zero_invalid(it, stage);
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        if (KV_FP8) {
+            if constexpr (decltype(expands)::value) dequant_tile(it, stage);
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();
+            return (const uint8_t*)btile;
+        }
         return (const uint8_t*)(ring + stage * kStageBytes);
     };
 
-    // The two roles run separate loops with the same three barriers per tile, so the registers of
+    // The two roles run separate loops with the same barriers per tile, so the registers of
     // one role (Q, the score accumulators) and of the other (the output accumulators) can share storage.
     float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
     if (is_score) {
         for (int it = 0; it < ntiles; ++it) {
-            const uint8_t* sb = tile_top(it);
+            const uint8_t* sb = tile_top(it, std::true_type{});
             // ---- A7: partial scores over this wave's half of the dims ----
             f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
             if (score_ok) {
+                if constexpr (!KV_FP8) {
 #pragma unroll
-                for (int kk = 0; kk < 9; ++kk) {
-                    const int kg = 9 * half + kk;      // kk step over the full 576 dims
-                    const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
-                    const bf16x8_t a0 = *(const bf16x8_t*)(ap);
-                    const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+                    for (int kk = 0; kk < 9; ++kk) {
+                        const int kg = 9 * half + kk;      // kk step over the full 576 dims
+                        const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
+                        const bf16x8_t a0 = *(const bf16x8_t*)(ap);
+                        const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
+                        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+                    }
+                } else {
+                    // One partial per scale group.  Steps kk (32 dims each) of the first half: 0..3 group 0,
+                    // 4..7 group 1, 8 group 2; of the second half: 9..11 group 2, 12..15 group 3, 16..17 rope.
+                    f32x4_t acc[3][2];
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) acc[j][0] = acc[j][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    auto step = [&](int kk, int slot) {
+                        const int kg = 9 * half + kk;
+                        const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
+                        const bf16x8_t a0 = *(const bf16x8_t*)(ap);
+                        const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                        acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], acc[slot][0], 0, 0, 0);
+                        acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], acc[slot][1], 0, 0, 0);
+                    };
+                    if (!half) {
+#pragma unroll
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2));
+                    } else {
+#pragma unroll
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 3 ? 0 : (kk < 7 ? 1 : 2));
+                    }
+                    // lane: tokens 4g + i (block 0) and 16 + 4g + i (block 1); scale slots per half
+                    const int gs0 = half ? 2 : 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x4_t ta = *(const f32x4_t*)tscale[4 * g + i];
+                        const f32x4_t tb = *(const f32x4_t*)tscale[16 + 4 * g + i];
+                        const float a0s = half ? ta[2] : ta[0], a1s = half ? ta[3] : ta[1];
+                        const float b0s = half ? tb[2] : tb[0], b1s = half ? tb[3] : tb[1];
+                        const float a2s = half ? 1.f : ta[2], b2s = half ? 1.f : tb[2];
+                        s0[i] = a0s * acc[0][0][i] + a1s * acc[1][0][i] + a2s * acc[2][0][i];
+                        s1[i] = b0s * acc[0][1][i] + b1s * acc[1][1][i] + b2s * acc[2][1][i];
+                    }
+                    (void)gs0;
                 }
                 if (half) {
                     xs[shb][0][lane] = s0;
@@ -348,15 +496,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
                     pw[j] = __builtin_amdgcn_exp2f(sv[j] - m_use);
                     l_run += pw[j];
                 }
-                uint4 pf;
-                pf.x = pack_bf16x2_hw(pw[0], pw[1]);
-                pf.y = pack_bf16x2_hw(pw[2], pw[3]);
-                pf.z = pack_bf16x2_hw(pw[4], pw[5]);
-                pf.w = pack_bf16x2_hw(pw[6], pw[7]);
-                *(uint4*)&pfrag[shb][4 * lane] = pf;
+                if constexpr (!KV_FP8) {
+                    uint4 pf;
+                    pf.x = pack_bf16x2_hw(pw[0], pw[1]);
+                    pf.y = pack_bf16x2_hw(pw[2], pw[3]);
+                    pf.z = pack_bf16x2_hw(pw[4], pw[5]);
+                    pf.w = pack_bf16x2_hw(pw[6], pw[7]);
+                    *(uint4*)&pfrag[0][shb][4 * lane] = pf;
+                } else {
+                    f32x4_t tsc[8];   // scales of the lane's 8 tokens
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        tsc[i] = *(const f32x4_t*)tscale[4 * g + i];
+                        tsc[4 + i] = *(const f32x4_t*)tscale[16 + 4 * g + i];
+                    }
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {   // fp16 weights: the value product runs in fp16
+                        uint4 pf;
+                        pf.x = pack_f16x2_rne(pw[0] * tsc[0][gg], pw[1] * tsc[1][gg]);
+                        pf.y = pack_f16x2_rne(pw[2] * tsc[2][gg], pw[3] * tsc[3][gg]);
+                        pf.z = pack_f16x2_rne(pw[4] * tsc[4][gg], pw[5] * tsc[5][gg]);
+                        pf.w = pack_f16x2_rne(pw[6] * tsc[6][gg], pw[7] * tsc[7][gg]);
+                        *(uint4*)&pfrag[gg][shb][4 * lane] = pf;
+                    }
+                }
                 if (lane < 16) xalpha[shb][lane] = alpha;
             } else if (!half && shb >= nhb) {   // head block beyond H: zero weights
-                *(uint4*)&pfrag[shb][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int gg = 0; gg < (KV_FP8 ? 4 : 1); ++gg) *(uint4*)&pfrag[gg][shb][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
                 if (lane < 16) xalpha[shb][lane] = 1.f;
             }
             wait_lgkmcnt0();
@@ -382,17 +549,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
 #pragma unroll
             for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         for (int it = 0; it < ntiles; ++it) {
-            const uint8_t* sb = tile_top(it);
+            const uint8_t* sb = tile_top(it, std::false_type{});
             __builtin_amdgcn_s_barrier();   // second-half partials published
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
 
             // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims ----
             float a_blk[4];
-            bf16x8_t pb[4];
+            uint4 pb[4];   // B operands: bf16 weights, or (FP8) fp16 weights times the wave's group scales
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 a_blk[b] = xalpha[b][lane & 15];
-                pb[b] = *(const bf16x8_t*)&pfrag[b][4 * lane];
+                pb[b] = *(const uint4*)&pfrag[KV_FP8 ? (vdim0 >> 7) : 0][b][4 * lane];
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -408,13 +575,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
 #pragma unroll
             for (int d = 0; d < 4; ++d) {   // 16-dim block within this wave's 64 dims
                 const uint8_t* vp = vp0 + vb[d];
-                union { bf16x8_t v; i16x4_t h[2]; } va;
+                union { bf16x8_t v; i16x4_t h[2]; uint4 u; f16x8_t f; } va;
                 va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
                 va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
+                if constexpr (!KV_FP8) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[b], oacc[b][d], 0, 0, 0);
+                    for (int b = 0; b < 4; ++b) {
+                        union { uint4 u; bf16x8_t v; } pv;
+                        pv.u = pb[b];
+                        oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pv.v, oacc[b][d], 0, 0, 0);
+                    }
+                } else {
+                    va.u = make_uint4(bf16x2_code_to_f16x2(va.u.x), bf16x2_code_to_f16x2(va.u.y),
+                                      bf16x2_code_to_f16x2(va.u.z), bf16x2_code_to_f16x2(va.u.w));
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        union { uint4 u; f16x8_t v; } pv;
+                        pv.u = pb[b];
+                        oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.f, pv.v, oacc[b][d], 0, 0, 0);
+                    }
+                }
             }
         }
         // ---- A10 (value waves): wait for the weight sums, normalize and write ----
@@ -425,15 +606,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
             const float lt = xsum[b][lane & 15];
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int head = head0 + 16 * b + (lane & 15);
-            uint16_t* orow = p.n_splits == 1
-                                 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * g
-                                 : p.ws_o + (((int64_t)rloc * p.n_splits + split) * p.H + head) * kDv + vdim0 + 4 * g;
+            const int64_t pidx = (((int64_t)rloc * p.n_splits + split) * p.H + head) * kDv + vdim0 + 4 * g;
+            if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
+                float* wo = (float*)p.ws_o + pidx;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint2 w;
-                w.x = pack_bf16x2_hw(oacc[b][d][0] * inv, oacc[b][d][1] * inv);
-                w.y = pack_bf16x2_hw(oacc[b][d][2] * inv, oacc[b][d][3] * inv);
-                *(uint2*)(orow + 16 * d) = w;
+                for (int d = 0; d < 4; ++d)
+                    *(f32x4_t*)(wo + 16 * d) = (f32x4_t){oacc[b][d][0] * inv, oacc[b][d][1] * inv,
+                                                         oacc[b][d][2] * inv, oacc[b][d][3] * inv};
+            } else {
+                uint16_t* orow = p.n_splits == 1 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * g
+                                                 : (uint16_t*)p.ws_o + pidx;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint2 w;
+                    w.x = pack_bf16x2_hw(oacc[b][d][0] * inv, oacc[b][d][1] * inv);
+                    w.y = pack_bf16x2_hw(oacc[b][d][2] * inv, oacc[b][d][3] * inv);
+                    *(uint2*)(orow + 16 * d) = w;
+                }
             }
         }
     }
@@ -441,7 +630,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_bf16_kernel(const 
 
 // A11: merge the splits of each row in split order:  LSE = m + log sum_s e^(lse_s - m),
 // out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16.  64 threads per (row, head), 8 dims each.
-__global__ __launch_bounds__(256) void split_combine_kernel(const uint16_t* __restrict__ ws_o,
+// Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
+template <bool F32>
+__global__ __launch_bounds__(256) void split_combine_kernel(const void* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse, int S, int H,
                                                             int row0, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
@@ -461,23 +652,32 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const uint16_t* __re
         const float inv = 1.f / tot;
         constexpr int kGroup = 4;   // splits whose loads are in flight together
         for (int s0 = 0; s0 < S; s0 += kGroup) {
-            uint4 v[kGroup];
+            float v[kGroup][8];
             float w[kGroup];
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) {
                 const int s = s0 + j < S ? s0 + j : S - 1;   // loads stay unconditional (clamped)
                 w[j] = s0 + j < S ? expf(ls[(int64_t)s * H] - m) * inv : 0.f;
-                v[j] = *(const uint4*)(ws_o + (((int64_t)rloc * S + s) * H + head) * kDv + d);
-            }
+                const int64_t off = (((int64_t)rloc * S + s) * H + head) * kDv + d;
+                if (F32) {
+                    const f32x4_t a = *(const f32x4_t*)((const float*)ws_o + off);
+                    const f32x4_t b = *(const f32x4_t*)((const float*)ws_o + off + 4);
 #pragma unroll
-            for (int j = 0; j < kGroup; ++j) {
-                const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                    for (int e = 0; e < 4; ++e) { v[j][e] = a[e]; v[j][4 + e] = b[e]; }
+                } else {
+                    const uint4 u = *(const uint4*)((const uint16_t*)ws_o + off);
+                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += w[j] * __uint_as_float(wd[e] << 16);
-                    acc[2 * e + 1] += w[j] * __uint_as_float(wd[e] & 0xffff0000u);
+                    for (int e = 0; e < 4; ++e) {
+                        v[j][2 * e] = __uint_as_float(wd[e] << 16);
+                        v[j][2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+                    }
                 }
             }
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += w[j] * v[j][e];
         }
     }
     const int64_t orow = ((int64_t)row0 + rloc) * H + head;
@@ -509,27 +709,34 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.scale_log2 = a.softmax_scale * kLog2e;
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
-    const size_t per_row = attn_ws_bytes_per_row(a.H, a.k);
+    const size_t per_row = attn_ws_bytes_per_row(a.H, a.k, a.kv_dtype);
     int rows_per_launch = a.rows;
     if (per_row > 0) {
         const size_t fit = a.ws_bytes / per_row;
         rows_per_launch = (int)(fit < (size_t)a.rows ? fit : (size_t)a.rows);
         if (rows_per_launch < 1) return hipErrorInvalidValue;   // host validation prevents this
     }
+    const bool fp8 = a.kv_dtype == 1;
     for (int row0 = 0; row0 < a.rows; row0 += rows_per_launch) {
         const int n = min(rows_per_launch, a.rows - row0);
         p.row0 = row0;
         // Workspace regions for a launch of rows_per_launch rows: partials, then LSEs.
-        p.ws_o = per_row > 0 ? (uint16_t*)a.ws : nullptr;
-        p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch * attn_ws_o_bytes_per_row(a.H, a.k))
+        p.ws_o = per_row > 0 ? a.ws : nullptr;
+        p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch *
+                                                               attn_ws_o_bytes_per_row(a.H, a.k, a.kv_dtype))
                                : nullptr;
         const int grid = n * p.n_splits * p.n_hblocks;
-        hipLaunchKernelGGL(sparse_mla_bf16_kernel, dim3(grid), dim3(kAttnThreads), 0, stream, p);
+        if (fp8) hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
+        else hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.n_splits > 1) {
-            hipLaunchKernelGGL(split_combine_kernel, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o, p.ws_lse,
-                               p.n_splits, a.H, row0, p.out, p.lse);
+            if (fp8)
+                hipLaunchKernelGGL(split_combine_kernel<true>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
+                                   p.ws_lse, p.n_splits, a.H, row0, p.out, p.lse);
+            else
+                hipLaunchKernelGGL(split_combine_kernel<false>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
+                                   p.ws_lse, p.n_splits, a.H, row0, p.out, p.lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

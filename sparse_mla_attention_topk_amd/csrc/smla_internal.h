@@ -13,13 +13,16 @@ constexpr int kHeadsPerBlock = 64; // heads handled by one workgroup (4 waves x 
 
 inline int attn_num_splits(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
 
-// Workspace of the attention entry points, per query row (0 when k fits one split): the bf16
-// partial outputs of every (split, head), then their fp32 LSEs.
-inline size_t attn_ws_o_bytes_per_row(int H, int k) { return (size_t)attn_num_splits(k) * H * 512 * 2; }
+// Workspace of the attention entry points, per query row (0 when k fits one split): the partial
+// outputs of every (split, head) -- bf16 for bf16 caches, fp32 for FP8 caches, whose group scales
+// make outputs large enough that bf16 partials would cost visible accuracy -- then their fp32 LSEs.
+inline size_t attn_ws_o_bytes_per_row(int H, int k, int kv_dtype) {
+    return (size_t)attn_num_splits(k) * H * 512 * (kv_dtype == 1 ? 4 : 2);
+}
 inline size_t attn_ws_lse_bytes_per_row(int H, int k) { return (size_t)attn_num_splits(k) * H * 4; }
-inline size_t attn_ws_bytes_per_row(int H, int k) {
+inline size_t attn_ws_bytes_per_row(int H, int k, int kv_dtype) {
     if (attn_num_splits(k) <= 1) return 0;
-    return attn_ws_o_bytes_per_row(H, k) + attn_ws_lse_bytes_per_row(H, k);
+    return attn_ws_o_bytes_per_row(H, k, kv_dtype) + attn_ws_lse_bytes_per_row(H, k);
 }
 
 struct AttnArgs {

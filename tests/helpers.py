@@ -29,12 +29,20 @@ def kv_np(kv: torch.Tensor) -> np.ndarray:
 
 
 def assert_attention_close(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, O_ref: np.ndarray, lse_ref: np.ndarray,
-                           what: str = "") -> dict:
+                           what: str = "", relative: bool = False) -> dict:
+    """Bounds on |out - O_ref| (max and mean) and on the LSE.  With ``relative`` (the FP8-KV
+    workloads, whose group scales of up to 2^4 give outputs far above unit scale, where bf16 output
+    rounding alone exceeds the absolute bounds) every error is divided by max(1, |reference|):
+    elementwise for the max, by max(1, mean |O_ref|) for the mean."""
     o = out_gpu.detach().float().cpu().numpy().astype(np.float64)
     assert o.shape == O_ref.shape, (o.shape, O_ref.shape)
     assert np.isfinite(o).all(), f"{what}: non-finite output"
     err = np.abs(o - O_ref)
+    if relative:
+        err = err / np.maximum(1.0, np.abs(O_ref))
     stats = {"max_abs": float(err.max()) if err.size else 0.0, "mean_abs": float(err.mean()) if err.size else 0.0}
+    if relative and err.size:
+        stats["mean_abs"] = float(np.abs(o - O_ref).mean() / max(1.0, float(np.abs(O_ref).mean())))
     ref_norm = float(np.linalg.norm(O_ref))
     stats["rel_fro"] = float(np.linalg.norm(o - O_ref) / ref_norm) if ref_norm > 0 else 0.0
     assert stats["max_abs"] <= MAX_ABS, (what, stats)
@@ -47,6 +55,8 @@ def assert_attention_close(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, O_ref: 
         assert np.array_equal(np.isneginf(l), np.isneginf(lse_ref)), f"{what}: -inf lse mismatch"
         if fin.any():
             d = np.abs(l[fin] - lse_ref[fin])
+            if relative:
+                d = d / np.maximum(1.0, np.abs(lse_ref[fin]))
             stats["lse_max_abs"] = float(d.max())
             assert stats["lse_max_abs"] <= LSE_ABS, (what, stats)
     return stats
