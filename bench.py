@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-MLA decode rows/s + gathered-KV HBM GB/s (H=64, topk=2048, 1 GPU)"
+METRIC_FP8 = "sparse-MLA decode rows/s + gathered-KV HBM GB/s (FP8 KV, B=128, H=64, topk=2048, 1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 N_SETS = 4
 
@@ -32,9 +33,30 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8"],
+                    help="decode_bf16: B=64, contexts U[8192, 65536], bf16 KV (the headline); "
+                         "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     return ap.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_bf16_B64_H64_k2048_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per sparse_mla_decode call from the committed counter record, or None when the
+    attention source has changed since the counters were taken."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_RECORD) if l.startswith("traffic-record:")][0]
+    except (OSError, IndexError):
+        return None
+    fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+    src = os.path.join(ROOT, fields["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["sha256"]:
+        return None
+    return int(fields["bytes_per_call"])
 
 
 def cpu_baseline(wl, n_rows):
@@ -79,12 +101,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = W.decode_bf16(dev, n_sets=N_SETS)
+    fp8 = args.workload == "decode_fp8"
+    wl = W.decode_fp8(dev, n_sets=N_SETS) if fp8 else W.decode_bf16(dev, n_sets=N_SETS)
     B, H, k = wl.sets[0].q.shape[0], wl.H, wl.k
-    gathered = B * k * W.BF16_RECORD_BYTES            # every row has >= k candidates
+    rec = W.FP8_RECORD_BYTES if fp8 else W.BF16_RECORD_BYTES
+    gathered = B * k * rec                            # every row has >= k candidates
     flops = B * H * k * (576 + 512) * 2
 
-    ws = smla.attention_workspace(B, H, k, dev)
+    ws = smla.attention_workspace(B, H, k, dev, wl.cache.kv_dtype)
     tws = smla.topk_workspace(B, k, wl.sets[0].scores.shape[1], dev)
     idx = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(N_SETS)]
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
@@ -97,7 +121,7 @@ def main():
     def attn(i):
         rs = wl.sets[i]
         smla.sparse_mla_decode(rs.q, wl.cache.kv, wl.cache.block_table, idx[i], wl.scale, row_req=rs.row_req,
-                               out=out, lse=lse, workspace=ws)
+                               kv_dtype=wl.cache.kv_dtype, out=out, lse=lse, workspace=ws)
 
     def steps(n, what):
         for st in range(n):
@@ -168,18 +192,19 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_rows)
 
     line = {
-        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if not fp8 else METRIC_FP8, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8_e4m3/bf16" if fp8 else "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "rows": B, "heads": H, "topk": k, "d_qk": 576, "d_v": 512,
-                   "page_block_size": 64, "kv": "bf16", "context": "uniform [8192, 65536]",
+                   "page_block_size": 64, "kv": "fp8_e4m3_g128" if fp8 else "bf16",
+                   "context": "uniform [32768, 131072]" if fp8 else "uniform [8192, 65536]",
                    "rotating_sets": N_SETS, "launch": "eager" if args.no_graph else "hip_graph_of_K_steps"},
         "gathered_kv_GBps": achieved,
         "step_gathered_kv_GBps": gathered / (ms_step * 1e-3) / 1e9,
         "attention_ms": attn_ms, "topk_ms": topk_ms, "wall_s": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "sparse_mla_decode (attention + split combine)",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None if fp8 else measured_traffic(),
+                     "kernel": "sparse_mla_decode call: attention kernel + split-combine kernel",
                      "algorithmic_bytes_per_launch": gathered,
                      "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12},
         "cpu_baseline": cpu,

@@ -268,11 +268,17 @@ __device__ __forceinline__ bool sample_threshold(const float* sv, int64_t L, int
     return true;
 }
 
-// Sampled positions: four per thread, spread evenly over the row.
+// Sampled positions: 128 blocks of 32 consecutive candidates (one cache line each) spread evenly over
+// the row; thread t takes 4 of them.  Whole lines keep the sample's memory traffic at 16 KB per row.
 template <class Src>
 __device__ __forceinline__ void load_sample(const Src& src, int64_t L, float* sv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = src.at(((int64_t)(threadIdx.x * 4 + i) * L) >> kSampleLog2);
+    for (int i = 0; i < 4; ++i) {
+        const int q = (int)threadIdx.x * 4 + i;                      // sample index 0 .. 4095
+        const int64_t b = ((int64_t)(q >> 5) * L) >> 7;               // start of block q / 32
+        const int64_t j = (b & ~(int64_t)31) + (q & 31);
+        sv[i] = src.at(j < L ? j : L - 1);
+    }
 }
 
 // Rows that go through a candidate filter (decided from L and k alone).
