@@ -149,6 +149,15 @@ __device__ __forceinline__ uint32_t bf16x2_code_to_f16x2(uint32_t w) {
     return r.u;
 }
 
+// Two e4m3 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values.  The scaled conversion with
+// scale 1.0 is exact: every e4m3 value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    union { decltype(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(0, 1.f, false)) v; uint32_t u; } r;
+    r.v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, HI);
+    return r.u;
+}
+
 // A head's reference max only moves when a tile's max exceeds it by more than this (log2 units);
 // in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
@@ -157,25 +166,36 @@ constexpr float kRescaleSlack = 8.f;
 // layout of the bf16 path: the e4m3 codes exactly (every e4m3 value is a bf16 value), the rope copied,
 // and the four fp32 group scales of each token into a small table.  The scales are applied in fp32:
 // the score waves keep one partial per 128-dim scale group and sum scale x partial; the softmax
-// publishes, for every group, the weights times that group's scales rounded to fp16, and a value
-// wave, whose 64 dims lie in one group, runs the value product in fp16 (the codes are exact in fp16
-// too) with that group's weights.  At the magnitudes these scales produce, rounding the scaled
+// publishes the fp32 weights, and a value wave, whose 64 dims lie in one group, multiplies them by
+// that group's scales, rounds to fp16 and runs the value product in fp16 (the codes are exact in fp16
+// too).  At the magnitudes these scales produce, rounding the scaled
 // values, or the scaled weights, to bf16 costs far more accuracy than the fp16 weights.
 template <bool KV_FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
-    constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + kStageBytes : kStages * kStageBytes;
+    // FP8: the ring of FP8 stages, then two bf16 tiles (tile it is read while tile it+1 is expanded)
+    constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + 2 * kStageBytes : kStages * kStageBytes;
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
     constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
     __shared__ uint32_t phys[kSplitSlots];
     __shared__ uint32_t tile_valid[kTilesPerSplit];
-    __shared__ __attribute__((aligned(16))) f32x4_t xs[4][2][kWave];        // second-half partial scores
-    // P fragments per head block; FP8: one set per scale group (weights times the group's scales)
-    __shared__ __attribute__((aligned(16))) uint32_t pfrag[KV_FP8 ? 4 : 1][4][kWave * 4];
-    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? kTileTok : 1][4];   // FP8: scales of the tile's tokens
+    // Weights of each head block: bf16 B-operand fragments (bf16 caches), or the lane's 8 fp32
+    // weights (FP8 caches; each value wave scales them by its group's token scales).
+    __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
+    // Second-half partial scores of each head block.  FP8 keeps them in the head block's weight area
+    // (2 KB there): they are read by the block's softmax wave before it writes the weights, and the
+    // value waves have taken the previous tile's weights before they are written.
+    __shared__ __attribute__((aligned(16))) f32x4_t xs_own[KV_FP8 ? 1 : 4][2][kWave];
+    // FP8: scales of the tile's tokens, one table per bf16 tile (the value waves read tile it's while
+    // tile it+1 is expanded)
+    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     __shared__ float xsum[4][16];      // per-head weight sums at the end
     __shared__ int s_first, s_last;
+    auto xs = [&](int b, int j) -> f32x4_t* {
+        if constexpr (KV_FP8) return (f32x4_t*)&pfrag[b][0][0] + j * kWave;   // 2 x 64 x 16 B = the block's area
+        else return &xs_own[b][j][0];
+    };
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -319,9 +339,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // 16c .. 16c+15 of token t = u / 32 (c = u % 32) into bf16 chunks 2c, 2c+1 and, for c % 8 == 0,
     // stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.  Invalid
     // tokens become zeros (codes, rope and scales).
-    uint8_t* const btile = ring + kStages * kFp8StageBytes;
+    auto btile_of = [&](int tile) { return ring + kStages * kFp8StageBytes + (tile & 1) * kStageBytes; };
     auto dequant_tile = [&](int tile, int stage) {
         const uint8_t* st = ring + stage * kFp8StageBytes;
+        uint8_t* const btile = btile_of(tile);
         const uint32_t vm = tile_valid[tile];
         // Invalid tokens are cleared with a bit mask (a select between vectors would go through
         // scratch memory, whose wait would also wait for the tile loads in flight).
@@ -332,19 +353,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             const uint32_t keep = 0u - ((vm >> t) & 1u);
             const int f = swz_key(t);
             const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
-            if ((c & 7) == 0) tscale[t][c >> 3] = keep ? *(const float*)(st + t * kFp8Record + 512 + 4 * (c >> 3)) : 0.f;
+            if ((c & 7) == 0) tscale[tile & 1][t][c >> 3] = keep ? *(const float*)(st + t * kFp8Record + 512 + 4 * (c >> 3)) : 0.f;
             uint8_t* dst = btile + t * kBf16Record;
-            // codes 0..7 of the chunk -> bf16 chunk 2c, codes 8..15 -> bf16 chunk 2c+1 (exact)
-            auto expand = [&](uint32_t w0, uint32_t w1) {
-                const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-                const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-                const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-                const auto g2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-                return make_uint4(pack_bf16x2_hw(a[0], a[1]) & keep, pack_bf16x2_hw(b[0], b[1]) & keep,
-                                  pack_bf16x2_hw(e[0], e[1]) & keep, pack_bf16x2_hw(g2[0], g2[1]) & keep);
-            };
-            *(uint4*)(dst + 16 * ((2 * c) ^ f)) = expand(codes.x, codes.y);
-            *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) = expand(codes.z, codes.w);
+            // codes 0..7 of the chunk -> bf16 chunk 2c, codes 8..15 -> bf16 chunk 2c+1; the conversion
+            // with scale 1.0 is exact (checked on the hardware for all 256 codes)
+            *(uint4*)(dst + 16 * ((2 * c) ^ f)) =
+                make_uint4(fp8x2_to_bf16x2<false>(codes.x) & keep, fp8x2_to_bf16x2<true>(codes.x) & keep,
+                           fp8x2_to_bf16x2<false>(codes.y) & keep, fp8x2_to_bf16x2<true>(codes.y) & keep);
+            *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
+                make_uint4(fp8x2_to_bf16x2<false>(codes.z) & keep, fp8x2_to_bf16x2<true>(codes.z) & keep,
+                           fp8x2_to_bf16x2<false>(codes.w) & keep, fp8x2_to_bf16x2<true>(codes.w) & keep);
         }
         if (tid < kTileTok * 8) {
             const int rt = tid >> 3, j = tid & 7;
@@ -373,31 +391,52 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
 
-    // Start of tile `it`, common to both roles: wait for this wave's loads of the tile, make the tile
-    // visible (first barrier) and start the load of tile it+2 into the stage every wave finished
-    // with in tile it-1.  bf16: invalid tokens are zeroed in the stage before the barrier.  FP8: the
-    // stage is expanded into the bf16 tile after it (the previous tile's bf16 data is no longer read),
-    // followed by a second barrier.
-    auto tile_top = [&](int it, auto expands) {
-        const int stage = it % kStages;
-        if (it + 1 < ntiles) {   // tile it+1 stays in flight
-            if (nload == 3) wait_vmcnt<3>();
-            else if (nload == 2) wait_vmcnt<2>();
+    // Start of tile `it`, common to both roles.
+    // bf16: wait for this wave's loads of the tile, zero its invalid chunks, make the tile visible
+    //   (first barrier) and start the load of tile it+2 into the stage every wave finished with in
+    //   tile it-1.
+    // FP8: the tile was expanded into bf16 tile it % 2 during the previous tile's value product (or
+    //   before the loop); the first barrier makes it visible, then the load of tile it+2 starts.
+    //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
+    //   the score waves expand tile it+1.
+    if (KV_FP8 && ntiles > 0) {
+        if (ntiles > 1) {
+            if (nload == 2) wait_vmcnt<2>();
             else wait_vmcnt<1>();
         } else {
             wait_vmcnt<0>();
         }
-        if (!KV_FP8) zero_invalid(it, stage);
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
+        if (is_score) dequant_tile(0, 0);
+    }
+    auto tile_top = [&](int it) {
+        const int stage = it % kStages;
+        if (!KV_FP8) {
+            if (it + 1 < ntiles) {   // tile it+1 stays in flight
+                if (nload == 3) wait_vmcnt<3>();
+                else wait_vmcnt<2>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            zero_invalid(it, stage);
+        }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
-        if (KV_FP8) {
-            if constexpr (decltype(expands)::value) dequant_tile(it, stage);
-            wait_lgkmcnt0();
-            __builtin_amdgcn_s_barrier();
-            return (const uint8_t*)btile;
-        }
+        if (KV_FP8) return (const uint8_t*)btile_of(it);
         return (const uint8_t*)(ring + stage * kStageBytes);
+    };
+    // FP8: before the third barrier of tile it, this wave's loads of tile it+1 have landed.
+    auto wait_next_fp8 = [&](int it) {
+        if (KV_FP8 && it + 1 < ntiles) {
+            if (it + 2 < ntiles) {   // tile it+2 stays in flight
+                if (nload == 2) wait_vmcnt<2>();
+                else wait_vmcnt<1>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
     };
 
     // The two roles run separate loops with the same barriers per tile, so the registers of
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
     if (is_score) {
         for (int it = 0; it < ntiles; ++it) {
-            const uint8_t* sb = tile_top(it, std::true_type{});
+            const uint8_t* sb = tile_top(it);
             // ---- A7: partial scores over this wave's half of the dims ----
             f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
             if (score_ok) {
@@ -444,8 +483,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     const int gs0 = half ? 2 : 0;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const f32x4_t ta = *(const f32x4_t*)tscale[4 * g + i];
-                        const f32x4_t tb = *(const f32x4_t*)tscale[16 + 4 * g + i];
+                        const f32x4_t ta = *(const f32x4_t*)tscale[it & 1][4 * g + i];
+                        const f32x4_t tb = *(const f32x4_t*)tscale[it & 1][16 + 4 * g + i];
                         const float a0s = half ? ta[2] : ta[0], a1s = half ? ta[3] : ta[1];
                         const float b0s = half ? tb[2] : tb[0], b1s = half ? tb[3] : tb[1];
                         const float a2s = half ? 1.f : ta[2], b2s = half ? 1.f : tb[2];
@@ -455,8 +494,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     (void)gs0;
                 }
                 if (half) {
-                    xs[shb][0][lane] = s0;
-                    xs[shb][1][lane] = s1;
+                    xs(shb, 0)[lane] = s0;
+                    xs(shb, 1)[lane] = s1;
                 }
             }
             wait_lgkmcnt0();                 // s_barrier does not wait for LDS writes by itself
@@ -464,7 +503,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 
             // ---- A8: online softmax of the first-half waves' 16 heads ----
             if (score_ok && !half) {
-                const f32x4_t t0 = xs[shb][0][lane], t1 = xs[shb][1][lane];
+                const f32x4_t t0 = xs(shb, 0)[lane], t1 = xs(shb, 1)[lane];
                 const uint32_t vmask = tile_valid[it];
                 // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
                 float sv[8];
@@ -502,32 +541,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     pf.y = pack_bf16x2_hw(pw[2], pw[3]);
                     pf.z = pack_bf16x2_hw(pw[4], pw[5]);
                     pf.w = pack_bf16x2_hw(pw[6], pw[7]);
-                    *(uint4*)&pfrag[0][shb][4 * lane] = pf;
-                } else {
-                    f32x4_t tsc[8];   // scales of the lane's 8 tokens
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        tsc[i] = *(const f32x4_t*)tscale[4 * g + i];
-                        tsc[4 + i] = *(const f32x4_t*)tscale[16 + 4 * g + i];
-                    }
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg) {   // fp16 weights: the value product runs in fp16
-                        uint4 pf;
-                        pf.x = pack_f16x2_rne(pw[0] * tsc[0][gg], pw[1] * tsc[1][gg]);
-                        pf.y = pack_f16x2_rne(pw[2] * tsc[2][gg], pw[3] * tsc[3][gg]);
-                        pf.z = pack_f16x2_rne(pw[4] * tsc[4][gg], pw[5] * tsc[5][gg]);
-                        pf.w = pack_f16x2_rne(pw[6] * tsc[6][gg], pw[7] * tsc[7][gg]);
-                        *(uint4*)&pfrag[gg][shb][4 * lane] = pf;
-                    }
+                    *(uint4*)&pfrag[shb][0][4 * lane] = pf;
+                } else {   // fp32 weights: tokens 4g + i (first vector), 16 + 4g + i (second)
+                    xs(shb, 0)[lane] = (f32x4_t){pw[0], pw[1], pw[2], pw[3]};
+                    xs(shb, 1)[lane] = (f32x4_t){pw[4], pw[5], pw[6], pw[7]};
                 }
                 if (lane < 16) xalpha[shb][lane] = alpha;
             } else if (!half && shb >= nhb) {   // head block beyond H: zero weights
-#pragma unroll
-                for (int gg = 0; gg < (KV_FP8 ? 4 : 1); ++gg) *(uint4*)&pfrag[gg][shb][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (!KV_FP8) {
+                    *(uint4*)&pfrag[shb][0][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+                } else {
+                    xs(shb, 0)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    xs(shb, 1)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                }
                 if (lane < 16) xalpha[shb][lane] = 1.f;
             }
+            wait_next_fp8(it);
             wait_lgkmcnt0();
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
+            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);   // during the value product
         }
         // ---- A10 (score waves): total weight and LSE of the first halves' heads ----
         const float l_tot = head_sum(l_run);
@@ -549,17 +581,37 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
             for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         for (int it = 0; it < ntiles; ++it) {
-            const uint8_t* sb = tile_top(it, std::false_type{});
+            const uint8_t* sb = tile_top(it);
             __builtin_amdgcn_s_barrier();   // second-half partials published
+            wait_next_fp8(it);
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
 
             // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims ----
             float a_blk[4];
             uint4 pb[4];   // B operands: bf16 weights, or (FP8) fp16 weights times the wave's group scales
+            if constexpr (!KV_FP8) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                a_blk[b] = xalpha[b][lane & 15];
-                pb[b] = *(const uint4*)&pfrag[KV_FP8 ? (vdim0 >> 7) : 0][b][4 * lane];
+                for (int b = 0; b < 4; ++b) {
+                    a_blk[b] = xalpha[b][lane & 15];
+                    pb[b] = *(const uint4*)&pfrag[b][0][4 * lane];
+                }
+            } else {
+                const int gv = vdim0 >> 7;   // the scale group of this wave's dims
+                float sc8[8];                // scales of the lane's tokens 4g + i and 16 + 4g + i
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sc8[i] = tscale[it & 1][4 * g + i][gv];
+                    sc8[4 + i] = tscale[it & 1][16 + 4 * g + i][gv];
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    a_blk[b] = xalpha[b][lane & 15];
+                    const f32x4_t p0 = xs(b, 0)[lane], p1 = xs(b, 1)[lane];
+                    pb[b] = make_uint4(pack_f16x2_rne(p0[0] * sc8[0], p0[1] * sc8[1]),
+                                       pack_f16x2_rne(p0[2] * sc8[2], p0[3] * sc8[3]),
+                                       pack_f16x2_rne(p1[0] * sc8[4], p1[1] * sc8[5]),
+                                       pack_f16x2_rne(p1[2] * sc8[6], p1[3] * sc8[7]));
+                }
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -629,8 +681,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 }
 
 // A11: merge the splits of each row in split order:  LSE = m + log sum_s e^(lse_s - m),
-// out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16.  64 threads per (row, head), 8 dims each.
-// Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
+// out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16, computed as an online merge over the
+// splits in order (the running max m and sum are updated split by split).  64 threads per
+// (row, head), 8 dims each.  Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
 template <bool F32>
 __global__ __launch_bounds__(256) void split_combine_kernel(const void* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse, int S, int H,
@@ -641,44 +694,55 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const void* __restri
     const int head = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
     const int d = 8 * (threadIdx.x & 63);
     const float* ls = ws_lse + (int64_t)rloc * S * H + head;
-    float m = -INFINITY;
-    for (int s = 0; s < S; ++s) m = fmaxf(m, ls[(int64_t)s * H]);
+    constexpr int kGroup = 4;   // splits whose loads are in flight together
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float LSE = -INFINITY;
-    if (m != -INFINITY) {
-        float tot = 0.f;
-        for (int s = 0; s < S; ++s) tot += expf(ls[(int64_t)s * H] - m);
-        LSE = m + logf(tot);
-        const float inv = 1.f / tot;
-        constexpr int kGroup = 4;   // splits whose loads are in flight together
-        for (int s0 = 0; s0 < S; s0 += kGroup) {
-            float v[kGroup][8];
-            float w[kGroup];
+    float m = -INFINITY, tot = 0.f;
+    // Online merge over groups of splits, in split order: the LSEs and partials of a group are loaded
+    // together (no load waits for another), and the running sum is rescaled when the max grows.
+    for (int s0 = 0; s0 < S; s0 += kGroup) {
+        float l4[kGroup], v[kGroup][8];
 #pragma unroll
-            for (int j = 0; j < kGroup; ++j) {
-                const int s = s0 + j < S ? s0 + j : S - 1;   // loads stay unconditional (clamped)
-                w[j] = s0 + j < S ? expf(ls[(int64_t)s * H] - m) * inv : 0.f;
-                const int64_t off = (((int64_t)rloc * S + s) * H + head) * kDv + d;
-                if (F32) {
-                    const f32x4_t a = *(const f32x4_t*)((const float*)ws_o + off);
-                    const f32x4_t b = *(const f32x4_t*)((const float*)ws_o + off + 4);
+        for (int j = 0; j < kGroup; ++j) {
+            const int s = s0 + j < S ? s0 + j : S - 1;   // loads stay unconditional (clamped)
+            l4[j] = s0 + j < S ? ls[(int64_t)s * H] : -INFINITY;
+            const int64_t off = (((int64_t)rloc * S + s) * H + head) * kDv + d;
+            if (F32) {
+                const f32x4_t a = *(const f32x4_t*)((const float*)ws_o + off);
+                const f32x4_t b = *(const f32x4_t*)((const float*)ws_o + off + 4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { v[j][e] = a[e]; v[j][4 + e] = b[e]; }
-                } else {
-                    const uint4 u = *(const uint4*)((const uint16_t*)ws_o + off);
-                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+                for (int e = 0; e < 4; ++e) { v[j][e] = a[e]; v[j][4 + e] = b[e]; }
+            } else {
+                const uint4 u = *(const uint4*)((const uint16_t*)ws_o + off);
+                const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[j][2 * e] = __uint_as_float(wd[e] << 16);
-                        v[j][2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    v[j][2 * e] = __uint_as_float(wd[e] << 16);
+                    v[j][2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
                 }
             }
-#pragma unroll
-            for (int j = 0; j < kGroup; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += w[j] * v[j][e];
         }
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+            if (l4[j] == -INFINITY) continue;        // empty split (or past S): contributes nothing
+            if (l4[j] > m) {                         // rescale what has been merged so far
+                const float c = m == -INFINITY ? 0.f : expf(m - l4[j]);
+                tot *= c;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] *= c;
+                m = l4[j];
+            }
+            const float w = expf(l4[j] - m);
+            tot += w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += w * v[j][e];
+        }
+    }
+    float LSE = -INFINITY;
+    if (tot > 0.f) {
+        LSE = m + logf(tot);
+        const float inv = 1.f / tot;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
     }
     const int64_t orow = ((int64_t)row0 + rloc) * H + head;
     uint4 o;
