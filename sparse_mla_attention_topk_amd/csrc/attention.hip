@@ -52,7 +52,6 @@ constexpr int kAttnWaves = 16;
 constexpr int kAttnThreads = kAttnWaves * kWave;               // 1024
 constexpr int kScoreWaves = 8;
 constexpr int kTileTok = 32;
-constexpr int kStages = 3;
 constexpr int kTilesPerSplit = kSplitSlots / kTileTok;         // 16
 constexpr int kStageBytes = kTileTok * kBf16Record;             // 36864
 constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-LDS loads of 1 KB per tile
@@ -173,6 +172,7 @@ constexpr float kRescaleSlack = 8.f;
 template <bool KV_FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
     // FP8: the ring of FP8 stages, then two bf16 tiles (tile it is read while tile it+1 is expanded)
+    constexpr int kStages = 3;   // ring depth: tiles are loaded two tiles ahead
     constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + 2 * kStageBytes : kStages * kStageBytes;
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
     constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
@@ -182,20 +182,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // Weights of each head block: bf16 B-operand fragments (bf16 caches), or the lane's 8 fp32
     // weights (FP8 caches; each value wave scales them by its group's token scales).
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
-    // Second-half partial scores of each head block.  FP8 keeps them in the head block's weight area
-    // (2 KB there): they are read by the block's softmax wave before it writes the weights, and the
-    // value waves have taken the previous tile's weights before they are written.
-    __shared__ __attribute__((aligned(16))) f32x4_t xs_own[KV_FP8 ? 1 : 4][2][kWave];
+    // Second-half partial scores of each head block.
+    __shared__ __attribute__((aligned(16))) f32x4_t xs_own[4][2][kWave];
     // FP8: scales of the tile's tokens, one table per bf16 tile (the value waves read tile it's while
     // tile it+1 is expanded)
     __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     __shared__ float xsum[4][16];      // per-head weight sums at the end
     __shared__ int s_first, s_last;
-    auto xs = [&](int b, int j) -> f32x4_t* {
-        if constexpr (KV_FP8) return (f32x4_t*)&pfrag[b][0][0] + j * kWave;   // 2 x 64 x 16 B = the block's area
-        else return &xs_own[b][j][0];
-    };
+    auto xs = [&](int b, int j) -> f32x4_t* { return &xs_own[b][j][0]; };
+    auto pw32 = [&](int b, int j) -> f32x4_t* { return (f32x4_t*)&pfrag[b][0][0] + j * kWave; };   // FP8 weights
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -334,11 +330,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             }
         }
     };
-    // FP8 (A6): expand the stage's records into the bf16 tile, done by the 512 threads of the score
-    // waves (the value waves hold their accumulators).  Unit u (tid and tid + 512) converts codes
-    // 16c .. 16c+15 of token t = u / 32 (c = u % 32) into bf16 chunks 2c, 2c+1 and, for c % 8 == 0,
-    // stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.  Invalid
-    // tokens become zeros (codes, rope and scales).
+    // FP8 (A6): expand the stage's records into the bf16 tile, one unit per thread: thread u converts
+    // codes 16c .. 16c+15 of token t = u / 32 (c = u % 32) into bf16 chunks 2c, 2c+1 and, for
+    // c % 8 == 0, stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.
+    // Invalid tokens become zeros (codes, rope and scales).
     auto btile_of = [&](int tile) { return ring + kStages * kFp8StageBytes + (tile & 1) * kStageBytes; };
     auto dequant_tile = [&](int tile, int stage) {
         const uint8_t* st = ring + stage * kFp8StageBytes;
@@ -346,9 +341,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         const uint32_t vm = tile_valid[tile];
         // Invalid tokens are cleared with a bit mask (a select between vectors would go through
         // scratch memory, whose wait would also wait for the tile loads in flight).
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int u = tid + 512 * h;
+        int u = tid;
+        asm volatile("" : "+v"(u));   // recompute the unit's offsets per tile (not held across the loop)
+        {
             const int t = u >> 5, c = u & 31;
             const uint32_t keep = 0u - ((vm >> t) & 1u);
             const int f = swz_key(t);
@@ -364,8 +359,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 make_uint4(fp8x2_to_bf16x2<false>(codes.z) & keep, fp8x2_to_bf16x2<true>(codes.z) & keep,
                            fp8x2_to_bf16x2<false>(codes.w) & keep, fp8x2_to_bf16x2<true>(codes.w) & keep);
         }
-        if (tid < kTileTok * 8) {
-            const int rt = tid >> 3, j = tid & 7;
+        if (u < kTileTok * 8) {
+            const int rt = u >> 3, j = u & 7;
             const uint32_t keep = 0u - ((vm >> rt) & 1u);
             uint4 r = *(const uint4*)(st + rt * kFp8Record + 528 + 16 * j);
             r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
@@ -392,10 +387,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
 
     // Start of tile `it`, common to both roles.
-    // bf16: wait for this wave's loads of the tile, zero its invalid chunks, make the tile visible
-    //   (first barrier) and start the load of tile it+2 into the stage every wave finished with in
-    //   tile it-1.
-    // FP8: the tile was expanded into bf16 tile it % 2 during the previous tile's value product (or
+    // bf16: wait for this wave's loads of the tile, zero its invalid chunks and make the tile visible
+    //   (first barrier); tile it+1 stays in flight.
+    // FP8: the tile was expanded into bf16 tile it % 2 after the third barrier of tile it-1 (or
     //   before the loop); the first barrier makes it visible, then the load of tile it+2 starts.
     //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
     //   the score waves expand tile it+1.
@@ -408,7 +402,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
-        if (is_score) dequant_tile(0, 0);
+        dequant_tile(0, 0);
     }
     auto tile_top = [&](int it) {
         const int stage = it % kStages;
@@ -423,9 +417,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        if (KV_FP8 && it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
         if (KV_FP8) return (const uint8_t*)btile_of(it);
         return (const uint8_t*)(ring + stage * kStageBytes);
+    };
+    // bf16: after the second barrier of tile it, the stage of tile it-1 (whose value product ends
+    // before that barrier) receives tile it+2.
+    auto issue_after_second = [&](int it) {
+        if (!KV_FP8 && it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
     };
     // FP8: before the third barrier of tile it, this wave's loads of tile it+1 have landed.
     auto wait_next_fp8 = [&](int it) {
@@ -500,6 +499,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             }
             wait_lgkmcnt0();                 // s_barrier does not wait for LDS writes by itself
             __builtin_amdgcn_s_barrier();   // second-half partials published
+            issue_after_second(it);
 
             // ---- A8: online softmax of the first-half waves' 16 heads ----
             if (score_ok && !half) {
@@ -543,23 +543,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     pf.w = pack_bf16x2_hw(pw[6], pw[7]);
                     *(uint4*)&pfrag[shb][0][4 * lane] = pf;
                 } else {   // fp32 weights: tokens 4g + i (first vector), 16 + 4g + i (second)
-                    xs(shb, 0)[lane] = (f32x4_t){pw[0], pw[1], pw[2], pw[3]};
-                    xs(shb, 1)[lane] = (f32x4_t){pw[4], pw[5], pw[6], pw[7]};
+                    pw32(shb, 0)[lane] = (f32x4_t){pw[0], pw[1], pw[2], pw[3]};
+                    pw32(shb, 1)[lane] = (f32x4_t){pw[4], pw[5], pw[6], pw[7]};
                 }
                 if (lane < 16) xalpha[shb][lane] = alpha;
             } else if (!half && shb >= nhb) {   // head block beyond H: zero weights
                 if constexpr (!KV_FP8) {
                     *(uint4*)&pfrag[shb][0][4 * lane] = make_uint4(0u, 0u, 0u, 0u);
                 } else {
-                    xs(shb, 0)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    xs(shb, 1)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    pw32(shb, 0)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    pw32(shb, 1)[lane] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
                 }
                 if (lane < 16) xalpha[shb][lane] = 1.f;
             }
             wait_next_fp8(it);
             wait_lgkmcnt0();
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);   // during the value product
+            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);
         }
         // ---- A10 (score waves): total weight and LSE of the first halves' heads ----
         const float l_tot = head_sum(l_run);
@@ -580,13 +580,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        for (int it = 0; it < ntiles; ++it) {
-            const uint8_t* sb = tile_top(it);
-            __builtin_amdgcn_s_barrier();   // second-half partials published
-            wait_next_fp8(it);
-            __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-
-            // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims ----
+        // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims (tile it in LDS at sb) ----
+        auto value_product = [&](int it, const uint8_t* sb) {
             float a_blk[4];
             uint4 pb[4];   // B operands: bf16 weights, or (FP8) fp16 weights times the wave's group scales
             if constexpr (!KV_FP8) {
@@ -606,7 +601,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     a_blk[b] = xalpha[b][lane & 15];
-                    const f32x4_t p0 = xs(b, 0)[lane], p1 = xs(b, 1)[lane];
+                    const f32x4_t p0 = pw32(b, 0)[lane], p1 = pw32(b, 1)[lane];
                     pb[b] = make_uint4(pack_f16x2_rne(p0[0] * sc8[0], p0[1] * sc8[1]),
                                        pack_f16x2_rne(p0[2] * sc8[2], p0[3] * sc8[3]),
                                        pack_f16x2_rne(p1[0] * sc8[4], p1[1] * sc8[5]),
@@ -649,7 +644,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     }
                 }
             }
+        };
+        // The value product of tile it runs after the first barrier of tile it+1, beside the scores of
+        // tile it+1: its weights and rescale factors are rewritten only after the second barrier of
+        // tile it+1, its bf16 tile (the ring stage, or the FP8 expansion buffer) only after that too.
+        const uint8_t* sb_prev = nullptr;
+        for (int it = 0; it < ntiles; ++it) {
+            const uint8_t* sb = tile_top(it);
+            if (it > 0) value_product(it - 1, sb_prev);
+            wait_lgkmcnt0();                 // this wave's reads of tile it-1 are done
+            __builtin_amdgcn_s_barrier();   // second-half partials published
+            issue_after_second(it);
+            wait_next_fp8(it);
+            __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
+            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);
+            sb_prev = sb;
         }
+        if (ntiles > 0) value_product(ntiles - 1, sb_prev);
         // ---- A10 (value waves): wait for the weight sums, normalize and write ----
         __syncthreads();
 #pragma unroll
