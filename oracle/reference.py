@@ -27,7 +27,10 @@ Sources (pages as titled; sections named):
   times the block size plus its offset in the block.
 * "Port DeepSeek-V4 optimization PR #174 to v0.26 ..." (MooreThreads/vllm-musa
   PR 178), table "Optimizations carried from PR #174": FP8 KV with fp32 scale
-  groups kept contiguous.
+  groups kept contiguous, and an FP8 cache write that quantizes new tokens in
+  128-element groups.  "[DeepSeek-V4][Preview] Batch-invariant kernels for
+  0-diff RL", section on the fused group-quantization operator: 128-element
+  groups with FP32 scales.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes):
@@ -43,7 +46,12 @@ design notes):
 * LSE is the natural-log log-sum-exp of the scaled scores; a row with no
   selected token has output 0 and LSE -inf;
 * the FP8 record is [512 e4m3 codes | 4 fp32 scales | 64 bf16 rope]; latent
-  entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format.
+  entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format;
+* the cache write quantizes group g of a token's 512 latent values with the
+  fp32 scale s = amax / 448 (amax = largest magnitude in the group) and the
+  codes e4m3(x / s), both divisions in fp32 with round-to-nearest-even, the
+  code rounded to nearest-even and saturated at +-448; an all-zero group gets
+  s = 0 and zero codes; the 64 rope values are stored unchanged.
 """
 
 from __future__ import annotations
@@ -100,6 +108,75 @@ def decode_record(rec: np.ndarray, kv_dtype: int) -> np.ndarray:
     rope = bf16_to_f64(rec[..., 528:656].view(np.uint16))                # [..., 64]
     lat = e4m3fn_to_f64(codes) * np.repeat(scales, 128, axis=-1)          # group g = d // 128
     return np.concatenate([lat, rope], axis=-1)
+
+
+def _e4m3fn_finite_table() -> np.ndarray:
+    """Values of the non-negative finite E4M3FN codes 0x00 .. 0x7E, in code order (ascending)."""
+    return e4m3fn_to_f64(np.arange(0x7F))
+
+
+def f32_to_e4m3fn(x) -> np.ndarray:
+    """float32 values -> E4M3FN codes, rounding to the nearest representable value with ties to
+    the code whose mantissa is even, and saturating magnitudes above 448 to +-448.  The sign of
+    zero is kept.  NaN gives the NaN code 0x7F (sign kept)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    table = _e4m3fn_finite_table()
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0x00)
+    hi = np.clip(np.searchsorted(table, np.minimum(a, table[-1]), side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = np.abs(a - table[lo])
+    d_hi = np.abs(table[hi] - a)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= table[-1], 0x7E, code)                       # saturate
+    code = np.where(np.isnan(x), 0x7F, code)
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_group(x_bits: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """One 128-entry scale group of bf16 latent values -> (e4m3 codes [128], fp32 scale).
+    s = fp32(amax / 448), codes = e4m3(fp32(x / s)); an all-zero group has s = 0, codes 0."""
+    x = bf16_to_f64(x_bits).astype(np.float32)                        # exact widening
+    amax = np.float32(np.max(np.abs(x)))
+    if amax == 0:
+        return np.zeros(len(x), dtype=np.uint8), np.float32(0.0)
+    s = np.float32(amax / np.float32(448.0))                          # IEEE fp32 division
+    y = (x / s).astype(np.float32)                                    # IEEE fp32 division
+    return f32_to_e4m3fn(y), s
+
+
+def encode_record(token_bits: np.ndarray, kv_dtype: int) -> np.ndarray:
+    """One token's 576 bf16 values (bit patterns: 512 latent, 64 rope) -> its cache record
+    (uint8).  bf16 caches store the 1152 bytes as they are; FP8 caches store the 512 codes, the
+    4 group scales and the 64 rope values."""
+    t = np.ascontiguousarray(token_bits, dtype=np.uint16)
+    assert t.shape == (D_QK,)
+    if kv_dtype == KV_BF16:
+        return t.view(np.uint8).copy()
+    rec = np.zeros(FP8_RECORD_BYTES, dtype=np.uint8)
+    scales = np.zeros(4, dtype=np.float32)
+    for g in range(4):
+        codes, s = quantize_group(t[128 * g:128 * (g + 1)])
+        rec[128 * g:128 * (g + 1)] = codes
+        scales[g] = s
+    rec[512:528] = scales.view(np.uint8)
+    rec[528:656] = t[512:576].view(np.uint8)
+    return rec
+
+
+def cache_write(cache: np.ndarray, kv_dtype: int, tokens_bits: np.ndarray,
+                slot_mapping: Sequence[int]) -> np.ndarray:
+    """Writes token t's record to physical slot slot_mapping[t] (block id * 64 + offset) of the
+    paged cache [num_pages, 64, record]; slots < 0 or past the cache are skipped.  Returns the
+    updated copy of the cache."""
+    out = np.array(cache, dtype=np.uint8, copy=True)
+    flat = out.reshape(-1, out.shape[-1])
+    for t, slot in enumerate(slot_mapping):
+        slot = int(slot)
+        if 0 <= slot < flat.shape[0]:
+            flat[slot] = encode_record(tokens_bits[t], kv_dtype)
+    return out
 
 
 # ----------------------------------------------------------------------------------------------

@@ -208,6 +208,154 @@ def test_fp8_record_group_scales_and_rope():
     np.testing.assert_array_equal(out[512:], rope)
 
 
+# ----------------------------------------------------------------------------------------------
+# FP8 cache write: e4m3 encoding and 128-entry group quantization
+# ----------------------------------------------------------------------------------------------
+
+def test_e4m3fn_encode_round_trips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3fn_to_f64(codes)
+    fin = ~np.isnan(vals)
+    np.testing.assert_array_equal(O.f32_to_e4m3fn(vals[fin].astype(np.float32)), codes[fin])
+
+
+def test_e4m3fn_encode_matches_torch_inside_the_range():
+    # torch's float32 -> float8_e4m3fn conversion rounds to nearest-even; it is an independent
+    # implementation for every magnitude up to 448 (it does not saturate, so nothing above).
+    rng = np.random.default_rng(7)
+    mags = np.concatenate([rng.uniform(0, 448, 20000), np.exp2(rng.uniform(-12, 8.8, 20000)),
+                           rng.uniform(0, 2 ** -6, 5000)])
+    x = (mags * rng.choice([-1.0, 1.0], mags.size)).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.f32_to_e4m3fn(x), ref)
+
+
+def test_e4m3fn_encode_ties_go_to_even_and_large_values_saturate():
+    table = O.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mid = ((table[:-1] + table[1:]) / 2).astype(np.float32)          # exact in fp32
+    got = O.f32_to_e4m3fn(mid)
+    lo = np.arange(0x7E)
+    np.testing.assert_array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    np.testing.assert_array_equal(O.f32_to_e4m3fn(-mid), np.where(lo % 2 == 0, lo, lo + 1) | 0x80)
+    big = np.array([448.0, 449.0, 464.0, 480.0, 1e6, 3e38], np.float32)
+    np.testing.assert_array_equal(O.f32_to_e4m3fn(big), np.full(6, 0x7E))
+    np.testing.assert_array_equal(O.f32_to_e4m3fn(-big), np.full(6, 0xFE))
+    assert list(O.f32_to_e4m3fn(np.array([0.0, -0.0], np.float32))) == [0x00, 0x80]
+
+
+def _bf16_bits(x):
+    """float32 values that are bf16-exact -> bf16 bit patterns."""
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_rne_bits(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_quantize_group_hand_case():
+    # amax 896 gives s = 2; x / s: 3 -> 1.5 (0x3C), -896 -> -448 (0xFE), 1 -> 0.5 (0x30),
+    # 0.25 -> 0.125 (0x20), 0.001953125 -> 2^-10, a tie between 0 and 2^-9 that goes to 0,
+    # 448 -> 224 = 1.75 * 2^7 (exponent field 14, mantissa 6: 0x76).
+    x = np.zeros(128, np.float32)
+    x[:6] = [3.0, -896.0, 1.0, 0.25, 0.001953125, 448.0]
+    codes, s = O.quantize_group(_bf16_bits(x))
+    assert s == np.float32(2.0)
+    assert list(codes[:6]) == [0x3C, 0xFE, 0x30, 0x20, 0x00, 0x76]
+    assert (codes[6:] == 0).all()
+
+
+def test_quantize_group_scale_max_code_and_error_bound():
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        mag = 2.0 ** rng.uniform(-20, 20)
+        x = (rng.standard_normal(128) * mag).astype(np.float32)
+        bits = _bf16_rne_bits(x)
+        xv = O.bf16_to_f64(bits)
+        codes, s = O.quantize_group(bits)
+        amax = np.float32(np.abs(xv).max())
+        assert s == np.float32(amax / np.float32(448.0))
+        top = int(np.argmax(np.abs(xv)))
+        assert codes[top] & 0x7F == 0x7E                             # the largest magnitude is +-448
+        deq = O.e4m3fn_to_f64(codes) * float(s)
+        y = np.abs(xv) / float(s)
+        # half a unit in the last place: 2^-4 relative for normals, 2^-10 absolute (x s) below 2^-6,
+        # plus the fp32 rounding of x / s and of s itself
+        bound = np.where(y >= 2 ** -6, np.abs(xv) * 2 ** -4, float(s) * 2 ** -10) + np.abs(xv) * 2 ** -22 + 1e-300
+        assert (np.abs(deq - xv) <= bound).all(), trial
+        assert (np.signbit(deq[xv != 0]) == np.signbit(xv[xv != 0])).all()
+
+
+def test_quantize_all_zero_group():
+    codes, s = O.quantize_group(np.zeros(128, np.uint16))
+    assert s == 0 and (codes == 0).all()
+    codes, s = O.quantize_group(np.full(128, 0x8000, np.uint16))     # -0.0 everywhere
+    assert s == 0 and (codes == 0).all()
+
+
+def test_encode_record_layout_and_round_trip():
+    rng = np.random.default_rng(3)
+    tok = _bf16_rne_bits(rng.standard_normal(576).astype(np.float32) * np.repeat([1, 10, 0.01, 300, 1], [128] * 4 + [64]))
+    rec = O.encode_record(tok, O.KV_FP8)
+    assert rec.shape == (656,) and rec.dtype == np.uint8
+    for g in range(4):
+        codes, s = O.quantize_group(tok[128 * g:128 * (g + 1)])
+        np.testing.assert_array_equal(rec[128 * g:128 * (g + 1)], codes)
+        assert rec[512 + 4 * g:516 + 4 * g].view(np.float32)[0] == s
+    np.testing.assert_array_equal(rec[528:].view(np.uint16), tok[512:])
+    dec = O.decode_record(rec, O.KV_FP8)
+    xv = O.bf16_to_f64(tok)
+    np.testing.assert_array_equal(dec[512:], xv[512:])
+    scales = np.repeat(rec[512:528].view(np.float32).astype(np.float64), 128)
+    assert (np.abs(dec[:512] - xv[:512]) <= np.maximum(np.abs(xv[:512]) * 2 ** -4, scales * 2 ** -10) * 1.0001).all()
+    np.testing.assert_array_equal(O.encode_record(tok, O.KV_BF16).view(np.uint16), tok)
+
+
+def test_cache_write_slots():
+    cache = np.full((3, 64, 656), 0xAB, np.uint8)
+    rng = np.random.default_rng(5)
+    toks = _bf16_rne_bits(rng.standard_normal((4, 576)).astype(np.float32))
+    out = O.cache_write(cache, O.KV_FP8, toks, [5, -1, 64 * 3, 130])
+    flat = out.reshape(-1, 656)
+    np.testing.assert_array_equal(flat[5], O.encode_record(toks[0], O.KV_FP8))
+    np.testing.assert_array_equal(flat[130], O.encode_record(toks[3], O.KV_FP8))
+    untouched = np.ones(192, bool)
+    untouched[[5, 130]] = False
+    assert (flat[untouched] == 0xAB).all()
+    assert (cache == 0xAB).all()                                       # input not modified
+
+
+def _enc_mutant_truncate(x):
+    x = np.asarray(x, np.float32).astype(np.float64)
+    table = O.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    code = np.clip(np.searchsorted(table, np.abs(x), side="right") - 1, 0, 0x7E)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def _enc_mutant_ties_away(x):
+    x = np.asarray(x, np.float32).astype(np.float64)
+    table = O.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(np.abs(table[hi] - a) <= np.abs(a - table[lo]), hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mutant", [_enc_mutant_truncate, _enc_mutant_ties_away])
+def test_pins_catch_e4m3_encoder_mutants(mutant, monkeypatch):
+    monkeypatch.setattr(O, "f32_to_e4m3fn", mutant)
+    caught = 0
+    for t in (test_e4m3fn_encode_matches_torch_inside_the_range,
+              test_e4m3fn_encode_ties_go_to_even_and_large_values_saturate, test_quantize_group_hand_case):
+        try:
+            t()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
+
+
 def test_bf16_record_layout():
     vals = (np.arange(576, dtype=np.float32) % 64 - 32.0) / 4.0  # at most 7 significant bits: bf16-exact
     rec = (vals.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8)
