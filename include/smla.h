@@ -9,6 +9,8 @@
  *   4. runs MQA attention in which every head reads the same 576-wide latent record
  *      (512 latent + 64 rope; values are the first 512 entries), with one fixed reduction order
  *                                                [smla_sparse_mla_decode, smla_sparse_mla_prefill_chunk]
+ * and writes new tokens' records into the paged cache, quantizing them for FP8 caches
+ *                                                [smla_kv_cache_write]
  * The result for a row never depends on the other rows of the call.
  *
  * Sources (pages by title, section):
@@ -158,6 +160,30 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
                                           const int32_t* idx, int32_t T, int32_t H, int32_t k,
                                           float softmax_scale, void* out, float* lse, void* ws,
                                           size_t ws_bytes, void* stream);
+
+/* KV insert: writes the records of T new tokens into the paged cache (the step that produces the
+ * records smla_sparse_mla_decode gathers).
+ * Sources: "Port DeepSeek-V4 optimization PR #174 to v0.26 ..." (MooreThreads/vllm-musa PR 178), table
+ * "Optimizations carried from PR #174" (FP8 cache write, contiguous fp32 scale groups);
+ * "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", fused group-quantization section
+ * (128-element groups, FP32 scales); "[JJ] Preallocate DeepSeek V4 padded-query output", "Operation
+ * contract" (the KV-insert operator mutates caller-owned storage only).
+ *   kv_in:  bf16 [T, 576] (512 latent then 64 rope), token t at kv_in + t*in_row_stride elements
+ *           (in_row_stride >= 576, multiple of 8); 16-byte aligned.
+ *   slot_mapping: int64 [T]; token t is written to physical slot slot_mapping[t] = block id * 64 +
+ *           offset in the block.  Slots < 0 or >= num_pages*64 are skipped (nothing written).
+ *   cache:  [num_pages, 64, record] bytes per kv_dtype, 16-byte aligned; only the records of the
+ *           listed slots change.
+ *   SMLA_KV_BF16: the record is the 1152 input bytes.
+ *   SMLA_KV_FP8_E4M3_G128: for each 128-entry group g of the latent, amax = largest |x|,
+ *           s_g = amax / 448 and code = e4m3(x / s_g), both divisions IEEE fp32 round-to-nearest-
+ *           even, the quotient saturated to [-448, 448] and rounded to the nearest e4m3 value (ties
+ *           to even mantissa); a group of zeros stores s_g = 0 and zero codes; the rope is stored
+ *           unchanged.  Latent values must be finite (the codes of a group holding inf or NaN are
+ *           unspecified).
+ * Tokens mapped to the same slot race: which record remains is unspecified.  T = 0 enqueues nothing. */
+smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,
+                                void* cache, int32_t kv_dtype, int64_t num_pages, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "SmlaError", "KV_BF16", "KV_FP8", "Capacity", "library_path", "load_library", "exported_symbols",
     "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row", "topk_workspace",
-    "sparse_mla_decode", "sparse_mla_prefill_chunk",
+    "sparse_mla_decode", "sparse_mla_prefill_chunk", "kv_cache_write",
 ]
 
 KV_BF16 = 0
@@ -29,7 +29,7 @@ _LIB: Optional[ctypes.CDLL] = None
 exported_symbols = (
     "smla_last_error", "smla_version", "smla_is_supported", "smla_workspace_size",
     "smla_fill_causal_lengths", "smla_topk_per_row", "smla_sparse_mla_decode",
-    "smla_sparse_mla_prefill_chunk",
+    "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write",
 )
 
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_WORKSPACE",
@@ -79,6 +79,7 @@ def load_library() -> ctypes.CDLL:
                                    ctypes.c_int),
         "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, SZ, P],
                                           ctypes.c_int),
+        "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -281,3 +282,27 @@ def sparse_mla_prefill_chunk(q: torch.Tensor, kv: torch.Tensor, block_table_row:
                                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                              _stream(dev)))
     return out, lse
+
+
+def kv_cache_write(kv_in: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                   kv_dtype: Optional[int] = None) -> torch.Tensor:
+    """Writes the records of the tokens ``kv_in`` [T, 576] (bf16; rows may be strided) to the
+    physical slots ``slot_mapping`` [T] (int64; < 0 skipped) of ``cache`` (uint8 [num_pages, 64,
+    record]), quantizing to FP8 records for FP8 caches.  Returns ``cache``."""
+    lib = load_library()
+    _require(kv_in, "kv_in", torch.bfloat16, contiguous=False)
+    if kv_in.dim() != 2 or kv_in.shape[1] != 576 or kv_in.stride(1) != 1:
+        raise ValueError("kv_in must be [T, 576] with contiguous rows")
+    dev = kv_in.device
+    _require(slot_mapping, "slot_mapping", torch.int64, dev)
+    _require(cache, "cache", torch.uint8, dev)
+    T = kv_in.shape[0]
+    if slot_mapping.numel() < T:
+        raise ValueError("slot_mapping is shorter than T")
+    dt = _kv_dtype_of(cache, kv_dtype)
+    rec = 1152 if dt == KV_BF16 else 656
+    if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != rec:
+        raise ValueError(f"cache must be [num_pages, 64, {rec}] for kv_dtype {dt}")
+    _check(lib.smla_kv_cache_write(_ptr(kv_in), kv_in.stride(0), _ptr(slot_mapping), T, _ptr(cache), dt,
+                                   cache.shape[0], _stream(dev)))
+    return cache

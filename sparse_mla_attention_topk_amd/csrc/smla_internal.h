@@ -53,5 +53,7 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
                        hipStream_t stream);
 hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_kv_cache_write(const void* in, int64_t in_row_stride, const int64_t* slots, int32_t T, void* cache,
+                                 int kv_dtype, int64_t num_pages, hipStream_t stream);
 
 }  // namespace smla

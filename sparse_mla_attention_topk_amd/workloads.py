@@ -272,3 +272,27 @@ def prefill_chunk(device, seed: int = 4, T: int = 4096, ctx: int = 131072, H: in
     return PrefillWorkload(name=f"prefill_T{T}_ctx{ctx}_H{H}_k{k}_mixed{n_dec}", cache=cache, q=q,
                            scores=scores, first_pos=first_pos, decode=dec, mix_order=mix_order, H=H, k=k,
                            scale=SOFTMAX_SCALE)
+
+
+@dataclasses.dataclass
+class CacheWriteWorkload:
+    """New tokens to insert into a paged cache."""
+    tokens: torch.Tensor        # bf16 [T, 576]: 512 latent, 64 rope
+    slots: torch.Tensor         # int64 [T]: physical slot (page * 64 + offset) of each token
+    num_pages: int
+
+
+def cache_write_tokens(device, T: int, num_pages: int, seed: int = 5, spread: float = 8.0) -> CacheWriteWorkload:
+    """T tokens of bf16 N(0,1) values, each 128-entry latent group (and the rope) multiplied by its own
+    2**U(-spread, spread), rounded to bf16; the tokens go to T distinct slots of a cache of
+    ``num_pages`` pages (page 0 excluded), drawn by a seeded permutation."""
+    g = _gen(seed, device)
+    vals = torch.randn((T, D_QK), generator=g, device=device, dtype=torch.float32)
+    expo = torch.rand((T, 5), generator=g, device=device, dtype=torch.float32) * (2 * spread) - spread
+    mult = torch.exp2(expo).repeat_interleave(torch.tensor([128, 128, 128, 128, 64], device=device), dim=1)
+    tokens = (vals * mult).to(torch.bfloat16)
+    nslots = (num_pages - 1) * PAGE
+    if T > nslots:
+        raise ValueError("more tokens than slots")
+    slots = torch.randperm(nslots, generator=g, device=device)[:T] + PAGE
+    return CacheWriteWorkload(tokens=tokens, slots=slots.to(torch.int64), num_pages=num_pages)

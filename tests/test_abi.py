@@ -165,3 +165,27 @@ def test_python_binding_requires_gpu_tensors():
     import torch
     with pytest.raises(ValueError):
         smla.topk_per_row(torch.zeros((2, 8)), 2)
+
+
+def test_kv_cache_write_validation(lib):
+    f = lib.smla_kv_cache_write
+    P = _fake
+    st = f(P(0x1000), 576, P(0x2000), 4, P(0x3000), 9, 10, None)
+    assert st == 2 and b"kv_dtype=9" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), -1, P(0x3000), 1, 10, None)
+    assert st == 1 and b"T=-1" in lib.smla_last_error()
+    st = f(P(0x1000), 500, P(0x2000), 4, P(0x3000), 1, 10, None)
+    assert st == 1 and b"in_row_stride=500" in lib.smla_last_error()
+    st = f(P(0x1000), 580, P(0x2000), 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"in_row_stride=580" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), 4, P(0x3000), 1, 0, None)
+    assert st == 1 and b"num_pages=0" in lib.smla_last_error()
+    st = f(P(0x1000), 576, None, 4, P(0x3000), 1, 10, None)
+    assert st == 1 and b"slot_mapping is NULL" in lib.smla_last_error()
+    st = f(P(0x1008), 576, P(0x2000), 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"kv_in must be 16-byte aligned" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2004), 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"slot_mapping" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), 4, P(0x3008), 1, 10, None)
+    assert st == 4 and b"cache must be 16-byte aligned" in lib.smla_last_error()
+    assert f(None, 576, None, 0, None, 1, 10, None) == 0        # T = 0: nothing to do
