@@ -33,9 +33,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8"],
+    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8"],
                     help="decode_bf16: B=64, contexts U[8192, 65536], bf16 KV (the headline); "
-                         "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV")
+                         "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV; "
+                         "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     return ap.parse_args()
@@ -88,12 +89,92 @@ def cpu_baseline(wl, n_rows):
                       f"{t_total:.1f} s on {os.cpu_count()} host cores' machine"}
 
 
+def _graph_time(torch, s, fn, n, warmup):
+    """ms per call of fn over one HIP graph of n calls (after a graph of warmup calls), timed with
+    events on the stream the kernels run on."""
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gw, g = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=s):
+            for i in range(warmup):
+                fn(i)
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        gw.replay()
+        torch.cuda.synchronize()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def bench_kv_write(args):
+    """FP8 cache write: T = 65536 new tokens (a 64K-token prefill) into a paged cache, four
+    rotating token sets so the 75 MB of input per call is not cache-resident; plus T = 128 (one
+    decode step of the FP8 decode workload's batch)."""
+    import numpy as np
+    import torch
+
+    import sparse_mla_attention_topk_amd as smla
+    from sparse_mla_attention_topk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, pages = 65536, 4200
+    sets = [W.cache_write_tokens(dev, T=T, num_pages=pages, seed=20 + i) for i in range(N_SETS)]
+    cache = torch.zeros((pages, 64, W.FP8_RECORD_BYTES), dtype=torch.uint8, device=dev)
+    small = W.cache_write_tokens(dev, T=128, num_pages=pages, seed=30)
+    for w in sets + [small]:
+        smla.kv_cache_write(w.tokens, w.slots, cache)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(dev)
+    big_ms = _graph_time(torch, s, lambda i: smla.kv_cache_write(sets[i % N_SETS].tokens, sets[i % N_SETS].slots,
+                                                                 cache), args.steps, args.warmup)
+    small_ms = _graph_time(torch, s, lambda i: smla.kv_cache_write(small.tokens, small.slots, cache), args.steps,
+                           args.warmup)
+    per_tok = 2 * 576 + W.FP8_RECORD_BYTES + 8          # bf16 token in, record out, slot
+    achieved = T * per_tok / (big_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_rows > 0:
+        import oracle.reference as O
+        toks = sets[0].tokens[:args.cpu_rows * 8].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        for t in toks:
+            O.encode_record(t, O.KV_FP8)
+        dt = time.perf_counter() - t0
+        cpu = {"value": len(toks) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{len(toks)} tokens of the same workload encoded by the oracle (numpy, 1 thread), "
+                         f"{dt:.1f} s"}
+    line = {
+        "metric": "FP8 KV cache write tokens/s (e4m3, 128-entry fp32 scale groups, T=65536, 1 GPU)",
+        "value": T / (big_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": big_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "kv_write_fp8_T65536", "tokens": T, "record_bytes": W.FP8_RECORD_BYTES,
+                   "rotating_sets": N_SETS, "launch": "hip_graph_of_K_calls"},
+        "decode_step_T128_us": small_ms * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "kv_cache_write_kernel<true>",
+                     "algorithmic_bytes_per_launch": T * per_tok},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (rows shard across GPUs "
               f"without any exchange, so the per-GPU figure is the one to read)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "kv_write_fp8":
+        return bench_kv_write(args)
     import torch
 
     import sparse_mla_attention_topk_amd as smla

@@ -175,11 +175,11 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
  *   cache:  [num_pages, 64, record] bytes per kv_dtype, 16-byte aligned; only the records of the
  *           listed slots change.
  *   SMLA_KV_BF16: the record is the 1152 input bytes.
- *   SMLA_KV_FP8_E4M3_G128: for each 128-entry group g of the latent, amax = largest |x|,
- *           s_g = amax / 448 and code = e4m3(x / s_g), both divisions IEEE fp32 round-to-nearest-
- *           even, the quotient saturated to [-448, 448] and rounded to the nearest e4m3 value (ties
- *           to even mantissa); a group of zeros stores s_g = 0 and zero codes; the rope is stored
- *           unchanged.  Latent values must be finite (the codes of a group holding inf or NaN are
+ *   SMLA_KV_FP8_E4M3_G128: for each 128-entry group g of the latent, amax = largest |x|; the
+ *           stored scale is s_g = amax / 448 and code = e4m3(x * r_g) with r_g = 448 / amax (IEEE
+ *           fp32 divisions and product, round-to-nearest-even), the product saturated to
+ *           [-448, 448] and rounded to the nearest e4m3 value (ties to even mantissa); a group of
+ *           zeros stores s_g = 0 and zero codes; the rope is stored unchanged.  Latent values must be finite (the codes of a group holding inf or NaN are
  *           unspecified).
  * Tokens mapped to the same slot race: which record remains is unspecified.  T = 0 enqueues nothing. */
 smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,

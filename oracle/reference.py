@@ -47,11 +47,12 @@ design notes):
   selected token has output 0 and LSE -inf;
 * the FP8 record is [512 e4m3 codes | 4 fp32 scales | 64 bf16 rope]; latent
   entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format;
-* the cache write quantizes group g of a token's 512 latent values with the
-  fp32 scale s = amax / 448 (amax = largest magnitude in the group) and the
-  codes e4m3(x / s), both divisions in fp32 with round-to-nearest-even, the
-  code rounded to nearest-even and saturated at +-448; an all-zero group gets
-  s = 0 and zero codes; the 64 rope values are stored unchanged.
+* the cache write quantizes group g of a token's 512 latent values so that
+  the group's largest magnitude amax maps to 448: the stored fp32 scale is
+  s = amax / 448 and the codes are e4m3(x * r) with the fp32 multiplier
+  r = 448 / amax (each division and the product rounded to nearest-even in
+  fp32; the code rounded to nearest-even and saturated at +-448); an all-zero
+  group gets s = 0 and zero codes; the 64 rope values are stored unchanged.
 """
 
 from __future__ import annotations
@@ -136,13 +137,15 @@ def f32_to_e4m3fn(x) -> np.ndarray:
 
 def quantize_group(x_bits: np.ndarray) -> Tuple[np.ndarray, np.float32]:
     """One 128-entry scale group of bf16 latent values -> (e4m3 codes [128], fp32 scale).
-    s = fp32(amax / 448), codes = e4m3(fp32(x / s)); an all-zero group has s = 0, codes 0."""
+    s = fp32(amax / 448), r = fp32(448 / amax), codes = e4m3(fp32(x * r)); an all-zero group has
+    s = 0, codes 0."""
     x = bf16_to_f64(x_bits).astype(np.float32)                        # exact widening
     amax = np.float32(np.max(np.abs(x)))
     if amax == 0:
         return np.zeros(len(x), dtype=np.uint8), np.float32(0.0)
     s = np.float32(amax / np.float32(448.0))                          # IEEE fp32 division
-    y = (x / s).astype(np.float32)                                    # IEEE fp32 division
+    r = np.float32(np.float32(448.0) / amax)                          # IEEE fp32 division
+    y = (x * r).astype(np.float32)                                    # IEEE fp32 product
     return f32_to_e4m3fn(y), s
 
 

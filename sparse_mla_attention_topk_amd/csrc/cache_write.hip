@@ -9,22 +9,24 @@
 // "[Bugfix] Make DSV4 sparse MLA work end-to-end ...", section "Purpose" (slot = block id * block
 // size + offset).
 //
-// One wave per token, four tokens per 256-thread workgroup; every token is independent, so the
-// result does not depend on how tokens are batched.
+// One wave per two tokens (both tokens' loads are issued before either is converted), eight tokens
+// per 256-thread workgroup; every token is independent, so the result does not depend on how
+// tokens are batched.
 //   bf16 record: the 1152 input bytes, copied (lanes 0..63 one 16-byte chunk each, lanes 0..7 one more).
 //   FP8 record [512 codes | 4 fp32 scales | 64 bf16 rope]: lane l holds latent values 8l .. 8l+7,
-//   which lie in scale group l / 16.  The group's largest magnitude comes from a max over its 16
-//   lanes; s = amax / 448 and every code is e4m3(x / s), both IEEE fp32 divisions.  The quotient is
-//   clamped to [-448, 448] (saturation) and converted by the hardware OCP E4M3 conversion, which rounds
-//   to nearest even.  An all-zero group stores s = 0 and zero codes.  Lane 16g stores s_g; lanes 0..7
-//   copy the rope.
+//   which lie in scale group l / 16.  The group's largest magnitude amax comes from a max over its 16
+//   lanes (one DPP row); the stored scale is s = amax / 448 and every code is e4m3(x * r) with
+//   r = 448 / amax (IEEE fp32 divisions and product).  x * r is clamped to [-448, 448] (saturation)
+//   and converted by the hardware OCP E4M3 conversion, which rounds to nearest even.  An all-zero
+//   group stores s = 0 and zero codes.  Lane 16g stores s_g; lanes 0..7 copy the rope.
 #include "smla_device.h"
 #include "smla_internal.h"
 
 namespace smla {
 namespace {
 
-constexpr int kTokPerBlock = 4;   // one wave per token
+constexpr int kTokPerWave = 2;
+constexpr int kTokPerBlock = 4 * kTokPerWave;
 
 // Codes of two fp32 values (already inside [-448, 448]) into bytes 0-1 (HI false) or 2-3 of `old`.
 template <bool HI>
@@ -32,55 +34,78 @@ __device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) 
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
-__device__ __forceinline__ float sat448(float y) { return fminf(fmaxf(y, -448.f), 448.f); }
+__device__ __forceinline__ float sat448(float y) { return __builtin_amdgcn_fmed3f(y, -448.f, 448.f); }
+
+// Max over the 16 lanes of each DPP row (rotations by 8, 4, 2, 1 within the row).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+    return v;
+}
+
+// One token's FP8 record from the lane's 8 latent values `lat`.
+__device__ __forceinline__ void write_fp8_record(uint8_t* dst, int lane, uint4 lat, uint4 rope) {
+    const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // bf16 -> fp32 is exact
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = row16_max(amax);   // lanes 16g .. 16g+15 hold group g
+    uint32_t lo = 0u, hi = 0u;
+    float s = 0.f;
+    if (amax > 0.f) {
+        s = amax / 448.f;
+        const float r = 448.f / amax;
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = sat448(x[i] * r);
+        lo = pack_e4m3x2<false>(y[0], y[1], 0u);
+        lo = pack_e4m3x2<true>(y[2], y[3], lo);
+        hi = pack_e4m3x2<false>(y[4], y[5], 0u);
+        hi = pack_e4m3x2<true>(y[6], y[7], hi);
+    }
+    *(uint2*)(dst + 8 * lane) = make_uint2(lo, hi);
+    if ((lane & 15) == 0) *(float*)(dst + 512 + 4 * (lane >> 4)) = s;
+    if (lane < 8) *(uint4*)(dst + 528 + 16 * lane) = rope;
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(const uint16_t* __restrict__ in, int64_t in_row_stride,
                                                              const int64_t* __restrict__ slots, int32_t T,
                                                              uint8_t* __restrict__ cache, int64_t num_slots) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) return;   // padding or out-of-range slot: nothing written
-    const uint16_t* src = in + t * in_row_stride;
-    const uint4 lat = *(const uint4*)(src + 8 * lane);
-    uint4 rope = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 8) rope = *(const uint4*)(src + 512 + 8 * lane);
-    if constexpr (!FP8) {
-        uint8_t* dst = cache + slot * kBf16Record;
-        *(uint4*)(dst + 16 * lane) = lat;
-        if (lane < 8) *(uint4*)(dst + 1024 + 16 * lane) = rope;
-        return;
-    } else {
-        uint8_t* dst = cache + slot * kFp8Record;
-        const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
-        float x[8];
+    const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kTokPerWave;
+    uint4 lat[kTokPerWave], rope[kTokPerWave];
+    int64_t slot[kTokPerWave];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {   // bf16 -> fp32 is exact
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int j = 0; j < kTokPerWave; ++j) {   // every load first (wave-uniform guards)
+        const int64_t t = t0 + j;
+        slot[j] = -1;
+        lat[j] = rope[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (t < T) {
+            slot[j] = slots[t];
+            const uint16_t* src = in + t * in_row_stride;
+            lat[j] = *(const uint4*)(src + 8 * lane);
+            if (lane < 8) rope[j] = *(const uint4*)(src + 512 + 8 * lane);
         }
-        float amax = 0.f;
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));   // the group's 16 lanes
-        uint32_t lo = 0u, hi = 0u;
-        float s = 0.f;
-        if (amax > 0.f) {
-            s = amax / 448.f;
-            float y[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = sat448(x[i] / s);
-            lo = pack_e4m3x2<false>(y[0], y[1], 0u);
-            lo = pack_e4m3x2<true>(y[2], y[3], lo);
-            hi = pack_e4m3x2<false>(y[4], y[5], 0u);
-            hi = pack_e4m3x2<true>(y[6], y[7], hi);
+    for (int j = 0; j < kTokPerWave; ++j) {
+        if (slot[j] < 0 || slot[j] >= num_slots) continue;   // past T, padding or out of range: nothing written
+        if constexpr (!FP8) {
+            uint8_t* dst = cache + slot[j] * kBf16Record;
+            *(uint4*)(dst + 16 * lane) = lat[j];
+            if (lane < 8) *(uint4*)(dst + 1024 + 16 * lane) = rope[j];
+        } else {
+            write_fp8_record(cache + slot[j] * kFp8Record, lane, lat[j], rope[j]);
         }
-        *(uint2*)(dst + 8 * lane) = make_uint2(lo, hi);
-        if ((lane & 15) == 0) *(float*)(dst + 512 + 4 * (lane >> 4)) = s;
-        if (lane < 8) *(uint4*)(dst + 528 + 16 * lane) = rope;
     }
 }
 

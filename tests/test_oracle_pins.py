@@ -266,6 +266,21 @@ def test_quantize_group_hand_case():
     assert (codes[6:] == 0).all()
 
 
+def test_quantize_group_multiplier_reading():
+    # The codes are e4m3(x * r) with r = fp32(448 / amax), not e4m3(x / s).  amax = 416: r rounds up
+    # (fp32(448/416) > 448/416), so x = -312 gives x * r just beyond -336, the midpoint of -320 (0xFA)
+    # and -352 (0xFB), and the code is 0xFB; the quotient x / s would land on -336 exactly and tie to
+    # the even 0xFA.
+    r = np.float32(448.0) / np.float32(416.0)
+    assert float(r) > 448.0 / 416.0
+    assert float(np.float32(np.float32(-312.0) * r)) < -336.0
+    x = np.zeros(128, np.float32)
+    x[0], x[1] = 416.0, -312.0
+    codes, s = O.quantize_group(_bf16_bits(x))
+    assert s == np.float32(np.float32(416.0) / np.float32(448.0))
+    assert codes[0] == 0x7E and codes[1] == 0xFB
+
+
 def test_quantize_group_scale_max_code_and_error_bound():
     rng = np.random.default_rng(11)
     for trial in range(200):
