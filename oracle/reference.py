@@ -45,6 +45,12 @@ design notes):
   the value vector is its first 512 entries;
 * LSE is the natural-log log-sum-exp of the scaled scores; a row with no
   selected token has output 0 and LSE -inf;
+* an attention sink is one logit per head (in the units of the scaled scores)
+  that joins the softmax denominator and carries no value: p_j = e^{s_j} /
+  (e^{sink} + sum_i e^{s_i}), LSE = log(e^{sink} + sum_i e^{s_i}); -inf means no
+  sink ("[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", section
+  "MHC, CUDA graphs, and weight reload": the sink weights keep their -inf
+  padding);
 * the FP8 record is [512 e4m3 codes | 4 fp32 scales | 64 bf16 rope]; latent
   entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format;
 * the cache write quantizes group g of a token's 512 latent values so that
@@ -269,22 +275,25 @@ def gather_tokens(kv: np.ndarray, kv_dtype: int, block_table_row: np.ndarray,
 # A7-A9: MQA attention over the gathered latent tokens
 # ----------------------------------------------------------------------------------------------
 
-def attention(q: np.ndarray, K: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+def attention(q: np.ndarray, K: np.ndarray, scale: float,
+              sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of every head of ``q`` [H, 576] over the shared tokens ``K`` [n, 576].
 
-    s[h, j] = scale * <q_h, K_j> over all 576 entries; p[h, :] = softmax(s[h, :]);
-    O[h, :] = sum_j p[h, j] * K_j[:512]; LSE[h] = log sum_j exp(s[h, j]).
-    With n = 0 the output is 0 and LSE is -inf.
+    s[h, j] = scale * <q_h, K_j> over all 576 entries; the softmax denominator of head h is
+    D_h = sum_j exp(s[h, j]) + exp(sink[h]) (no sink term when ``sink`` is None or -inf);
+    O[h, :] = sum_j (exp(s[h, j]) / D_h) * K_j[:512]; LSE[h] = log D_h.
+    With n = 0 the output is 0 and LSE is sink[h] (-inf without a sink).
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     H = q.shape[0]
+    sk = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64).reshape(H)
     if K.shape[0] == 0:
-        return np.zeros((H, D_V)), np.full(H, -np.inf)
+        return np.zeros((H, D_V)), sk.copy()
     s = scale * (q @ K.T)                       # [H, n]
-    m = s.max(axis=1, keepdims=True)
+    m = np.maximum(s.max(axis=1), sk)[:, None]  # [H, 1], finite: n >= 1
     e = np.exp(s - m)
-    l = e.sum(axis=1, keepdims=True)
+    l = e.sum(axis=1, keepdims=True) + np.exp(sk[:, None] - m)
     p = e / l
     O = p @ K[:, :D_V]
     lse = (m + np.log(l))[:, 0]
@@ -318,9 +327,11 @@ def split_combine(parts: Sequence[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np.nd
 
 def attention_rows(q_bits: np.ndarray, kv: np.ndarray, kv_dtype: int, block_table: np.ndarray,
                    row_req: Optional[Sequence[int]], idx: np.ndarray, scale: float,
-                   rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                   rows: Optional[Sequence[int]] = None,
+                   sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention for each requested row over the tokens listed in ``idx`` [R, k] (entries -1
-    are skipped).  ``q_bits`` holds bf16 patterns [R, H, 576]."""
+    are skipped).  ``q_bits`` holds bf16 patterns [R, H, 576]; ``sink`` is the per-head sink
+    logit [H] or None."""
     sel = list(range(idx.shape[0])) if rows is None else list(rows)
     H = q_bits.shape[1]
     O = np.zeros((len(sel), H, D_V))
@@ -329,7 +340,7 @@ def attention_rows(q_bits: np.ndarray, kv: np.ndarray, kv_dtype: int, block_tabl
         req = 0 if row_req is None else int(row_req[r])
         pos = [int(p) for p in idx[r] if p >= 0]
         K = gather_tokens(kv, kv_dtype, block_table[req], pos)
-        O[o], LSE[o] = attention(bf16_to_f64(q_bits[r]), K, scale)
+        O[o], LSE[o] = attention(bf16_to_f64(q_bits[r]), K, scale, sink)
     return O, LSE
 
 

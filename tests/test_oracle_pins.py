@@ -493,6 +493,46 @@ def test_attention_single_token_and_empty():
     assert (Oe == 0).all() and np.isneginf(le).all()
 
 
+def test_attention_sink_minus_inf_is_no_sink():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((16, 576))
+    K = rng.standard_normal((40, 576))
+    O0, l0 = O.attention(q, K, 1 / 24)
+    O1, l1 = O.attention(q, K, 1 / 24, np.full(16, -np.inf))
+    np.testing.assert_array_equal(O0, O1)
+    np.testing.assert_array_equal(l0, l1)
+
+
+def test_attention_sink_is_a_valueless_extra_split():
+    # The sink adds e^sink to the denominator and nothing to the numerator: the same as combining the
+    # sink-free result with one more split whose output is 0 and whose LSE is the sink.
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((16, 576))
+    K = rng.standard_normal((50, 576))
+    sink = rng.standard_normal(16) * 3
+    sink[3] = -np.inf
+    O_s, l_s = O.attention(q, K, 1 / 24, sink)
+    O_c, l_c = O.split_combine([O.attention(q, K, 1 / 24), (np.zeros((16, 512)), sink)])
+    np.testing.assert_allclose(O_s, O_c, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l_s, l_c, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_sink_closed_forms():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, 576))
+    K = rng.standard_normal((1, 576))
+    s = (q @ K.T)[0, 0] / 24
+    sink = np.array([0.7])
+    Ov, lv = O.attention(q, K, 1 / 24, sink)
+    p = 1.0 / (1.0 + math.exp(sink[0] - s))                        # one token against the sink
+    np.testing.assert_allclose(Ov[0], p * K[0, :512], rtol=1e-12)
+    assert abs(lv[0] - math.log(math.exp(s) + math.exp(0.7))) < 1e-12
+    Oe, le = O.attention(q, np.zeros((0, 576)), 1 / 24, sink)      # no tokens: O = 0, LSE = sink
+    assert (Oe == 0).all() and le[0] == 0.7
+    Ob, _ = O.attention(q, K, 1 / 24, np.array([500.0]))           # a dominant sink drives O to 0
+    assert np.abs(Ob).max() < 1e-100
+
+
 def test_split_combine_equals_single_pass():
     rng = np.random.default_rng(10)
     q = rng.standard_normal((6, 576)); K = rng.standard_normal((90, 576)) * 2
