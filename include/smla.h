@@ -134,11 +134,17 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
  *   row_req: int32 [rows] request id of each row, or NULL for "request 0".
  *   idx:    int32 [rows, k] logical token positions (from smla_topk_per_row); entries < 0 skipped.
  *   For row r and head h: s_j = softmax_scale * <q[r,h,:], K_j> over the 576 entries of each
- *   listed token's record K_j; p = softmax over the listed tokens; out[r,h,:] = sum_j p_j K_j[0:512]
- *   rounded to bf16 (RNE); lse[r,h] = natural-log log-sum-exp of s (fp32).  A row with no valid
- *   token gets out = 0 and lse = -inf.  Slots are reduced in a fixed order that depends only on k:
- *   the k slots are cut into ceil(k/512) splits, each split accumulates its tiles in slot order with
- *   an fp32 online softmax, and the splits are combined in split order.
+ *   listed token's record K_j; D = sum_j e^{s_j} + e^{sink[h]}; out[r,h,:] = sum_j (e^{s_j} / D)
+ *   K_j[0:512] rounded to bf16 (RNE); lse[r,h] = ln D (fp32).  Without a sink (sink NULL, or
+ *   sink[h] = -inf) the e^{sink} term is absent and p is the plain softmax.  A row with no valid
+ *   token gets out = 0 and lse = sink[h] (-inf without a sink).  Slots are reduced in a fixed order
+ *   that depends only on k: the k slots are cut into ceil(k/512) splits, each split accumulates its
+ *   tiles in slot order with an fp32 online softmax, the splits are combined in split order, and
+ *   the sink term comes last.
+ *   sink:   fp32 [H] per-head attention-sink logits, in the units of the scaled scores, or NULL
+ *           ("[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", section "MHC, CUDA
+ *           graphs, and weight reload": sink weights keep -inf padding, i.e. -inf = no sink);
+ *           entries must be finite or -inf; 4-byte aligned.
  *   out: bf16 [rows, H, 512], 16-byte aligned; lse: fp32 [rows, H] or NULL.
  *   ws: attention workspace (256-byte aligned) of at least the size smla_workspace_size reports for
  *   a capacity with max_rows >= 1; rows beyond what it holds are processed in further launches.
@@ -148,7 +154,7 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
 smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                    int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
                                    int32_t num_reqs, const int32_t* row_req, const int32_t* idx,
-                                   int32_t rows, int32_t H, int32_t k, float softmax_scale,
+                                   int32_t rows, int32_t H, int32_t k, float softmax_scale, const float* sink,
                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill chunk of one request: T query rows that all read the request whose block table row is
@@ -158,8 +164,8 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
                                           int32_t kv_dtype, int64_t num_pages,
                                           const int32_t* block_table_row, int64_t bt_len,
                                           const int32_t* idx, int32_t T, int32_t H, int32_t k,
-                                          float softmax_scale, void* out, float* lse, void* ws,
-                                          size_t ws_bytes, void* stream);
+                                          float softmax_scale, const float* sink, void* out, float* lse,
+                                          void* ws, size_t ws_bytes, void* stream);
 
 /* KV insert: writes the records of T new tokens into the paged cache (the step that produces the
  * records smla_sparse_mla_decode gathers).

@@ -75,9 +75,9 @@ def load_library() -> ctypes.CDLL:
         "smla_workspace_size": ([ctypes.POINTER(Capacity), ctypes.POINTER(SZ), ctypes.POINTER(SZ)], ctypes.c_int),
         "smla_fill_causal_lengths": ([I64, I32, P, P], ctypes.c_int),
         "smla_topk_per_row": ([P, P, I64, P, I32, I32, P, P, SZ, P], ctypes.c_int),
-        "smla_sparse_mla_decode": ([P, I64, P, I32, I64, P, I64, I32, P, P, I32, I32, I32, F32, P, P, P, SZ, P],
-                                   ctypes.c_int),
-        "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, SZ, P],
+        "smla_sparse_mla_decode": ([P, I64, P, I32, I64, P, I64, I32, P, P, I32, I32, I32, F32, P, P, P, P, SZ,
+                                    P], ctypes.c_int),
+        "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, P, SZ, P],
                                           ctypes.c_int),
         "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
     }
@@ -201,6 +201,13 @@ def _attn_outputs(rows: int, H: int, device, out, lse):
     return out, lse
 
 
+def _check_sink(sink: Optional[torch.Tensor], H: int, device) -> None:
+    if sink is not None:
+        _require(sink, "sink", torch.float32, device)
+        if sink.numel() < H:
+            raise ValueError("sink is shorter than H")
+
+
 def _kv_dtype_of(kv: torch.Tensor, kv_dtype: Optional[int]) -> int:
     if kv_dtype is not None:
         return int(kv_dtype)
@@ -228,10 +235,12 @@ def attention_workspace(rows: int, H: int, k: int, device, kv_dtype: int = KV_BF
 def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, idx: torch.Tensor,
                       softmax_scale: float, row_req: Optional[torch.Tensor] = None,
                       kv_dtype: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      sink: Optional[torch.Tensor] = None):
     """Sparse MLA attention of each row of ``q`` [rows, H, 576] (bf16) over the tokens in ``idx``
     [rows, k] (int32 logical positions, -1 skipped) of the paged cache ``kv`` (uint8 bytes
-    [num_pages, 64, record]).  Returns (out bf16 [rows, H, 512], lse fp32 [rows, H] or None)."""
+    [num_pages, 64, record]), with optional per-head sink logits ``sink`` (fp32 [H], -inf = none).
+    Returns (out bf16 [rows, H, 512], lse fp32 [rows, H] or None)."""
     lib = load_library()
     _require(q, "q", torch.bfloat16, contiguous=False)
     if q.dim() != 3 or q.shape[2] != 576 or q.stride(2) != 1 or q.stride(1) != 576:
@@ -246,6 +255,7 @@ def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tens
         raise ValueError("idx is smaller than rows*k")
     if row_req is not None:
         _require(row_req, "row_req", torch.int32, dev)
+    _check_sink(sink, H, dev)
     out, lse = _attn_outputs(rows, H, dev, out, lse)
     if workspace is None:
         workspace = attention_workspace(rows, H, k, dev, _kv_dtype_of(kv, kv_dtype))
@@ -253,15 +263,15 @@ def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tens
     bt2 = block_table if block_table.dim() == 2 else block_table.view(1, -1)
     _check(lib.smla_sparse_mla_decode(_ptr(q), q.stride(0), _ptr(kv), _kv_dtype_of(kv, kv_dtype), kv.shape[0],
                                       _ptr(bt2), bt2.shape[1], bt2.shape[0], _ptr(row_req), _ptr(idx), rows, H, k,
-                                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                      _stream(dev)))
+                                      float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      ws_bytes, _stream(dev)))
     return out, lse
 
 
 def sparse_mla_prefill_chunk(q: torch.Tensor, kv: torch.Tensor, block_table_row: torch.Tensor, idx: torch.Tensor,
                              softmax_scale: float, kv_dtype: Optional[int] = None,
                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                             workspace: Optional[torch.Tensor] = None):
+                             workspace: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None):
     """Prefill chunk of one request: every row of ``q`` reads the request of ``block_table_row``."""
     lib = load_library()
     _require(q, "q", torch.bfloat16, contiguous=False)
@@ -273,14 +283,15 @@ def sparse_mla_prefill_chunk(q: torch.Tensor, kv: torch.Tensor, block_table_row:
     _require(idx, "idx", torch.int32, dev)
     T, H = q.shape[0], q.shape[1]
     k = idx.shape[-1]
+    _check_sink(sink, H, dev)
     out, lse = _attn_outputs(T, H, dev, out, lse)
     if workspace is None:
         workspace = attention_workspace(T, H, k, dev, _kv_dtype_of(kv, kv_dtype))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.smla_sparse_mla_prefill_chunk(_ptr(q), q.stride(0), _ptr(kv), _kv_dtype_of(kv, kv_dtype), kv.shape[0],
                                              _ptr(block_table_row), block_table_row.numel(), _ptr(idx), T, H, k,
-                                             float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                             _stream(dev)))
+                                             float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace),
+                                             ws_bytes, _stream(dev)))
     return out, lse
 
 

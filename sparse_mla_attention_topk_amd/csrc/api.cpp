@@ -183,28 +183,33 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
 smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                    int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
                                    int32_t num_reqs, const int32_t* row_req, const int32_t* idx, int32_t rows,
-                                   int32_t H, int32_t k, float softmax_scale, void* out, float* lse, void* ws,
-                                   size_t ws_bytes, void* stream) {
+                                   int32_t H, int32_t k, float softmax_scale, const float* sink, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
     smla_status st = check_attention(q, q_row_stride, kv, kv_dtype, num_pages, block_table, bt_stride, num_reqs, idx,
                                      rows, H, k, softmax_scale, out, lse, ws, ws_bytes);
     if (st != SMLA_OK) return st;
     if (rows == 0) return ok();
     if (row_req && !aligned(row_req, 4)) return fail(SMLA_ERR_ALIGNMENT, "row_req must be 4-byte aligned");
-    smla::AttnArgs a{q,  q_row_stride, kv,  kv_dtype, num_pages, block_table,   bt_stride, num_reqs, row_req,
-                     idx, rows,        H,   k,        softmax_scale, out,       lse,       ws,       ws_bytes};
+    if (sink && !aligned(sink, 4)) return fail(SMLA_ERR_ALIGNMENT, "sink must be 4-byte aligned");
+    smla::AttnArgs a{q,   q_row_stride, kv,  kv_dtype,      num_pages, block_table, bt_stride, num_reqs, row_req,
+                     idx, rows,         H,   k,             softmax_scale, sink,    out,       lse,      ws,
+                     ws_bytes};
     return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_decode");
 }
 
 smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                           int64_t num_pages, const int32_t* block_table_row, int64_t bt_len,
                                           const int32_t* idx, int32_t T, int32_t H, int32_t k, float softmax_scale,
-                                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                                          const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                                          void* stream) {
     smla_status st = check_attention(q, q_row_stride, kv, kv_dtype, num_pages, block_table_row, bt_len, 1, idx, T, H,
                                      k, softmax_scale, out, lse, ws, ws_bytes);
     if (st != SMLA_OK) return st;
     if (T == 0) return ok();
-    smla::AttnArgs a{q,   q_row_stride, kv, kv_dtype, num_pages,     block_table_row, bt_len, 1,  nullptr,
-                     idx, T,            H,  k,        softmax_scale, out,             lse,    ws, ws_bytes};
+    if (sink && !aligned(sink, 4)) return fail(SMLA_ERR_ALIGNMENT, "sink must be 4-byte aligned");
+    smla::AttnArgs a{q,   q_row_stride, kv, kv_dtype, num_pages,     block_table_row, bt_len, 1,   nullptr,
+                     idx, T,            H,  k,        softmax_scale, sink,            out,    lse, ws,
+                     ws_bytes};
     return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_prefill_chunk");
 }
 

@@ -93,6 +93,7 @@ struct AttnParams {
     float* lse;
     void* ws_o;          // [rows][splits][H][512] split partials: bf16 (bf16 cache) or fp32 (FP8 cache)
     float* ws_lse;       // fp32 [rows][splits][H]
+    const float* sink;   // fp32 [H] per-head sink logits (natural-log units of the scaled scores), or null
 };
 
 // One direct-to-LDS 16-byte load: lane l's 16 bytes at `g` land at LDS byte lds_base + 16 l.  Issued
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // tile it+1 is expanded)
     __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
-    __shared__ float xsum[4][16];      // per-head weight sums at the end
+    __shared__ float xmul[4][16];      // per-head output multiplier at the end
     __shared__ int s_first, s_last;
     auto xs = [&](int b, int j) -> f32x4_t* { return &xs_own[b][j][0]; };
     auto pw32 = [&](int b, int j) -> f32x4_t* { return (f32x4_t*)&pfrag[b][0][0] + j * kWave; };   // FP8 weights
@@ -561,12 +562,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
             if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);
         }
-        // ---- A10 (score waves): total weight and LSE of the first halves' heads ----
+        // ---- A10 (score waves): output multiplier and LSE of the first halves' heads.  With one
+        // split the sink joins here: it adds e^sink to the denominator and nothing to the output.
+        // With several splits the split results exclude it and the combine adds it last. ----
         const float l_tot = head_sum(l_run);
-        if (score_ok && !half && lane < 16) xsum[shb][lane] = l_tot;
+        float mult = 0.f, lse_v = -INFINITY;
+        if (score_ok && !half && lane < 16) {
+            const int head = head0 + shb * 16 + lane;
+            const float snk = (p.sink && p.n_splits == 1) ? p.sink[head] : -INFINITY;
+            if (snk == -INFINITY) {
+                if (l_tot > 0.f) {
+                    mult = 1.f / l_tot;
+                    lse_v = (m_run + __log2f(l_tot)) * kLn2;
+                }
+            } else if (!(l_tot > 0.f)) {
+                lse_v = snk;                  // no token: output 0, LSE = the sink
+            } else {
+                const float s2 = snk * kLog2e;
+                const float mn = fmaxf(m_run, s2);
+                const float c = __builtin_amdgcn_exp2f(m_run - mn);
+                const float lall = l_tot * c + __builtin_amdgcn_exp2f(s2 - mn);
+                mult = c / lall;
+                lse_v = (mn + __log2f(lall)) * kLn2;
+            }
+            xmul[shb][lane] = mult;
+        }
         __syncthreads();
         if (score_ok && !half && lane < 16) {
-            const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
             const int head = head0 + shb * 16 + lane;
             if (p.n_splits == 1) {
                 if (p.lse) p.lse[row * p.H + head] = lse_v;
@@ -666,8 +688,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if (b >= nhb) break;
-            const float lt = xsum[b][lane & 15];
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const float inv = xmul[b][lane & 15];
             const int head = head0 + 16 * b + (lane & 15);
             const int64_t pidx = (((int64_t)rloc * p.n_splits + split) * p.H + head) * kDv + vdim0 + 4 * g;
             if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
@@ -693,13 +714,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 
 // A11: merge the splits of each row in split order:  LSE = m + log sum_s e^(lse_s - m),
 // out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16, computed as an online merge over the
-// splits in order (the running max m and sum are updated split by split).  64 threads per
-// (row, head), 8 dims each.  Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
+// splits in order (the running max m and sum are updated split by split), and then the head's sink
+// logit, if any, as one more term with no output.  64 threads per (row, head), 8 dims each.
+// Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
 template <bool F32>
 __global__ __launch_bounds__(256) void split_combine_kernel(const void* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse, int S, int H,
-                                                            int row0, uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse) {
+                                                            int row0, const float* __restrict__ sink,
+                                                            uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int hq = H / 4;
     const int rloc = blockIdx.x / hq;
     const int head = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
@@ -748,6 +770,18 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const void* __restri
             for (int e = 0; e < 8; ++e) acc[e] += w * v[j][e];
         }
     }
+    // The sink, last: one more term e^sink in the denominator with no output (skipped at -inf).
+    const float snk = sink ? sink[head] : -INFINITY;
+    if (snk != -INFINITY) {
+        if (snk > m) {
+            const float c = m == -INFINITY ? 0.f : expf(m - snk);
+            tot *= c;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= c;
+            m = snk;
+        }
+        tot += expf(snk - m);
+    }
     float LSE = -INFINITY;
     if (tot > 0.f) {
         LSE = m + logf(tot);
@@ -784,6 +818,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.scale_log2 = a.softmax_scale * kLog2e;
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
+    p.sink = a.sink;
     const size_t per_row = attn_ws_bytes_per_row(a.H, a.k, a.kv_dtype);
     int rows_per_launch = a.rows;
     if (per_row > 0) {
@@ -808,10 +843,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         if (p.n_splits > 1) {
             if (fp8)
                 hipLaunchKernelGGL(split_combine_kernel<true>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
-                                   p.ws_lse, p.n_splits, a.H, row0, p.out, p.lse);
+                                   p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             else
                 hipLaunchKernelGGL(split_combine_kernel<false>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
-                                   p.ws_lse, p.n_splits, a.H, row0, p.out, p.lse);
+                                   p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -40,6 +40,7 @@ struct AttnArgs {
     int32_t H;
     int32_t k;
     float softmax_scale;
+    const float* sink;
     void* out;
     float* lse;
     void* ws;

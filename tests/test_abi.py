@@ -122,8 +122,8 @@ def _decode(lib, **kw):
     c = lambda v: None if v is None else _fake(v)
     return lib.smla_sparse_mla_decode(c(a["q"]), a["q_row_stride"], c(a["kv"]), a["kv_dtype"], a["num_pages"],
                                       c(a["bt"]), a["bt_stride"], a["num_reqs"], c(a["row_req"]), c(a["idx"]),
-                                      a["rows"], a["H"], a["k"], a["scale"], c(a["out"]), c(a["lse"]), c(a["ws"]),
-                                      a["ws_bytes"], None)
+                                      a["rows"], a["H"], a["k"], a["scale"], c(a.get("sink")), c(a["out"]),
+                                      c(a["lse"]), c(a["ws"]), a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -144,6 +144,7 @@ def _decode(lib, **kw):
     (dict(ws=None), 3, b"ws is NULL"),
     (dict(ws_bytes=100), 3, b"ws_bytes=100"),
     (dict(ws=0x60010), 4, b"ws must be 256-byte aligned"),
+    (dict(sink=0x70002), 4, b"sink must be 4-byte aligned"),
 ])
 def test_decode_validation(lib, kw, status, needle):
     st = _decode(lib, **kw)

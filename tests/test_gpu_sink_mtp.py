@@ -1,0 +1,132 @@
+"""GPU parity of the attention sink (a per-head logit in the softmax denominator with no value;
+-inf = none) on the one-split path (k <= 512, handled in the attention kernel) and the split path
+(handled by the combine), and of MTP-shaped batches: several consecutive query tokens per request,
+each with its own causal candidate count, mixed in one decode call."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as O
+import sparse_mla_attention_topk_amd as smla
+from sparse_mla_attention_topk_amd import workloads as W
+from tests.helpers import assert_attention_close, bf16_bits_np, bits_equal, kv_np, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def wl():
+    log("[sink] building tiny decode workload")
+    return W.tiny_decode(DEV)
+
+
+def _sinks(H, seed, with_neg_inf=True):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = torch.randn(H, generator=g) * 3.0 + 2.0
+    if with_neg_inf:
+        s[1::5] = -float("inf")
+    return s.to(DEV)
+
+
+def _decode(wl, rs, k, sink, idx=None, q=None, row_req=None):
+    idx = smla.topk_per_row(rs.scores, k, lengths=rs.lengths) if idx is None else idx
+    q = rs.q if q is None else q
+    lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_decode(q, wl.cache.kv, wl.cache.block_table, idx, wl.scale,
+                                    row_req=rs.row_req if row_req is None else row_req, lse=lse, sink=sink,
+                                    kv_dtype=wl.cache.kv_dtype)
+    torch.cuda.synchronize()
+    return idx, out, lse
+
+
+@pytest.mark.parametrize("k", [100, 512, 2048])
+def test_sink_parity(wl, k):
+    rs = wl.sets[0]
+    H = rs.q.shape[1]
+    sink = _sinks(H, k)
+    idx, out, lse = _decode(wl, rs, k, sink)
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(rs.q), kv_np(wl.cache.kv), wl.cache.kv_dtype,
+                                      wl.cache.block_table.cpu().numpy(), rs.row_req.cpu().numpy(),
+                                      idx.cpu().numpy(), wl.scale, sink=sink.cpu().numpy().astype(np.float64))
+    st = assert_attention_close(out, lse, O_ref, lse_ref, f"sink k={k}")
+    log(f"[sink] k={k} {st}")
+
+
+@pytest.mark.parametrize("k", [256, 1024])
+def test_minus_inf_sink_is_bitwise_no_sink(wl, k):
+    rs = wl.sets[0]
+    H = rs.q.shape[1]
+    _, o0, l0 = _decode(wl, rs, k, None)
+    _, o1, l1 = _decode(wl, rs, k, torch.full((H,), -float("inf"), device=DEV))
+    assert bits_equal(o0, o1) and bits_equal(l0, l1)
+
+
+@pytest.mark.parametrize("k", [64, 1024])
+def test_sink_with_no_valid_token(wl, k):
+    rs = wl.sets[0]
+    H = rs.q.shape[1]
+    sink = _sinks(H, 7)
+    idx = torch.full((rs.q.shape[0], k), -1, dtype=torch.int32, device=DEV)
+    _, out, lse = _decode(wl, rs, k, sink, idx=idx)
+    assert (out.float() == 0).all()
+    exp = sink.cpu().numpy()
+    got = lse.cpu().numpy()
+    for r in range(got.shape[0]):
+        np.testing.assert_array_equal(got[r], exp)
+
+
+def test_sink_row_alone_equals_in_batch(wl):
+    rs = wl.sets[0]
+    H = rs.q.shape[1]
+    sink = _sinks(H, 3)
+    idx, out, lse = _decode(wl, rs, 2048, sink)
+    _, o1, l1 = _decode(wl, rs, 2048, sink, idx=idx[1:2].contiguous(), q=rs.q[1:2].contiguous(),
+                        row_req=rs.row_req[1:2].contiguous())
+    assert bits_equal(o1[0], out[1]) and bits_equal(l1[0], lse[1])
+
+
+def test_sink_fp8_cache():
+    wl8 = W.decode_workload("tiny_fp8", B=3, H=32, k=1024, ctx_lo=1500, ctx_hi=4000, kv_dtype=W.KV_FP8, seed=12, device=DEV)
+    rs = wl8.sets[0]
+    sink = _sinks(32, 12)
+    idx, out, lse = _decode(wl8, rs, 1024, sink)
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(rs.q), kv_np(wl8.cache.kv), W.KV_FP8,
+                                      wl8.cache.block_table.cpu().numpy(), rs.row_req.cpu().numpy(),
+                                      idx.cpu().numpy(), wl8.scale, sink=sink.cpu().numpy().astype(np.float64))
+    assert_attention_close(out, lse, O_ref, lse_ref, "fp8 sink", relative=True)
+
+
+def test_mtp_rows():
+    """Requests with next_n = 4 query tokens each (one target + three draft tokens): token t of a
+    request of context c sees positions 0 .. c - 4 + t, i.e. causal lengths from smla_fill_causal_lengths.
+    All rows go through one top-k and one decode call, then match the oracle and their single-row runs."""
+    next_n, nreq, H, k = 4, 5, 64, 512
+    g = torch.Generator(device=DEV).manual_seed(41)
+    ctx = W.uniform_int(600, 3000, nreq, g, DEV)
+    cache = W.make_paged_cache(ctx, W.KV_BF16, g, DEV)
+    rows = next_n * nreq
+    row_req = torch.arange(nreq, dtype=torch.int32, device=DEV).repeat_interleave(next_n)
+    lengths = torch.cat([smla.fill_causal_lengths(int(c) - next_n, next_n, device=DEV) for c in ctx.tolist()])
+    stride = int(ctx.max())
+    scores = torch.randn((rows, stride), generator=g, device=DEV)
+    q = torch.randn((rows, H, 576), generator=g, device=DEV).to(torch.bfloat16)
+    idx = smla.topk_per_row(scores, k, lengths=lengths)
+    lse = torch.empty((rows, H), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_decode(q, cache.kv, cache.block_table, idx, 1 / 24, row_req=row_req, lse=lse)
+    torch.cuda.synchronize()
+    ref_idx, O_ref, lse_ref = O.decode_rows(bf16_bits_np(q), kv_np(cache.kv), W.KV_BF16,
+                                            cache.block_table.cpu().numpy(), row_req.cpu().numpy(),
+                                            scores.cpu().numpy(), lengths.cpu().numpy(), k, 1 / 24)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert_attention_close(out, lse, O_ref, lse_ref, "mtp rows")
+    # the draft rows of a request see one more position each
+    ln = lengths.cpu().numpy().reshape(nreq, next_n)
+    assert (np.diff(ln, axis=1) == 1).all() and (ln[:, -1] == ctx.cpu().numpy()).all()
+    for r in [0, 7, rows - 1]:
+        lse1 = torch.empty((1, H), dtype=torch.float32, device=DEV)
+        o1, _ = smla.sparse_mla_decode(q[r:r + 1].contiguous(), cache.kv, cache.block_table, idx[r:r + 1].contiguous(),
+                                       1 / 24, row_req=row_req[r:r + 1].contiguous(), lse=lse1)
+        torch.cuda.synchronize()
+        assert bits_equal(o1[0], out[r]) and bits_equal(lse1[0], lse[r]), r
