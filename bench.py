@@ -33,10 +33,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8"],
+    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8", "decode_swa192"],
                     help="decode_bf16: B=64, contexts U[8192, 65536], bf16 KV (the headline); "
                          "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV; "
-                         "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step)")
+                         "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step); "
+                         "decode_swa192: B=64 draft rows over 128 sliding-window + 5 draft positions, index "
+                         "width 192 (and the same rows at width 256)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     return ap.parse_args()
@@ -167,6 +169,56 @@ def bench_kv_write(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_swa(args):
+    """Attention over sliding-window + draft index rows: B = 64 rows, H = 64, each row 133 valid
+    positions (128 window + 5 draft) padded with -1 to width 192, and the same rows padded to 256.
+    Four rotating (Q, indices) sets over one bf16 KV pool of contexts U[8192, 65536]."""
+    import torch
+
+    import sparse_mla_attention_topk_amd as smla
+    from sparse_mla_attention_topk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H = 64, 64
+    wl = W.decode_bf16(dev, n_sets=N_SETS)
+    ctx = wl.cache.ctx_lens.to(dev)
+    idx192 = W.swa_draft_indices(ctx)
+    idx256 = torch.full((B, 256), -1, dtype=torch.int32, device=dev)
+    idx256[:, :192] = idx192
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream(dev)
+
+    def call(idx):
+        return lambda i: smla.sparse_mla_decode(wl.sets[i % N_SETS].q, wl.cache.kv, wl.cache.block_table, idx,
+                                                wl.scale, row_req=wl.sets[i % N_SETS].row_req, out=out, lse=lse)
+    for i in range(N_SETS):
+        call(idx192)(i)
+        call(idx256)(i)
+    torch.cuda.synchronize()
+    ms192 = _graph_time(torch, s, call(idx192), args.steps, args.warmup)
+    ms256 = _graph_time(torch, s, call(idx256), args.steps, args.warmup)
+    valid = int((idx192 >= 0).sum())
+    gathered = valid * W.BF16_RECORD_BYTES
+    achieved = gathered / (ms192 * 1e-3) / 1e9
+    line = {
+        "metric": "sparse-MLA decode rows/s, sliding-window + draft rows (128 + 5 valid, index width 192, H=64, 1 GPU)",
+        "value": B / (ms192 * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms192, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_swa192_B64_H64", "rows": B, "heads": H, "index_width": 192,
+                   "valid_per_row": 133, "rotating_sets": N_SETS, "launch": "hip_graph_of_K_calls"},
+        "attention_us_width192": ms192 * 1e3, "attention_us_width256": ms256 * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "sparse_mla_decode call (one split: attention kernel only)",
+                     "algorithmic_bytes_per_launch": gathered},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -175,6 +227,8 @@ def main():
         sys.exit(2)
     if args.workload == "kv_write_fp8":
         return bench_kv_write(args)
+    if args.workload == "decode_swa192":
+        return bench_swa(args)
     import torch
 
     import sparse_mla_attention_topk_amd as smla

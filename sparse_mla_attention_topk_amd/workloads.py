@@ -296,3 +296,17 @@ def cache_write_tokens(device, T: int, num_pages: int, seed: int = 5, spread: fl
         raise ValueError("more tokens than slots")
     slots = torch.randperm(nslots, generator=g, device=device)[:T] + PAGE
     return CacheWriteWorkload(tokens=tokens, slots=slots.to(torch.int64), num_pages=num_pages)
+
+
+def swa_draft_indices(ctx_lens: torch.Tensor, window: int = 128, draft: int = 5, width: int = 192) -> torch.Tensor:
+    """Index rows of a draft batch over sliding-window KV: a request whose context holds c positions
+    (the last ``draft`` of them draft tokens) attends to its last ``window`` committed positions and to
+    all ``draft`` draft positions, i.e. positions max(0, c - draft - window) .. c - 1 in ascending order,
+    padded with -1 to ``width`` (a multiple of the 64-entry tile: 192 for 128 + 5)."""
+    rows = ctx_lens.numel()
+    out = torch.full((rows, width), -1, dtype=torch.int32)
+    for r, c in enumerate(ctx_lens.tolist()):
+        lo = max(0, int(c) - draft - window)
+        n = int(c) - lo
+        out[r, :n] = torch.arange(lo, int(c), dtype=torch.int32)
+    return out.to(ctx_lens.device)

@@ -130,3 +130,30 @@ def test_mtp_rows():
                                        1 / 24, row_req=row_req[r:r + 1].contiguous(), lse=lse1)
         torch.cuda.synchronize()
         assert bits_equal(o1[0], out[r]) and bits_equal(lse1[0], lse[r]), r
+
+
+def test_sliding_window_draft_rows_width_192():
+    """Sliding-window + draft index rows (128 window + 5 draft positions, -1 padded to 192, a multiple
+    of the 64-entry tile) against the oracle; the same rows padded to 256 give bit-identical results
+    (trailing -1 tiles are not visited, so the reduction is the same)."""
+    H, B = 64, 12
+    g = torch.Generator(device=DEV).manual_seed(51)
+    ctx = W.uniform_int(100, 5000, B, g, DEV)
+    ctx[0] = 60                                                        # shorter than the window
+    cache = W.make_paged_cache(ctx, W.KV_BF16, g, DEV)
+    row_req = torch.arange(B, dtype=torch.int32, device=DEV)
+    q = torch.randn((B, H, 576), generator=g, device=DEV).to(torch.bfloat16)
+    idx = W.swa_draft_indices(ctx)
+    assert idx.shape == (B, 192)
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_decode(q, cache.kv, cache.block_table, idx, 1 / 24, row_req=row_req, lse=lse)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(q), kv_np(cache.kv), W.KV_BF16, cache.block_table.cpu().numpy(),
+                                      row_req.cpu().numpy(), idx.cpu().numpy(), 1 / 24)
+    assert_attention_close(out, lse, O_ref, lse_ref, "swa+draft k=192")
+    idx256 = torch.full((B, 256), -1, dtype=torch.int32, device=DEV)
+    idx256[:, :192] = idx
+    lse2 = torch.empty_like(lse)
+    out2, _ = smla.sparse_mla_decode(q, cache.kv, cache.block_table, idx256, 1 / 24, row_req=row_req, lse=lse2)
+    torch.cuda.synchronize()
+    assert bits_equal(out, out2) and bits_equal(lse, lse2)
