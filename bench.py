@@ -33,12 +33,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8", "decode_swa192"],
+    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8", "decode_swa192", "prefill_c4"],
                     help="decode_bf16: B=64, contexts U[8192, 65536], bf16 KV (the headline); "
                          "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV; "
                          "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step); "
                          "decode_swa192: B=64 draft rows over 128 sliding-window + 5 draft positions, index "
-                         "width 192 (and the same rows at width 256)")
+                         "width 192 (and the same rows at width 256); "
+                         "prefill_c4: one request, T=4096 query tokens at positions 126976..131071 of a "
+                         "131072-token context, causal top-k 2048 + prefill attention")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     return ap.parse_args()
@@ -219,6 +221,63 @@ def bench_swa(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_prefill(args):
+    """Prefill chunk: T = 4096 causal query rows of one 131072-token bf16 context (2 GiB of scores),
+    top-k 2048 per row, then sparse_mla_prefill_chunk.  The context's 151 MB of KV is read 4096 x 2048
+    times (9.66 GB algorithmic), so the attention is bound by MFMA and the L2/MALL, not HBM."""
+    import torch
+
+    import sparse_mla_attention_topk_amd as smla
+    from sparse_mla_attention_topk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.prefill_chunk(dev)
+    T, H, k = wl.q.shape[0], wl.H, wl.k
+    lengths = smla.fill_causal_lengths(wl.first_pos, T, device=dev)
+    bt = wl.cache.block_table[0].contiguous()
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = smla.attention_workspace(T, H, k, dev)
+    tws = smla.topk_workspace(T, k, wl.scores.shape[1], dev)
+
+    def topk(i):
+        smla.topk_per_row(wl.scores, k, lengths=lengths, out=idx, workspace=tws)
+
+    def attn(i):
+        smla.sparse_mla_prefill_chunk(wl.q, wl.cache.kv, bt, idx, wl.scale, out=out, lse=lse, workspace=ws)
+
+    def step(i):
+        topk(i)
+        attn(i)
+    step(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(dev)
+    n, w = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    step_ms = _graph_time(torch, s, step, n, w)
+    attn_ms = _graph_time(torch, s, attn, n, w)
+    topk_ms = _graph_time(torch, s, topk, n, w)
+    flops = T * H * k * (576 + 512) * 2
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    gathered = T * k * W.BF16_RECORD_BYTES
+    line = {
+        "metric": "sparse-MLA prefill-chunk rows/s (T=4096 causal rows, 131072-token context, H=64, topk=2048, 1 GPU)",
+        "value": T / (step_ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": n, "warmup": w,
+        "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "rows": T, "heads": H, "topk": k, "context": 131072,
+                   "first_pos": wl.first_pos, "launch": "hip_graph_of_K_steps"},
+        "attention_ms": attn_ms, "topk_ms": topk_ms,
+        "attention_effective_GBps": gathered / (attn_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0,
+                     "traffic": None, "kernel": "sparse_mla_prefill_chunk call: attention kernel + split-combine kernel",
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -229,6 +288,8 @@ def main():
         return bench_kv_write(args)
     if args.workload == "decode_swa192":
         return bench_swa(args)
+    if args.workload == "prefill_c4":
+        return bench_prefill(args)
     import torch
 
     import sparse_mla_attention_topk_amd as smla
