@@ -141,20 +141,12 @@ __device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi) {
     return r.u;
 }
 
-// Two bf16 values holding small integers times powers of two (e4m3 codes) -> the same two values in
-// fp16 (exact: every e4m3 value is an fp16 value, so the truncating conversion does not round).
-__device__ __forceinline__ uint32_t bf16x2_code_to_f16x2(uint32_t w) {
-    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.f, 0.f)) v; uint32_t u; } r;
-    r.v = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-    return r.u;
-}
-
-// Two e4m3 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values.  The scaled conversion with
-// scale 1.0 is exact: every e4m3 value is a bf16 value.
+// Two e4m3 codes (bytes 0-1, or 2-3 when HI, of w) -> two fp16 values.  The scaled conversion with
+// scale 1.0 is exact: every e4m3 value is an fp16 value.
 template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    union { decltype(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(0, 1.f, false)) v; uint32_t u; } r;
-    r.v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, HI);
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+    union { decltype(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(0, 1.f, false)) v; uint32_t u; } r;
+    r.v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.f, HI);
     return r.u;
 }
 
@@ -162,14 +154,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
 
-// KV_FP8: the ring holds FP8 records, and every tile is first expanded into one bf16 tile with the
-// layout of the bf16 path: the e4m3 codes exactly (every e4m3 value is a bf16 value), the rope copied,
-// and the four fp32 group scales of each token into a small table.  The scales are applied in fp32:
-// the score waves keep one partial per 128-dim scale group and sum scale x partial; the softmax
+// KV_FP8: the ring holds FP8 records, and every tile is first expanded into a tile with the layout of
+// the bf16 path: the 512 e4m3 codes as fp16 (exact: every e4m3 value is an fp16 value), the bf16 rope
+// copied, and the four fp32 group scales of each token into a small table.  The latent part of the
+// scores is an fp16 product: each score wave holds its latent Q slice in fp16, divided per head by a
+// power of two 2^e that keeps it inside the fp16 range (e = 0 unless |q| reaches 2^15, so the
+// conversion from bf16 is exact); the rope part stays bf16.  The scales are applied in fp32: the
+// score waves keep one partial per 128-dim scale group and sum 2^e x scale x partial; the softmax
 // publishes the fp32 weights, and a value wave, whose 64 dims lie in one group, multiplies them by
-// that group's scales, rounds to fp16 and runs the value product in fp16 (the codes are exact in fp16
-// too).  At the magnitudes these scales produce, rounding the scaled
-// values, or the scaled weights, to bf16 costs far more accuracy than the fp16 weights.
+// that group's scales, rounds to fp16 and runs the value product in fp16 on the codes as they are.
+// At the magnitudes these scales produce, rounding the scaled values, or the scaled weights, to bf16
+// costs far more accuracy than the fp16 weights.
 template <bool KV_FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
     // FP8: the ring of FP8 stages, then two bf16 tiles (tile it is read while tile it+1 is expanded)
@@ -260,6 +255,43 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // vector-memory operations are the tile loads, which the loop waits for explicitly.
     wait_vmcnt<0>();
     __syncthreads();
+    // FP8: the latent steps of the Q slice in fp16, divided by 2^e for the head (lane & 15); the rope
+    // steps (the last two of the second half) stay bf16.
+    float qscale = 1.f;
+    if constexpr (KV_FP8) {
+        if (score_ok) {
+            const int nlat = half ? 7 : 9;
+            float mx = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 9; ++kk) {
+                if (kk < nlat) {
+                    union { bf16x8_t v; uint32_t w[4]; } q;
+                    q.v = qv[kk];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(q.w[e] << 16)),
+                                             fabsf(__uint_as_float(q.w[e] & 0xffff0000u))));
+                }
+            }
+            mx = head_max(mx);
+            const int ex = (int)((__float_as_uint(mx) >> 23) & 0xffu) - 127;
+            const int e2 = ex > 14 ? ex - 14 : 0;
+            qscale = __uint_as_float((uint32_t)(127 + e2) << 23);
+            const float inv = __uint_as_float((uint32_t)(127 - e2) << 23);
+#pragma unroll
+            for (int kk = 0; kk < 9; ++kk) {
+                if (kk < nlat) {
+                    union { bf16x8_t v; uint32_t w[4]; } q;
+                    q.v = qv[kk];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        q.w[e] = pack_f16x2_rne(__uint_as_float(q.w[e] << 16) * inv,
+                                                __uint_as_float(q.w[e] & 0xffff0000u) * inv);
+                    qv[kk] = q.v;
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int kk = 0; kk < 9; ++kk) asm volatile("" : "+v"(qv[kk]));   // opaque: Q is never re-loaded
     const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
@@ -351,14 +383,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
             if ((c & 7) == 0) tscale[tile & 1][t][c >> 3] = keep ? *(const float*)(st + t * kFp8Record + 512 + 4 * (c >> 3)) : 0.f;
             uint8_t* dst = btile + t * kBf16Record;
-            // codes 0..7 of the chunk -> bf16 chunk 2c, codes 8..15 -> bf16 chunk 2c+1; the conversion
-            // with scale 1.0 is exact (checked on the hardware for all 256 codes)
+            // codes 0..7 of the chunk -> fp16 chunk 2c, codes 8..15 -> fp16 chunk 2c+1; the conversion
+            // with scale 1.0 is exact
             *(uint4*)(dst + 16 * ((2 * c) ^ f)) =
-                make_uint4(fp8x2_to_bf16x2<false>(codes.x) & keep, fp8x2_to_bf16x2<true>(codes.x) & keep,
-                           fp8x2_to_bf16x2<false>(codes.y) & keep, fp8x2_to_bf16x2<true>(codes.y) & keep);
+                make_uint4(fp8x2_to_f16x2<false>(codes.x) & keep, fp8x2_to_f16x2<true>(codes.x) & keep,
+                           fp8x2_to_f16x2<false>(codes.y) & keep, fp8x2_to_f16x2<true>(codes.y) & keep);
             *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
-                make_uint4(fp8x2_to_bf16x2<false>(codes.z) & keep, fp8x2_to_bf16x2<true>(codes.z) & keep,
-                           fp8x2_to_bf16x2<false>(codes.w) & keep, fp8x2_to_bf16x2<true>(codes.w) & keep);
+                make_uint4(fp8x2_to_f16x2<false>(codes.z) & keep, fp8x2_to_f16x2<true>(codes.z) & keep,
+                           fp8x2_to_f16x2<false>(codes.w) & keep, fp8x2_to_f16x2<true>(codes.w) & keep);
         }
         if (u < kTileTok * 8) {
             const int rt = u >> 3, j = u & 7;
@@ -464,34 +496,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     f32x4_t acc[3][2];
 #pragma unroll
                     for (int j = 0; j < 3; ++j) acc[j][0] = acc[j][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    auto step = [&](int kk, int slot) {
+                    auto step = [&](int kk, int slot, bool rope) {
                         const int kg = 9 * half + kk;
                         const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
-                        const bf16x8_t a0 = *(const bf16x8_t*)(ap);
-                        const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
-                        acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], acc[slot][0], 0, 0, 0);
-                        acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], acc[slot][1], 0, 0, 0);
+                        union { bf16x8_t b; f16x8_t h; } a0, a1, qq;
+                        a0.b = *(const bf16x8_t*)(ap);
+                        a1.b = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                        qq.b = qv[kk];
+                        if (rope) {   // bf16 rope x bf16 Q
+                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.b, qq.b, acc[slot][0], 0, 0, 0);
+                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.b, qq.b, acc[slot][1], 0, 0, 0);
+                        } else {      // fp16 codes x fp16 Q
+                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qq.h, acc[slot][0], 0, 0, 0);
+                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qq.h, acc[slot][1], 0, 0, 0);
+                        }
                     };
                     if (!half) {
 #pragma unroll
-                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2));
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2), false);
                     } else {
 #pragma unroll
-                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 3 ? 0 : (kk < 7 ? 1 : 2));
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 3 ? 0 : (kk < 7 ? 1 : 2), kk >= 7);
                     }
-                    // lane: tokens 4g + i (block 0) and 16 + 4g + i (block 1); scale slots per half
-                    const int gs0 = half ? 2 : 0;
+                    // lane: tokens 4g + i (block 0) and 16 + 4g + i (block 1); scale slots per half; the
+                    // latent partials carry the Q factor 2^e, the rope partial (second half) does not
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const f32x4_t ta = *(const f32x4_t*)tscale[it & 1][4 * g + i];
                         const f32x4_t tb = *(const f32x4_t*)tscale[it & 1][16 + 4 * g + i];
-                        const float a0s = half ? ta[2] : ta[0], a1s = half ? ta[3] : ta[1];
-                        const float b0s = half ? tb[2] : tb[0], b1s = half ? tb[3] : tb[1];
-                        const float a2s = half ? 1.f : ta[2], b2s = half ? 1.f : tb[2];
+                        const float a0s = (half ? ta[2] : ta[0]) * qscale, a1s = (half ? ta[3] : ta[1]) * qscale;
+                        const float b0s = (half ? tb[2] : tb[0]) * qscale, b1s = (half ? tb[3] : tb[1]) * qscale;
+                        const float a2s = half ? 1.f : ta[2] * qscale, b2s = half ? 1.f : tb[2] * qscale;
                         s0[i] = a0s * acc[0][0][i] + a1s * acc[1][0][i] + a2s * acc[2][0][i];
                         s1[i] = b0s * acc[0][1][i] + b1s * acc[1][1][i] + b2s * acc[2][1][i];
                     }
-                    (void)gs0;
                 }
                 if (half) {
                     xs(shb, 0)[lane] = s0;
@@ -655,9 +693,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                         pv.u = pb[b];
                         oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pv.v, oacc[b][d], 0, 0, 0);
                     }
-                } else {
-                    va.u = make_uint4(bf16x2_code_to_f16x2(va.u.x), bf16x2_code_to_f16x2(va.u.y),
-                                      bf16x2_code_to_f16x2(va.u.z), bf16x2_code_to_f16x2(va.u.w));
+                } else {   // the tile holds the codes as fp16
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         union { uint4 u; f16x8_t v; } pv;

@@ -107,3 +107,23 @@ def test_fp8_edge_slots_and_poison():
     assert (out[0].float() == 0).all() and torch.isneginf(lse[0]).all()
     assert (out[5].float() == 0).all() and torch.isneginf(lse[5]).all()
     log(f"[fp8] edge {st}")
+
+
+def test_fp8_q_beyond_fp16_range():
+    """Q entries far above the fp16 range (2^17, -2^20) in latent dims whose codes are zero in every
+    record: the fp16 latent Q slice must be rescaled per head (an unscaled conversion would give inf,
+    and inf x 0 = NaN), and the result must match the oracle."""
+    wl = W.decode_workload("fp8_bigq", B=4, H=32, k=700, ctx_lo=900, ctx_hi=3000, kv_dtype=W.KV_FP8, seed=321,
+                           device=DEV)
+    rs = wl.sets[0]
+    kv = wl.cache.kv
+    kv[:, :, 5] = 0                     # code of latent dim 5 (scale group 0, first half of the dims)
+    kv[:, :, 300] = 0                   # latent dim 300 (group 2, second half)
+    q = rs.q.clone()
+    q[:, ::2, 5] = 2.0 ** 17
+    q[:, 1::3, 300] = -(2.0 ** 20)
+    idx, out, lse = _run(wl, rs, q=q)
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(q), kv_np(kv), W.KV_FP8, wl.cache.block_table.cpu().numpy(),
+                                      rs.row_req.cpu().numpy(), idx.cpu().numpy(), wl.scale)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, "fp8 large q", relative=True)
+    log(f"[fp8] large q {st}")
