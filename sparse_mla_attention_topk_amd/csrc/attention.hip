@@ -87,6 +87,7 @@ struct AttnParams {
     int32_t H;
     int32_t n_splits;
     int32_t n_hblocks;
+    int32_t heads_per_wg;   // 64, 32 or 16: heads of one workgroup (each head's arithmetic is the same)
     float scale_log2;
     int32_t row0;
     uint16_t* out;
@@ -203,8 +204,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     const int split = rs % p.n_splits;
     const int rloc = rs / p.n_splits;
     const int64_t row = (int64_t)p.row0 + rloc;
-    const int head0 = hb_item * kHeadsPerBlock;
-    const int nhb = min(4, (p.H - head0) / 16);   // valid 16-head blocks of this item (H % 16 == 0)
+    const int head0 = hb_item * p.heads_per_wg;
+    const int nhb = min(p.heads_per_wg / 16, (p.H - head0) / 16);   // valid 16-head blocks (H % 16 == 0)
 
     const bool is_score = wid < kScoreWaves;
     const int shb = wid & 3, half = (wid >> 2) & 1;   // score waves: head block, dim half
@@ -850,7 +851,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.k = a.k;
     p.H = a.H;
     p.n_splits = attn_num_splits(a.k);
-    p.n_hblocks = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    // Launches with fewer (row, split) items than CUs split the heads over 2 or 4 workgroups (each of
+    // which gathers the same records): a head's arithmetic does not depend on the heads it shares a
+    // workgroup with, so the results are the same bits either way.
+    int dev = 0, num_cu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
     p.scale_log2 = a.softmax_scale * kLog2e;
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
@@ -871,6 +876,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch *
                                                                attn_ws_o_bytes_per_row(a.H, a.k, a.kv_dtype))
                                : nullptr;
+        p.heads_per_wg = kHeadsPerBlock;
+        while (p.heads_per_wg > 16 && (int64_t)n * p.n_splits * ((a.H + p.heads_per_wg - 1) / p.heads_per_wg) < num_cu)
+            p.heads_per_wg /= 2;
+        p.n_hblocks = (a.H + p.heads_per_wg - 1) / p.heads_per_wg;
         const int grid = n * p.n_splits * p.n_hblocks;
         if (fp8) hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         else hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream, p);

@@ -139,3 +139,23 @@ def test_poisoned_pages_never_read():
     rs = wl.sets[0]
     _, out, lse = _run(wl, rs)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_head_split_invariance(big):
+    """Launches with few (row, split) items split the heads over 2 or 4 workgroups; a head's result must
+    not depend on that.  k = 256 (one split): 320 rows run 64 heads per workgroup, 128 rows 32, 64 rows
+    and a single row 16 -- the shared rows must agree bit for bit."""
+    wl, _ = big
+    rs = wl.sets[0]
+    k = 256
+    idx = smla.topk_per_row(rs.scores, k, lengths=rs.lengths)
+    rep = lambda t, n: t.repeat((n,) + (1,) * (t.dim() - 1))[: 64 * n].contiguous()
+    outs = {}
+    for n_rep in (5, 2, 1):
+        _, o, l = _run(wl, rs, idx=rep(idx, n_rep), row_req=rep(rs.row_req, n_rep), q=rep(rs.q, n_rep))
+        outs[n_rep] = (o[:64], l[:64])
+    for n_rep in (2, 1):
+        assert bits_equal(outs[n_rep][0], outs[5][0]) and bits_equal(outs[n_rep][1], outs[5][1]), n_rep
+    _, o1, l1 = _run(wl, rs, idx=idx[9:10].contiguous(), row_req=rs.row_req[9:10].contiguous(),
+                     q=rs.q[9:10].contiguous())
+    assert bits_equal(o1[0], outs[5][0][9]) and bits_equal(l1[0], outs[5][1][9])
