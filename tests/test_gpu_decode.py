@@ -159,3 +159,35 @@ def test_head_split_invariance(big):
     _, o1, l1 = _run(wl, rs, idx=idx[9:10].contiguous(), row_req=rs.row_req[9:10].contiguous(),
                      q=rs.q[9:10].contiguous())
     assert bits_equal(o1[0], outs[5][0][9]) and bits_equal(l1[0], outs[5][1][9])
+
+
+def test_maximum_k_and_many_splits():
+    """k = 16384, the largest supported width: 32 splits, combined in order by the split-combine kernel
+    in several groups of loads."""
+    k = 16384
+    wl = W.decode_workload("maxk", B=3, H=16, k=k, ctx_lo=k, ctx_hi=k + 3000, kv_dtype=W.KV_BF16, seed=88,
+                           device=DEV)
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, [0, 1, 2])
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, "k=16384")
+    log(f"[decode] k=16384 {st}")
+
+
+def test_workspace_smaller_than_the_batch():
+    """A workspace that holds 2 rows: the call runs 4 launches of at most 2 rows; every row must equal
+    its value from one launch with a workspace for all 7 rows."""
+    wl = W.decode_workload("ws", B=7, H=64, k=1500, ctx_lo=1600, ctx_hi=5000, kv_dtype=W.KV_BF16, seed=99,
+                           device=DEV)
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    _, per_row = smla.workspace_size(smla.Capacity.make(1, 1500, 64, 1))
+    small = torch.zeros(2 * per_row, dtype=torch.uint8, device=DEV)
+    lse2 = torch.empty_like(lse)
+    out2, _ = smla.sparse_mla_decode(rs.q, wl.cache.kv, wl.cache.block_table, idx, wl.scale, row_req=rs.row_req,
+                                     lse=lse2, workspace=small)
+    torch.cuda.synchronize()
+    assert bits_equal(out, out2) and bits_equal(lse, lse2)
+    ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, list(range(7)))
+    assert_attention_close(out2, lse2, O_ref, lse_ref, "small workspace")
