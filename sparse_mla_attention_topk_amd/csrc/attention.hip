@@ -754,14 +754,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 // splits in order (the running max m and sum are updated split by split), and then the head's sink
 // logit, if any, as one more term with no output.  64 threads per (row, head), 8 dims each.
 // Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
+constexpr int kCombineHeads = 16;   // heads per combine workgroup (64 threads each)
+
 template <bool F32>
-__global__ __launch_bounds__(256) void split_combine_kernel(const void* __restrict__ ws_o,
+__global__ __launch_bounds__(64 * kCombineHeads) void split_combine_kernel(const void* __restrict__ ws_o,
                                                             const float* __restrict__ ws_lse, int S, int H,
                                                             int row0, const float* __restrict__ sink,
                                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int hq = H / 4;
+    const int hq = H / kCombineHeads;
     const int rloc = blockIdx.x / hq;
-    const int head = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
+    const int head = (blockIdx.x % hq) * kCombineHeads + (threadIdx.x >> 6);
     const int d = 8 * (threadIdx.x & 63);
     const float* ls = ws_lse + (int64_t)rloc * S * H + head;
     constexpr int kGroup = 4;   // splits whose loads are in flight together
@@ -887,10 +889,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         if (p.n_splits > 1) {
             if (fp8)
-                hipLaunchKernelGGL(split_combine_kernel<true>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
+                hipLaunchKernelGGL(split_combine_kernel<true>, dim3(n * (a.H / kCombineHeads)), dim3(64 * kCombineHeads), 0,
+                                   stream, p.ws_o,
                                    p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             else
-                hipLaunchKernelGGL(split_combine_kernel<false>, dim3(n * (a.H / 4)), dim3(256), 0, stream, p.ws_o,
+                hipLaunchKernelGGL(split_combine_kernel<false>, dim3(n * (a.H / kCombineHeads)), dim3(64 * kCombineHeads), 0,
+                                   stream, p.ws_o,
                                    p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
