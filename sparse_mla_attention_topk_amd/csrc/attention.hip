@@ -168,7 +168,7 @@ constexpr float kRescaleSlack = 8.f;
 // costs far more accuracy than the fp16 weights.
 template <bool KV_FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
-    // FP8: the ring of FP8 stages, then two bf16 tiles (tile it is read while tile it+1 is expanded)
+    // FP8: the ring of FP8 stages, then two expanded tiles (tile it is read while tile it+1 is expanded)
     constexpr int kStages = 3;   // ring depth: tiles are loaded two tiles ahead
     constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + 2 * kStageBytes : kStages * kStageBytes;
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
     // Second-half partial scores of each head block.
     __shared__ __attribute__((aligned(16))) f32x4_t xs_own[4][2][kWave];
-    // FP8: scales of the tile's tokens, one table per bf16 tile (the value waves read tile it's while
+    // FP8: scales of the tile's tokens, one table per expanded tile (the value waves read tile it's while
     // tile it+1 is expanded)
     __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
@@ -364,8 +364,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             }
         }
     };
-    // FP8 (A6): expand the stage's records into the bf16 tile, one unit per thread: thread u converts
-    // codes 16c .. 16c+15 of token t = u / 32 (c = u % 32) into bf16 chunks 2c, 2c+1 and, for
+    // FP8 (A6): expand the stage's records into an expanded tile, one unit per thread: thread u converts
+    // codes 16c .. 16c+15 of token t = u / 32 (c = u % 32) into fp16 chunks 2c, 2c+1 and, for
     // c % 8 == 0, stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.
     // Invalid tokens become zeros (codes, rope and scales).
     auto btile_of = [&](int tile) { return ring + kStages * kFp8StageBytes + (tile & 1) * kStageBytes; };
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // Start of tile `it`, common to both roles.
     // bf16: wait for this wave's loads of the tile, zero its invalid chunks and make the tile visible
     //   (first barrier); tile it+1 stays in flight.
-    // FP8: the tile was expanded into bf16 tile it % 2 after the third barrier of tile it-1 (or
+    // FP8: the tile was expanded into expansion buffer it % 2 after the third barrier of tile it-1 (or
     //   before the loop); the first barrier makes it visible, then the load of tile it+2 starts.
     //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
     //   the score waves expand tile it+1.
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         };
         // The value product of tile it runs after the first barrier of tile it+1, beside the scores of
         // tile it+1: its weights and rescale factors are rewritten only after the second barrier of
-        // tile it+1, its bf16 tile (the ring stage, or the FP8 expansion buffer) only after that too.
+        // tile it+1, its 1152-byte tile (the ring stage, or the FP8 expansion buffer) only after that too.
         const uint8_t* sb_prev = nullptr;
         for (int it = 0; it < ntiles; ++it) {
             const uint8_t* sb = tile_top(it);
