@@ -88,6 +88,7 @@ struct AttnParams {
     int32_t n_splits;
     int32_t n_hblocks;
     int32_t heads_per_wg;   // 64, 32 or 16: heads of one workgroup (each head's arithmetic is the same)
+    int32_t splits_per_wg;  // 1, 2 or 4 consecutive splits of a row run by one workgroup, one after the other
     float scale_log2;
     int32_t row0;
     uint16_t* out;
@@ -174,8 +175,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
     constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
-    __shared__ uint32_t phys[kSplitSlots];
-    __shared__ uint32_t tile_valid[kTilesPerSplit];
+    // Splits run by one workgroup (FP8: at most 2, for LDS) and their slots' physical records.
+    constexpr int kMaxGroup = KV_FP8 ? 2 : 4;
+    __shared__ uint32_t phys[kMaxGroup * kSplitSlots];
+    __shared__ uint32_t tile_valid[kMaxGroup * kTilesPerSplit];
     // Weights of each head block: bf16 B-operand fragments (bf16 caches), or the lane's 8 fp32
     // weights (FP8 caches; each value wave scales them by its group's token scales).
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     __shared__ float xmul[4][16];      // per-head output multiplier at the end
-    __shared__ int s_first, s_last;
+    __shared__ int s_first[kMaxGroup], s_last[kMaxGroup];
     auto xs = [&](int b, int j) -> f32x4_t* { return &xs_own[b][j][0]; };
     auto pw32 = [&](int b, int j) -> f32x4_t* { return (f32x4_t*)&pfrag[b][0][0] + j * kWave; };   // FP8 weights
 
@@ -201,8 +204,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     const int item = xcd * per + (xcd < rem ? xcd : rem) + local;
     const int hb_item = item % p.n_hblocks;
     const int rs = item / p.n_hblocks;
-    const int split = rs % p.n_splits;
-    const int rloc = rs / p.n_splits;
+    const int n_groups = (p.n_splits + p.splits_per_wg - 1) / p.splits_per_wg;
+    const int split0 = (rs % n_groups) * p.splits_per_wg;      // first split of this workgroup
+    const int ns = min(p.splits_per_wg, p.n_splits - split0);  // its splits split0 .. split0 + ns - 1
+    const int rloc = rs / n_groups;
     const int64_t row = (int64_t)p.row0 + rloc;
     const int head0 = hb_item * p.heads_per_wg;
     const int nhb = min(p.heads_per_wg / 16, (p.H - head0) / 16);   // valid 16-head blocks (H % 16 == 0)
@@ -224,32 +229,46 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int kk = 0; kk < 9; ++kk) qv[kk] = (bf16x8_t){};
     }
 
-    // ---- A4: translate this split's slots to physical token records ----
-    const int slot0 = split * kSplitSlots;
-    const int nslots = min(kSplitSlots, p.k - slot0);
+    // ---- A4: translate the slots of this workgroup's splits to physical token records: local slot j
+    // (split j / 512 of the group) is slot 512 split0 + j of the row.  Each thread owns local slots tid
+    // and tid + 1024; both index loads go out before either page-table load. ----
+    const int slot_base = split0 * kSplitSlots;
+    const int nslot = min(ns * kSplitSlots, p.k - slot_base);
     const int req = p.row_req ? p.row_req[row] : 0;
     const bool req_ok = req >= 0 && req < p.num_reqs;
-    if (tid == 0) { s_first = kSplitSlots; s_last = -1; }
-    if (tid < kTilesPerSplit) tile_valid[tid] = 0u;
+    if (tid < kMaxGroup) { s_first[tid] = kSplitSlots; s_last[tid] = -1; }
+    if (tid < kMaxGroup * kTilesPerSplit) tile_valid[tid] = 0u;
     __syncthreads();
-    if (tid < kSplitSlots) {
-        const int j = tid;
-        int32_t pos = p.idx[row * p.k + slot0 + (j < nslots ? j : 0)];
-        if (!(j < nslots && req_ok)) pos = -1;
-        uint32_t ph = kNoToken;
-        const int64_t lp = pos >> 6;
-        if (pos >= 0 && lp < p.bt_stride) {
-            const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
-            if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(pos & (kPage - 1));
+    {
+        constexpr int kRounds = (kMaxGroup * kSplitSlots + kAttnThreads - 1) / kAttnThreads;   // 1 or 2
+        int32_t pos[kRounds];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int j = tid + kAttnThreads * r;
+            pos[r] = p.idx[row * p.k + slot_base + (j < nslot ? j : 0)];
         }
-        phys[j] = ph;
-        const uint64_t vbits = __ballot(ph != kNoToken);
-        if (lane == 0 && vbits) {
-            const int jw = j - lane;    // first slot of this wave's 64
-            atomicMin(&s_first, jw + (int)__builtin_ctzll(vbits));
-            atomicMax(&s_last, jw + 63 - (int)__builtin_clzll(vbits));
-            atomicOr(&tile_valid[jw / kTileTok], (uint32_t)vbits);
-            atomicOr(&tile_valid[jw / kTileTok + 1], (uint32_t)(vbits >> 32));
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int j = tid + kAttnThreads * r;
+            if (j >= ns * kSplitSlots) break;   // uniform in the wave (64 divides 512)
+            int32_t ps = pos[r];
+            if (!(j < nslot && req_ok)) ps = -1;
+            uint32_t ph = kNoToken;
+            const int64_t lp = ps >> 6;
+            if (ps >= 0 && lp < p.bt_stride) {
+                const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
+                if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(ps & (kPage - 1));
+            }
+            phys[j] = ph;
+            const uint64_t vbits = __ballot(ph != kNoToken);
+            if (lane == 0 && vbits) {
+                const int jw = j - lane;                        // first slot of this wave's 64
+                const int ls = jw / kSplitSlots, jl = jw % kSplitSlots;
+                atomicMin(&s_first[ls], jl + (int)__builtin_ctzll(vbits));
+                atomicMax(&s_last[ls], jl + 63 - (int)__builtin_clzll(vbits));
+                atomicOr(&tile_valid[ls * kTilesPerSplit + jl / kTileTok], (uint32_t)vbits);
+                atomicOr(&tile_valid[ls * kTilesPerSplit + jl / kTileTok + 1], (uint32_t)(vbits >> 32));
+            }
         }
     }
     // Drain every compiler-visible global load here: inside the tile loop the only outstanding
@@ -295,8 +314,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     }
 #pragma unroll
     for (int kk = 0; kk < 9; ++kk) asm volatile("" : "+v"(qv[kk]));   // opaque: Q is never re-loaded
-    const int ntiles = s_last < 0 ? 0 : s_last / kTileTok + 1;
-    const uint32_t dummy = s_last < 0 ? 0u : phys[s_first];
+    // The split being run (ls of the group): its tile count (tiles end at its last valid slot), a valid
+    // record for the loads of its invalid slots (record 0 if it has none), and its slot offset.
+    int cur = 0, ntiles = 0, cur_slot0 = 0;
+    uint32_t dummy = 0u;
+    auto begin_split = [&](int ls) {
+        cur = ls;
+        cur_slot0 = ls * kSplitSlots;
+        const int last = s_last[ls];
+        ntiles = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / kTileTok + 1);
+        dummy = __builtin_amdgcn_readfirstlane(last < 0 ? 0u : phys[cur_slot0 + s_first[ls]]);
+    };
 
     // ---- A5: gather.  Load instruction i of a tile covers stage bytes 1024 i .. +1024; wave w issues
     // i = w, w + 16, w + 32 (those below the tile's count: 36 for bf16, 21 for FP8).  Lane l of
@@ -306,26 +334,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     constexpr int kLoads = KV_FP8 ? kFp8TileLoads : kTileLoads;
     const int nload = (wid < kLoads ? 1 : 0) + (wid + kAttnWaves < kLoads ? 1 : 0) +
                       (wid + 2 * kAttnWaves < kLoads ? 1 : 0);   // loads of this wave per tile (uniform)
-    uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
+    // Per-lane offsets of load r: the token's slot (4 bytes each) and the chunk's byte offset in the
+    // record.  Recomputed at every issue from an opaque copy of the lane id, so that they are not held
+    // in registers across the tile loop.
+    auto load_offsets = [&](uint32_t* dtok, uint32_t* doff) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int r = 0; r < kMaxLoadsPerWave; ++r) {
-        const int i = wid + kAttnWaves * r;
-        const int qd = kWave * (i < kLoads ? i : 0) + lane;
-        if (KV_FP8) {
-            const int qc = qd < kFp8TileChunks ? qd : kFp8TileChunks - 1;
-            const int t = qc / kFp8Chunks;
-            dtok[r] = 4u * (uint32_t)t;
-            doff[r] = 16u * (uint32_t)(qc - kFp8Chunks * t);
-        } else {
-            const int t = qd / 72;
-            dtok[r] = 4u * (uint32_t)t;
-            doff[r] = 16u * (uint32_t)((qd - 72 * t) ^ swz_key(t));
+        for (int r = 0; r < kMaxLoadsPerWave; ++r) {
+            const int i = wid + kAttnWaves * r;
+            const int qd = kWave * (i < kLoads ? i : 0) + ln;
+            if (KV_FP8) {
+                const int qc = qd < kFp8TileChunks ? qd : kFp8TileChunks - 1;
+                const int t = qc / kFp8Chunks;
+                dtok[r] = 4u * (uint32_t)t;
+                doff[r] = 16u * (uint32_t)(qc - kFp8Chunks * t);
+            } else {
+                const int t = qd / 72;
+                dtok[r] = 4u * (uint32_t)t;
+                doff[r] = 16u * (uint32_t)((qd - 72 * t) ^ swz_key(t));
+            }
         }
-    }
+    };
     const uint32_t ring_lds = lds_offset(ring);
     const bool half_load = KV_FP8 && wid + kAttnWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
     auto issue_tile = [&](int tile, int stage) {
-        const uint8_t* phys_tile = (const uint8_t*)phys + tile * kTileTok * 4;
+        const uint8_t* phys_tile = (const uint8_t*)(phys + cur_slot0 + tile * kTileTok);
+        uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
+        load_offsets(dtok, doff);
         const uint8_t* src[kMaxLoadsPerWave];
 #pragma unroll
         for (int r = 0; r < kMaxLoadsPerWave; ++r) {   // all slot reads first: the asm below is a compiler barrier
@@ -352,7 +388,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     };
     // bf16: zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
-        const uint32_t vm = tile_valid[tile];
+        const uint32_t vm = tile_valid[cur * kTilesPerSplit + tile];
         if (vm != 0xffffffffu) {
             uint8_t* sbase = ring + stage * kStageBytes;
 #pragma unroll
@@ -372,7 +408,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     auto dequant_tile = [&](int tile, int stage) {
         const uint8_t* st = ring + stage * kFp8StageBytes;
         uint8_t* const btile = btile_of(tile);
-        const uint32_t vm = tile_valid[tile];
+        const uint32_t vm = tile_valid[cur * kTilesPerSplit + tile];
         // Invalid tokens are cleared with a bit mask (a select between vectors would go through
         // scratch memory, whose wait would also wait for the tile loads in flight).
         int u = tid;
@@ -418,7 +454,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int j = 0; j < 4; ++j) vb[j] = tv * kBf16Record + 8 * (lane & 1) + 16 * ((2 * j + ((lane >> 1) & 1)) ^ fv);
     }
 
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
+    // Start of split ls of the group (both roles, after the previous split's final barrier): its first
+    // tiles are requested and, for FP8, tile 0 is expanded.
+    auto start_split = [&](int ls) {
+        begin_split(ls);
+        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
+        if (KV_FP8 && ntiles > 0) {
+            if (ntiles > 1) {
+                if (nload == 2) wait_vmcnt<2>();
+                else wait_vmcnt<1>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
+            dequant_tile(0, 0);
+        }
+    };
 
     // Start of tile `it`, common to both roles.
     // bf16: wait for this wave's loads of the tile, zero its invalid chunks and make the tile visible
@@ -427,17 +479,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     //   before the loop); the first barrier makes it visible, then the load of tile it+2 starts.
     //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
     //   the score waves expand tile it+1.
-    if (KV_FP8 && ntiles > 0) {
-        if (ntiles > 1) {
-            if (nload == 2) wait_vmcnt<2>();
-            else wait_vmcnt<1>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        wait_lgkmcnt0();
-        __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
-        dequant_tile(0, 0);
-    }
     auto tile_top = [&](int it) {
         const int stage = it % kStages;
         if (!KV_FP8) {
@@ -476,6 +517,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // one role (Q, the score accumulators) and of the other (the output accumulators) can share storage.
     float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
     if (is_score) {
+      // The group's splits one after the other; each starts from a fresh softmax state.
+      for (int ls = 0; ls < ns; ++ls) {
+        start_split(ls);
+        m_run = -INFINITY;
+        l_run = 0.f;
         for (int it = 0; it < ntiles; ++it) {
             const uint8_t* sb = tile_top(it);
             // ---- A7: partial scores over this wave's half of the dims ----
@@ -544,7 +590,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             // ---- A8: online softmax of the first-half waves' 16 heads ----
             if (score_ok && !half) {
                 const f32x4_t t0 = xs(shb, 0)[lane], t1 = xs(shb, 1)[lane];
-                const uint32_t vmask = tile_valid[it];
+                const uint32_t vmask = tile_valid[cur * kTilesPerSplit + it];
                 // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
                 float sv[8];
 #pragma unroll
@@ -632,9 +678,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             if (p.n_splits == 1) {
                 if (p.lse) p.lse[row * p.H + head] = lse_v;
             } else {
-                p.ws_lse[((int64_t)rloc * p.n_splits + split) * p.H + head] = lse_v;
+                p.ws_lse[((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head] = lse_v;
             }
         }
+      }
     } else {
         f32x4_t oacc[4][4];                 // [head block][16-dim block of the wave's 64 dims]
 #pragma unroll
@@ -707,6 +754,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         // The value product of tile it runs after the first barrier of tile it+1, beside the scores of
         // tile it+1: its weights and rescale factors are rewritten only after the second barrier of
         // tile it+1, its 1152-byte tile (the ring stage, or the FP8 expansion buffer) only after that too.
+      for (int ls = 0; ls < ns; ++ls) {
+        start_split(ls);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         const uint8_t* sb_prev = nullptr;
         for (int it = 0; it < ntiles; ++it) {
             const uint8_t* sb = tile_top(it);
@@ -727,7 +780,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             if (b >= nhb) break;
             const float inv = xmul[b][lane & 15];
             const int head = head0 + 16 * b + (lane & 15);
-            const int64_t pidx = (((int64_t)rloc * p.n_splits + split) * p.H + head) * kDv + vdim0 + 4 * g;
+            const int64_t pidx = (((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head) * kDv + vdim0 + 4 * g;
             if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
                 float* wo = (float*)p.ws_o + pidx;
 #pragma unroll
@@ -746,6 +799,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 }
             }
         }
+      }
     }
 }
 
@@ -878,11 +932,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch *
                                                                attn_ws_o_bytes_per_row(a.H, a.k, a.kv_dtype))
                                : nullptr;
+        // Launches with at least twice as many (row, split) items as CUs run 2 or 4 consecutive splits of a
+        // row per workgroup (FP8: 2), one after the other: the index translation and Q serve them all.
+        // Each split reduces its own tiles in order with its own softmax state, so the bits are the same.
         p.heads_per_wg = kHeadsPerBlock;
+        const int hb64 = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+        const int max_group = fp8 ? 2 : 4;
+        p.splits_per_wg = 1;
+        while (2 * p.splits_per_wg <= max_group && 2 * p.splits_per_wg <= p.n_splits &&
+               (int64_t)n * ((p.n_splits + 2 * p.splits_per_wg - 1) / (2 * p.splits_per_wg)) * hb64 >= num_cu)
+            p.splits_per_wg *= 2;
         while (p.heads_per_wg > 16 && (int64_t)n * p.n_splits * ((a.H + p.heads_per_wg - 1) / p.heads_per_wg) < num_cu)
             p.heads_per_wg /= 2;
         p.n_hblocks = (a.H + p.heads_per_wg - 1) / p.heads_per_wg;
-        const int grid = n * p.n_splits * p.n_hblocks;
+        const int grid = n * ((p.n_splits + p.splits_per_wg - 1) / p.splits_per_wg) * p.n_hblocks;
         if (fp8) hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         else hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
