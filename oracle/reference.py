@@ -58,7 +58,14 @@ design notes):
   s = amax / 448 and the codes are e4m3(x * r) with the fp32 multiplier
   r = 448 / amax (each division and the product rounded to nearest-even in
   fp32; the code rounded to nearest-even and saturated at +-448); an all-zero
-  group gets s = 0 and zero codes; the 64 rope values are stored unchanged.
+  group gets s = 0 and zero codes; the 64 rope values are stored unchanged;
+* indexer scores ("MQA logits" of the DSA indexer: the pages name the operation and its
+  paged form -- "[SM120] Sync DS4 with upstream main + validated perf backports", sections
+  "September 12 follow-up" and "2026-09-12 live validation and promotion update" -- but give
+  no formula): the published lightning-indexer form of DeepSeek sparse attention, one shared
+  128-wide bf16 index key per token (MQA) and index heads h with per-row weights w_h:
+  score[p] = sum_h w_h * relu(<q_h, k_p>) with relu(x) = x if x > 0 else 0, for positions p
+  below the clamped length whose page is listed; every other position of the row is -inf.
 """
 
 from __future__ import annotations
@@ -319,6 +326,80 @@ def split_combine(parts: Sequence[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np.nd
         for s in range(len(parts)):
             O[h] += (w[s] / tot) * Os[s, h]
     return O, LSE
+
+
+# ----------------------------------------------------------------------------------------------
+# Indexer scores (paged MQA logits): the producer of the scores the top-k consumes
+# ----------------------------------------------------------------------------------------------
+
+D_INDEX = 128
+INDEX_RECORD_BYTES = 2 * D_INDEX
+
+
+def indexer_scores_row(q: np.ndarray, w: np.ndarray, kidx: np.ndarray, block_table_row: np.ndarray,
+                       length: int, stride: int, page: int = PAGE) -> np.ndarray:
+    """Scores of one query row for positions 0 .. stride-1 (float64).
+
+    ``q`` [Hi, d] and ``w`` [Hi] are the row's index queries and head weights (float64),
+    ``kidx`` the index-key cache [num_pages, page, d] (float64).  With L the length clamped to
+    [0, stride], position p < L whose page entry block_table_row[p // page] names a page of the
+    cache has score sum_h w_h * relu(<q_h, k_p>), k_p = kidx[block_table_row[p // page], p % page];
+    every other position has -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    out = np.full(int(stride), -np.inf)
+    L = clamp_length(length, stride)
+    num_pages = kidx.shape[0]
+    for p in range(L):
+        lp = p // page
+        if lp >= len(block_table_row):
+            continue
+        pg = int(block_table_row[lp])
+        if pg < 0 or pg >= num_pages:
+            continue
+        k = kidx[pg, p % page]
+        dots = q @ k                                   # [Hi]: <q_h, k_p>
+        relu = np.where(dots > 0, dots, 0.0)
+        out[p] = float(np.sum(w * relu))
+    return out
+
+
+def indexer_scores(q_bits: np.ndarray, w: np.ndarray, kidx_bits: np.ndarray, block_table: np.ndarray,
+                   row_req: Optional[Sequence[int]], lengths: Sequence[int], stride: int,
+                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """indexer_scores_row for each requested row: ``q_bits`` bf16 patterns [R, Hi, d], ``w``
+    fp32 [R, Hi], ``kidx_bits`` bf16 patterns [num_pages, 64, d]; row r reads the block table
+    row of request row_req[r] (0 when row_req is None)."""
+    sel = list(range(len(lengths))) if rows is None else list(rows)
+    K = bf16_to_f64(kidx_bits)
+    out = np.empty((len(sel), int(stride)))
+    for o, r in enumerate(sel):
+        req = 0 if row_req is None else int(row_req[r])
+        out[o] = indexer_scores_row(bf16_to_f64(q_bits[r]), np.asarray(w[r], dtype=np.float64), K,
+                                    block_table[req], int(lengths[r]), stride)
+    return out
+
+
+def indexer_error_scale(q_bits: np.ndarray, w: np.ndarray, kidx_bits: np.ndarray, block_table: np.ndarray,
+                        row_req: Optional[Sequence[int]], lengths: Sequence[int], stride: int,
+                        rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """M[r, p] = sum_h |w_h| * sum_d |q_hd| |k_pd| for the scored positions (0 elsewhere): the
+    magnitude that bounds the rounding error of any fp32 evaluation of a score."""
+    sel = list(range(len(lengths))) if rows is None else list(rows)
+    K = np.abs(bf16_to_f64(kidx_bits))
+    out = np.zeros((len(sel), int(stride)))
+    for o, r in enumerate(sel):
+        req = 0 if row_req is None else int(row_req[r])
+        qa = np.abs(bf16_to_f64(q_bits[r]))
+        wa = np.abs(np.asarray(w[r], dtype=np.float64))
+        L = clamp_length(int(lengths[r]), stride)
+        bt = block_table[req]
+        for p in range(L):
+            lp = p // PAGE
+            if lp < len(bt) and 0 <= int(bt[lp]) < K.shape[0]:
+                out[o, p] = float(wa @ (qa @ K[int(bt[lp]), p % PAGE]))
+    return out
 
 
 # ----------------------------------------------------------------------------------------------

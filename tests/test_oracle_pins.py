@@ -616,3 +616,163 @@ def test_pins_catch_attention_mutants(mutant):
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / 24)[0, :, 0].numpy()
     ok_sdpa = bool(np.allclose(Om, ref, atol=1e-10))
     assert not (ok_closed and ok_sdpa)
+
+
+# ----------------------------------------------------------------------------------------------
+# Indexer scores (paged MQA logits)
+# ----------------------------------------------------------------------------------------------
+
+def _indexer_hand_inputs(golden_dir):
+    with open(os.path.join(golden_dir, "indexer_hand_case.json")) as f:
+        case = json.load(f)
+    q = np.array(case["q"]); w = np.array(case["w"])
+    kidx = np.zeros((case["num_pages"], case["page"], q.shape[1]))
+    for e in case["keys"]:
+        kidx[e["page"], e["slot"]] = e["k"]
+    return case, q, w, kidx
+
+
+def _indexer_hand_case_holds(fn, golden_dir):
+    """True when fn(q, w, kidx, block_table_row, length, stride) reproduces every hand-derived
+    value of the fixture and scores 0 at the other positions below the clamped length."""
+    case, q, w, kidx = _indexer_hand_inputs(golden_dir)
+    for row in case["rows"]:
+        got = fn(q, w, kidx, np.array(row["block_table"]), row["length"], row["stride"])
+        for p, v in row["expected"].items():
+            if not (got[int(p)] == _num(v)):
+                return False
+        L = min(max(row["length"], 0), row["stride"])
+        listed = [p for p in range(L) if row["block_table"][p // 64] >= 0]
+        special = {int(p) for p in row["expected"]}
+        if any(got[p] != 0.0 for p in listed if p not in special):
+            return False
+    return True
+
+
+def test_indexer_golden_hand_case(golden_dir):
+    assert _indexer_hand_case_holds(O.indexer_scores_row, golden_dir)
+
+
+def _brute_indexer(q, w, kidx, bt, length, stride):
+    """Pure-Python loops over heads and dims (tiny inputs only)."""
+    out = [-math.inf] * stride
+    L = min(max(length, 0), stride)
+    for p in range(L):
+        pg = int(bt[p // 64]) if p // 64 < len(bt) else -1
+        if pg < 0 or pg >= kidx.shape[0]:
+            continue
+        tot = 0.0
+        for h in range(len(w)):
+            dot = 0.0
+            for d in range(q.shape[1]):
+                dot += float(q[h, d]) * float(kidx[pg, p % 64, d])
+            if dot > 0:
+                tot += float(w[h]) * dot
+        out[p] = tot
+    return np.array(out)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_indexer_matches_brute_force_loops(seed):
+    rng = np.random.default_rng(seed)
+    Hi, d, npages = 3, 8, 4
+    kidx = _bf16_round(rng.standard_normal((npages, 64, d)))
+    q = _bf16_round(rng.standard_normal((Hi, d)))
+    w = rng.standard_normal(Hi).astype(np.float32).astype(np.float64)
+    bt = np.array([2, 0, -1, 3])
+    for length, stride in [(150, 200), (64, 64), (255, 256), (0, 10), (300, 256)]:
+        got = O.indexer_scores_row(q, w, kidx, bt, length, stride)
+        ref = _brute_indexer(q, w, kidx, bt, length, stride)
+        fin = np.isfinite(ref)
+        np.testing.assert_array_equal(np.isfinite(got), fin)
+        np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def _rand_bf16_bits(rng, shape):
+    return _bf16_rne_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def test_indexer_relu_odd_part_is_a_plain_product():
+    """relu(x) - relu(-x) = x, so scores(q) - scores(-q) = sum_h w_h <q_h, k_p>: one matrix
+    product over the dense context, gathered here by direct page arithmetic."""
+    rng = np.random.default_rng(5)
+    R, Hi, npages, L = 2, 16, 6, 300
+    kbits = _rand_bf16_bits(rng, (npages, 64, 128))
+    qbits = _rand_bf16_bits(rng, (R, Hi, 128))
+    w = rng.standard_normal((R, Hi)).astype(np.float32)
+    bt = np.array([[4, 1, 5, 0, 2], [3, 2, 1, 0, 4]])
+    pos = O.indexer_scores(qbits, w, kbits, bt, [0, 1], [L, L], 320)
+    neg = O.indexer_scores(qbits ^ np.uint16(0x8000), w, kbits, bt, [0, 1], [L, L], 320)
+    K = O.bf16_to_f64(kbits)
+    for r in range(R):
+        dense = np.stack([K[bt[r][p >> 6], p & 63] for p in range(L)])            # [L, 128]
+        lin = torch.from_numpy(dense) @ torch.from_numpy(O.bf16_to_f64(qbits[r])).T @ \
+            torch.from_numpy(w[r].astype(np.float64))
+        np.testing.assert_allclose(pos[r, :L] - neg[r, :L], lin.numpy(), rtol=1e-12, atol=1e-10)
+        assert np.all(np.isneginf(pos[r, L:])) and np.all(np.isneginf(neg[r, L:]))
+
+
+def test_indexer_weights_are_linear_and_one_hot_heads_isolate_relu():
+    rng = np.random.default_rng(6)
+    Hi, d = 4, 128
+    kidx = _bf16_round(rng.standard_normal((3, 64, d)))
+    q = _bf16_round(rng.standard_normal((Hi, d)))
+    w = rng.standard_normal(Hi)
+    bt = np.array([1, 2, 0])
+    a = O.indexer_scores_row(q, w, kidx, bt, 170, 192)
+    np.testing.assert_array_equal(O.indexer_scores_row(q, 2 * w, kidx, bt, 170, 192)[:170], 2 * a[:170])
+    np.testing.assert_array_equal(O.indexer_scores_row(q, 0 * w, kidx, bt, 170, 192)[:170], np.zeros(170))
+    # one head of weight 1 whose query is the unit vector e_7: the score is relu(k_p[7])
+    e = np.zeros((1, d)); e[0, 7] = 1.0
+    got = O.indexer_scores_row(e, np.ones(1), kidx, bt, 170, 192)
+    k7 = np.array([kidx[bt[p // 64], p % 64, 7] for p in range(170)])
+    np.testing.assert_array_equal(got[:170], np.maximum(k7, 0.0))
+
+
+def test_indexer_page_permutation_invariance():
+    """Moving the pages of the cache and rewriting the block table leaves every score as is."""
+    rng = np.random.default_rng(7)
+    kbits = _rand_bf16_bits(rng, (5, 64, 128))
+    qbits = _rand_bf16_bits(rng, (1, 8, 128))
+    w = rng.standard_normal((1, 8)).astype(np.float32)
+    bt = np.array([[3, 0, 4]])
+    perm = np.array([2, 4, 0, 1, 3])                 # new position of old page i
+    moved = np.empty_like(kbits); moved[perm] = kbits
+    a = O.indexer_scores(qbits, w, kbits, bt, None, [190], 192)
+    b = O.indexer_scores(qbits, w, moved, perm[bt], None, [190], 192)
+    np.testing.assert_array_equal(a, b)
+
+
+# Indexer mutants, planted in copies of the oracle's row function on the CPU: each must fail a pin.
+
+def _idx_mutant_relu_after_weight(q, w, kidx, bt, length, stride, page=64):
+    out = O.indexer_scores_row(q, w, kidx, bt, length, stride)
+    L = min(max(length, 0), stride)
+    for p in range(L):
+        if np.isfinite(out[p]):
+            dots = q @ kidx[bt[p // 64], p % 64]
+            out[p] = float(np.sum(np.maximum(w * dots, 0)))
+    return out
+
+
+def _idx_mutant_no_relu(q, w, kidx, bt, length, stride, page=64):
+    out = O.indexer_scores_row(q, w, kidx, bt, length, stride)
+    L = min(max(length, 0), stride)
+    for p in range(L):
+        if np.isfinite(out[p]):
+            out[p] = float(w @ (q @ kidx[bt[p // 64], p % 64]))
+    return out
+
+
+def _idx_mutant_identity_pages(q, w, kidx, bt, length, stride, page=64):    # block table ignored
+    return O.indexer_scores_row(q, w, kidx, np.where(np.asarray(bt) >= 0, np.arange(len(bt)), -1), length, stride)
+
+
+def _idx_mutant_no_clamp(q, w, kidx, bt, length, stride, page=64):          # negative length wraps
+    return O.indexer_scores_row(q, w, kidx, bt, length % stride if length < 0 else length, stride)
+
+
+@pytest.mark.parametrize("mutant", [_idx_mutant_relu_after_weight, _idx_mutant_no_relu,
+                                    _idx_mutant_identity_pages, _idx_mutant_no_clamp])
+def test_pins_catch_indexer_mutants(mutant, golden_dir):
+    assert not _indexer_hand_case_holds(mutant, golden_dir)
