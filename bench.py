@@ -33,14 +33,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8", "decode_swa192", "prefill_c4"],
+    ap.add_argument("--workload", default="decode_bf16", choices=["decode_bf16", "decode_fp8", "kv_write_fp8", "decode_swa192", "prefill_c4",
+                                                              "indexer"],
                     help="decode_bf16: B=64, contexts U[8192, 65536], bf16 KV (the headline); "
                          "decode_fp8: B=128, contexts U[32768, 131072], FP8 KV; "
                          "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step); "
                          "decode_swa192: B=64 draft rows over 128 sliding-window + 5 draft positions, index "
                          "width 192 (and the same rows at width 256); "
                          "prefill_c4: one request, T=4096 query tokens at positions 126976..131071 of a "
-                         "131072-token context, causal top-k 2048 + prefill attention")
+                         "131072-token context, causal top-k 2048 + prefill attention; "
+                         "indexer: indexer scores (paged MQA logits) of B=64 decode rows, 64 index heads of "
+                         "width 128, contexts U[8192, 65536], score rows of 65536")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH/WRITE_SIZE)")
     return ap.parse_args()
@@ -278,6 +281,72 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_indexer(args):
+    """Indexer scores (paged MQA logits) for B = 64 decode rows: 64 index heads of width 128, one bf16
+    128-wide key per token (256 B) in pages of 64, contexts U[8192, 65536] (2.36 M keys, 604 MB per
+    call, larger than the 256 MB last-level cache), every row written in full (65536 fp32 entries, -inf
+    past its length).  Four rotating (Q, weights) sets."""
+    import numpy as np
+    import torch
+
+    import sparse_mla_attention_topk_amd as smla
+    from sparse_mla_attention_topk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.indexer_decode(dev, n_sets=N_SETS)
+    B, Hi, S = wl.q[0].shape[0], wl.Hi, wl.stride
+    out = torch.empty((B, S), dtype=torch.float32, device=dev)
+
+    def call(i):
+        smla.paged_mqa_logits(wl.q[i % N_SETS], wl.weights[i % N_SETS], wl.kidx, wl.block_table, lengths=wl.lengths,
+                              row_req=wl.row_req, out=out)
+    for i in range(N_SETS):
+        call(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(dev)
+    ms = _graph_time(torch, s, call, args.steps, args.warmup)
+    keys = int(wl.ctx_lens.sum())
+    pages = int(sum((int(L) + 63) // 64 for L in wl.ctx_lens))
+    key_bytes = keys * 256
+    alg_bytes = key_bytes + B * S * 4 + B * Hi * 128 * 2 + B * Hi * 4 + pages * 4
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    flops = keys * Hi * 128 * 2
+    cpu = None
+    if args.cpu_rows > 0:
+        from threadpoolctl import threadpool_limits
+
+        import oracle.reference as O
+        n = max(1, min(B, args.cpu_rows // 8))
+        qb = wl.q[0][:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        kb = wl.kidx.view(torch.int16).cpu().numpy().view(np.uint16)
+        wn, btn = wl.weights[0][:n].cpu().numpy(), wl.block_table.cpu().numpy()
+        ln = wl.lengths.cpu().numpy()
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.indexer_scores(qb, wn, kb, btn, list(range(n)), ln[:n], S)
+            dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} rows of the same workload ({int(ln[:n].sum())} keys) scored by the oracle "
+                         f"(numpy fp64, 1 thread), {dt:.1f} s"}
+    line = {
+        "metric": "indexer scores (paged MQA logits) rows/s + key-stream HBM GB/s (B=64, Hi=64, d=128, 1 GPU)",
+        "value": B / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": wl.name, "rows": B, "index_heads": Hi, "index_dim": 128, "page_block_size": 64,
+                   "context": "uniform [8192, 65536]", "score_row": S, "keys_per_call": keys,
+                   "rotating_sets": N_SETS, "launch": "hip_graph_of_K_calls"},
+        "key_GBps": key_bytes / (ms * 1e-3) / 1e9,
+        "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "paged_mqa_logits_kernel<4>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +359,8 @@ def main():
         return bench_swa(args)
     if args.workload == "prefill_c4":
         return bench_prefill(args)
+    if args.workload == "indexer":
+        return bench_indexer(args)
     import torch
 
     import sparse_mla_attention_topk_amd as smla

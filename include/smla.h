@@ -11,6 +11,7 @@
  *                                                [smla_sparse_mla_decode, smla_sparse_mla_prefill_chunk]
  * and writes new tokens' records into the paged cache, quantizing them for FP8 caches
  *                                                [smla_kv_cache_write]
+ * and produces the indexer scores the selector ranks  [smla_paged_mqa_logits]
  * The result for a row never depends on the other rows of the call.
  *
  * Sources (pages by title, section):
@@ -190,6 +191,36 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
  * Tokens mapped to the same slot race: which record remains is unspecified.  T = 0 enqueues nothing. */
 smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,
                                 void* cache, int32_t kv_dtype, int64_t num_pages, void* stream);
+
+/* Indexer scores (paged MQA logits): the per-position scores smla_topk_per_row consumes.
+ * Sources: "[SM120] Sync DS4 with upstream main + validated perf backports", sections "September 12
+ * follow-up" and "2026-09-12 live validation and promotion update" name the DSA indexer's paged MQA
+ * logits without a formula; the formula is the published lightning-indexer form of DeepSeek sparse
+ * attention (a reading).  Paging and length clamping as for the latent cache ("[Bugfix] Make DSV4
+ * sparse MLA work end-to-end ...", section "Purpose").
+ *   q:       bf16 [rows, Hi, 128] index queries, row r at q + r*q_row_stride elements
+ *            (q_row_stride >= Hi*128, multiple of 8); 16-byte aligned.
+ *   weights: fp32 [rows, Hi] per-row head weights, row r at weights + r*w_row_stride
+ *            (w_row_stride >= Hi, multiple of 4); 16-byte aligned.
+ *   kidx:    bf16 [num_pages, 64, 128] paged index-key cache (one 128-wide key per token, shared by
+ *            every index head); 16-byte aligned.
+ *   block_table / bt_stride / num_reqs / row_req: as for smla_sparse_mla_decode.
+ *   lengths: int32 [rows] or NULL (NULL: out_stride); L_r = clamp(lengths[r], 0, out_stride).
+ *   out:     fp32 [rows, out_stride], 4-byte aligned.  For p < L_r whose page
+ *            block_table[req*bt_stride + p/64] lies in [0, num_pages) (with p/64 < bt_stride and req
+ *            in [0, num_reqs)):
+ *              out[r*out_stride + p] = sum_h weights[r, h] * relu(<q[r, h, :], key_p>),
+ *            relu(x) = x if x > 0 else 0, key_p = token p % 64 of that page; every other p in
+ *            [0, out_stride) gets -inf.  Every entry of the row is written.
+ *   Arithmetic: bf16 products accumulated in fp32 (MFMA, 32 dims per step), then one fp32 fused
+ *   multiply-add per head in a fixed order and a fixed pairwise sum over four partial sums; the
+ *   result for a row does not depend on the other rows of the call.
+ * Requires Hi in {16, 32, 48, 64}, 1 <= out_stride <= 2^31 - 1, rows >= 0, num_pages >= 1.  rows = 0
+ * enqueues nothing. */
+smla_status smla_paged_mqa_logits(const void* q, int64_t q_row_stride, const float* weights, int64_t w_row_stride,
+                                  const void* kidx, int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                  int32_t num_reqs, const int32_t* row_req, const int32_t* lengths, int32_t rows,
+                                  int32_t Hi, float* out, int64_t out_stride, void* stream);
 
 #ifdef __cplusplus
 }

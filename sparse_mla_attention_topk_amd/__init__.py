@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "SmlaError", "KV_BF16", "KV_FP8", "Capacity", "library_path", "load_library", "exported_symbols",
     "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row", "topk_workspace",
-    "sparse_mla_decode", "sparse_mla_prefill_chunk", "kv_cache_write",
+    "sparse_mla_decode", "sparse_mla_prefill_chunk", "kv_cache_write", "paged_mqa_logits",
 ]
 
 KV_BF16 = 0
@@ -29,7 +29,7 @@ _LIB: Optional[ctypes.CDLL] = None
 exported_symbols = (
     "smla_last_error", "smla_version", "smla_is_supported", "smla_workspace_size",
     "smla_fill_causal_lengths", "smla_topk_per_row", "smla_sparse_mla_decode",
-    "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write",
+    "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write", "smla_paged_mqa_logits",
 )
 
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_WORKSPACE",
@@ -80,6 +80,7 @@ def load_library() -> ctypes.CDLL:
         "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, P, SZ, P],
                                           ctypes.c_int),
         "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
+        "smla_paged_mqa_logits": ([P, I64, P, I64, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -317,3 +318,51 @@ def kv_cache_write(kv_in: torch.Tensor, slot_mapping: torch.Tensor, cache: torch
     _check(lib.smla_kv_cache_write(_ptr(kv_in), kv_in.stride(0), _ptr(slot_mapping), T, _ptr(cache), dt,
                                    cache.shape[0], _stream(dev)))
     return cache
+
+
+def paged_mqa_logits(q: torch.Tensor, weights: torch.Tensor, kidx: torch.Tensor, block_table: torch.Tensor,
+                     lengths: Optional[torch.Tensor] = None, row_req: Optional[torch.Tensor] = None,
+                     out_stride: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexer scores of each row of ``q`` [rows, Hi, 128] (bf16) with head weights ``weights``
+    [rows, Hi] (fp32) over the paged index-key cache ``kidx`` (bf16 [num_pages, 64, 128]):
+    out[r, p] = sum_h w[r, h] * relu(<q[r, h], key_p>) for p below the row's length (``lengths``
+    int32 [rows], clamped to [0, out_stride]; None: out_stride) whose page is listed, -inf elsewhere.
+    ``block_table`` int32 [num_reqs, max_pages]; ``row_req`` int32 [rows] (None: request 0).
+    Returns ``out`` fp32 [rows, out_stride] (allocated when None)."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, contiguous=False)
+    if q.dim() != 3 or q.shape[2] != 128 or q.stride(2) != 1 or q.stride(1) != 128:
+        raise ValueError("q must be [rows, Hi, 128] with contiguous heads")
+    dev = q.device
+    rows, Hi = q.shape[0], q.shape[1]
+    _require(weights, "weights", torch.float32, dev, contiguous=False)
+    if weights.dim() != 2 or weights.shape[0] != rows or weights.shape[1] != Hi or weights.stride(1) != 1:
+        raise ValueError("weights must be [rows, Hi] with contiguous rows")
+    _require(kidx, "kidx", torch.bfloat16, dev)
+    if kidx.dim() != 3 or kidx.shape[1] != 64 or kidx.shape[2] != 128:
+        raise ValueError("kidx must be [num_pages, 64, 128]")
+    _require(block_table, "block_table", torch.int32, dev)
+    if lengths is not None:
+        _require(lengths, "lengths", torch.int32, dev)
+        if lengths.numel() < rows:
+            raise ValueError("lengths is shorter than rows")
+    if row_req is not None:
+        _require(row_req, "row_req", torch.int32, dev)
+        if row_req.numel() < rows:
+            raise ValueError("row_req is shorter than rows")
+    if out is None:
+        if out_stride is None:
+            raise ValueError("out_stride is required when out is not given")
+        out = torch.empty(rows, int(out_stride), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", torch.float32, dev)
+        if out.dim() != 2 or out.shape[0] != rows:
+            raise ValueError("out must be a contiguous [rows, stride] tensor")
+        if out_stride is not None and int(out_stride) != out.shape[1]:
+            raise ValueError("out_stride does not match out")
+    bt2 = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    _check(lib.smla_paged_mqa_logits(_ptr(q), q.stride(0), _ptr(weights), weights.stride(0), _ptr(kidx),
+                                     kidx.shape[0], _ptr(bt2), bt2.shape[1], bt2.shape[0], _ptr(row_req),
+                                     _ptr(lengths), rows, Hi, _ptr(out), out.shape[1],
+                                     _stream(dev)))
+    return out

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsmla.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "topk.hip", "attention.hip", "cache_write.hip"]
+SOURCES = ["api.cpp", "topk.hip", "attention.hip", "cache_write.hip", "indexer.hip"]
 ARCH = os.environ.get("SMLA_OFFLOAD_ARCH", "gfx950")
 
 

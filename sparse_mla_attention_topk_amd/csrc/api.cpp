@@ -238,4 +238,47 @@ smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const 
                       "kv_cache_write");
 }
 
+smla_status smla_paged_mqa_logits(const void* q, int64_t q_row_stride, const float* weights, int64_t w_row_stride,
+                                  const void* kidx, int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                  int32_t num_reqs, const int32_t* row_req, const int32_t* lengths, int32_t rows,
+                                  int32_t Hi, float* out, int64_t out_stride, void* stream) {
+    if (Hi < 16 || Hi > 64 || Hi % 16 != 0)
+        return fail(SMLA_ERR_UNSUPPORTED, "index heads Hi=%d is not supported; supported: 16, 32, 48, 64", Hi);
+    if (rows < 0) return fail(SMLA_ERR_INVALID_ARG, "rows=%d must be >= 0", rows);
+    if (out_stride < 1 || out_stride > kMaxStride)
+        return fail(SMLA_ERR_CAPACITY, "out_stride=%lld is outside [1, %lld]", (long long)out_stride,
+                    (long long)kMaxStride);
+    if (num_pages < 1) return fail(SMLA_ERR_INVALID_ARG, "num_pages=%lld must be >= 1", (long long)num_pages);
+    if (num_pages > kMaxPages)
+        return fail(SMLA_ERR_CAPACITY, "num_pages=%lld exceeds the supported maximum %lld", (long long)num_pages,
+                    (long long)kMaxPages);
+    if (bt_stride < 1) return fail(SMLA_ERR_INVALID_ARG, "bt_stride=%lld must be >= 1", (long long)bt_stride);
+    if (num_reqs < 1) return fail(SMLA_ERR_INVALID_ARG, "num_reqs=%d must be >= 1", num_reqs);
+    if (q_row_stride < (int64_t)Hi * 128)
+        return fail(SMLA_ERR_INVALID_ARG, "q_row_stride=%lld must be >= Hi*128=%lld", (long long)q_row_stride,
+                    (long long)Hi * 128);
+    if (w_row_stride < Hi)
+        return fail(SMLA_ERR_INVALID_ARG, "w_row_stride=%lld must be >= Hi=%d", (long long)w_row_stride, Hi);
+    if (rows == 0) return ok();
+    if (!q) return fail(SMLA_ERR_INVALID_ARG, "q is NULL");
+    if (!weights) return fail(SMLA_ERR_INVALID_ARG, "weights is NULL");
+    if (!kidx) return fail(SMLA_ERR_INVALID_ARG, "kidx is NULL");
+    if (!block_table) return fail(SMLA_ERR_INVALID_ARG, "block_table is NULL");
+    if (!out) return fail(SMLA_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(q, 16)) return fail(SMLA_ERR_ALIGNMENT, "q must be 16-byte aligned");
+    if (q_row_stride % 8 != 0)
+        return fail(SMLA_ERR_ALIGNMENT, "q_row_stride=%lld must be a multiple of 8 elements", (long long)q_row_stride);
+    if (!aligned(weights, 16)) return fail(SMLA_ERR_ALIGNMENT, "weights must be 16-byte aligned");
+    if (w_row_stride % 4 != 0)
+        return fail(SMLA_ERR_ALIGNMENT, "w_row_stride=%lld must be a multiple of 4 elements", (long long)w_row_stride);
+    if (!aligned(kidx, 16)) return fail(SMLA_ERR_ALIGNMENT, "kidx must be 16-byte aligned");
+    if (!aligned(block_table, 4)) return fail(SMLA_ERR_ALIGNMENT, "block_table must be 4-byte aligned");
+    if (row_req && !aligned(row_req, 4)) return fail(SMLA_ERR_ALIGNMENT, "row_req must be 4-byte aligned");
+    if (lengths && !aligned(lengths, 4)) return fail(SMLA_ERR_ALIGNMENT, "lengths must be 4-byte aligned");
+    if (!aligned(out, 4)) return fail(SMLA_ERR_ALIGNMENT, "out must be 4-byte aligned");
+    smla::IdxArgs a{q,         q_row_stride, weights, w_row_stride, kidx, num_pages, block_table, bt_stride,
+                    num_reqs, row_req,      lengths, rows,         Hi,   out,       out_stride};
+    return hip_status(smla::launch_paged_mqa_logits(a, (hipStream_t)stream), "paged_mqa_logits");
+}
+
 }  // extern "C"

@@ -47,6 +47,25 @@ struct AttnArgs {
     size_t ws_bytes;
 };
 
+// Indexer scores (paged MQA logits).
+struct IdxArgs {
+    const void* q;           // bf16 [rows][Hi][128], row stride q_row_stride elements
+    int64_t q_row_stride;
+    const float* weights;    // fp32 [rows][Hi], row stride w_row_stride elements
+    int64_t w_row_stride;
+    const void* kidx;        // bf16 [num_pages][64][128]
+    int64_t num_pages;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int32_t num_reqs;
+    const int32_t* row_req;
+    const int32_t* lengths;
+    int32_t rows;
+    int32_t Hi;
+    float* out;              // fp32 [rows][out_stride]
+    int64_t out_stride;
+};
+
 // Top-k workspace bytes per row for the chunked path (0: the row is processed by one workgroup).
 size_t topk_ws_bytes_per_row(int64_t row_stride, int32_t k);
 hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t row_stride,
@@ -54,6 +73,7 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
                        hipStream_t stream);
 hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_paged_mqa_logits(const IdxArgs& a, hipStream_t stream);
 hipError_t launch_kv_cache_write(const void* in, int64_t in_row_stride, const int64_t* slots, int32_t T, void* cache,
                                  int kv_dtype, int64_t num_pages, hipStream_t stream);
 

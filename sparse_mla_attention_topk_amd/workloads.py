@@ -84,6 +84,21 @@ def uniform_int(lo: int, hi: int, n: int, g: torch.Generator, device) -> torch.T
     return torch.randint(lo, hi + 1, (n,), generator=g, device=device, dtype=torch.int64)
 
 
+def page_table(ctx_lens: torch.Tensor, g: torch.Generator, device):
+    """Block table (CPU int32 [requests, max_pages]) that hands out physical pages 1..N through a
+    seeded random permutation, and N.  Unused entries are 0 (the null page)."""
+    npages = [int(math.ceil(int(L) / PAGE)) for L in ctx_lens]
+    total = sum(npages)
+    max_pages = max(1, max(npages) if npages else 1)
+    perm = torch.randperm(total, generator=g, device=device).cpu() + 1
+    bt = torch.zeros((len(npages), max_pages), dtype=torch.int32)
+    off = 0
+    for r, n in enumerate(npages):
+        bt[r, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    return bt, total
+
+
 def make_paged_cache(ctx_lens: torch.Tensor, kv_dtype: int, g: torch.Generator, device,
                      chunk_pages: int = 4096) -> PagedCache:
     """Allocate a paged cache holding one context per entry of ``ctx_lens``.
@@ -94,15 +109,7 @@ def make_paged_cache(ctx_lens: torch.Tensor, kv_dtype: int, g: torch.Generator, 
     2**U(-4, 4) per (token, 128-group) and bf16 N(0,1) rope.
     """
     ctx_lens = ctx_lens.to(torch.int64).cpu()
-    npages = [int(math.ceil(int(L) / PAGE)) for L in ctx_lens]
-    total = sum(npages)
-    max_pages = max(1, max(npages) if npages else 1)
-    perm = torch.randperm(total, generator=g, device=device).cpu() + 1
-    bt = torch.zeros((len(npages), max_pages), dtype=torch.int32)
-    off = 0
-    for r, n in enumerate(npages):
-        bt[r, :n] = perm[off:off + n].to(torch.int32)
-        off += n
+    bt, total = page_table(ctx_lens, g, device)
     rec = BF16_RECORD_BYTES if kv_dtype == KV_BF16 else FP8_RECORD_BYTES
     kv = torch.empty((total + 1, PAGE, rec), dtype=torch.uint8, device=device)
     # Fill physical pages in chunks so the fp32 intermediates stay small.
@@ -310,3 +317,75 @@ def swa_draft_indices(ctx_lens: torch.Tensor, window: int = 128, draft: int = 5,
         n = int(c) - lo
         out[r, :n] = torch.arange(lo, int(c), dtype=torch.int32)
     return out.to(ctx_lens.device)
+
+
+# --------------------------------------------------------------------------------------------
+# Indexer inputs: a paged index-key cache (one 128-wide bf16 key per token), index queries and
+# per-row head weights.
+# --------------------------------------------------------------------------------------------
+
+D_INDEX = 128
+
+
+def make_index_cache(block_table_cpu: torch.Tensor, ctx_lens, num_pages: int, g: torch.Generator, device,
+                     chunk_pages: int = 8192) -> torch.Tensor:
+    """bf16 [num_pages, 64, 128] index keys drawn N(0,1) for pages 1..num_pages-1; the null page 0
+    and every slot past a context's end in its last page hold NaN."""
+    kidx = torch.empty((num_pages, PAGE, D_INDEX), dtype=torch.bfloat16, device=device)
+    for p0 in range(1, num_pages, chunk_pages):
+        p1 = min(num_pages, p0 + chunk_pages)
+        kidx[p0:p1] = torch.randn((p1 - p0, PAGE, D_INDEX), generator=g, device=device,
+                                  dtype=torch.float32).to(torch.bfloat16)
+    kidx[0] = float("nan")
+    for r, L in enumerate(ctx_lens):
+        L = int(L)
+        if L % PAGE:
+            kidx[int(block_table_cpu[r, L // PAGE]), L % PAGE:] = float("nan")
+    return kidx
+
+
+@dataclasses.dataclass
+class IndexerWorkload:
+    name: str
+    kidx: torch.Tensor          # bf16 [num_pages, 64, 128]
+    block_table: torch.Tensor   # int32 [num_requests, max_pages]
+    ctx_lens: torch.Tensor      # int64 [num_requests] (CPU)
+    q: List[torch.Tensor]       # per set: bf16 [rows, Hi, 128]
+    weights: List[torch.Tensor] # per set: fp32 [rows, Hi]
+    lengths: torch.Tensor       # int32 [rows]
+    row_req: torch.Tensor       # int32 [rows]
+    Hi: int
+    stride: int
+
+
+def indexer_queries(rows: int, Hi: int, g: torch.Generator, device):
+    """Index queries bf16 N(0,1) [rows, Hi, 128] and head weights fp32 N(0, 1/Hi) [rows, Hi]."""
+    q = torch.randn((rows, Hi, D_INDEX), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((rows, Hi), generator=g, device=device, dtype=torch.float32) / math.sqrt(Hi)
+    return q, w
+
+
+def indexer_workload(name: str, B: int, Hi: int, ctx_lo: int, ctx_hi: int, seed: int, device, n_sets: int = 1,
+                     stride: Optional[int] = None) -> IndexerWorkload:
+    """B decode rows, one request each, context lengths uniform in [ctx_lo, ctx_hi]; each row
+    scores its whole context.  Draw order: lengths, page permutation, keys, then (Q, weights) per set."""
+    g = _gen(seed, device)
+    ctx = uniform_int(ctx_lo, ctx_hi, B, g, device).cpu()
+    bt, total = page_table(ctx, g, device)
+    kidx = make_index_cache(bt, ctx, total + 1, g, device)
+    qs, ws = [], []
+    for _ in range(n_sets):
+        q, w = indexer_queries(B, Hi, g, device)
+        qs.append(q)
+        ws.append(w)
+    return IndexerWorkload(name=name, kidx=kidx, block_table=bt.to(device), ctx_lens=ctx, q=qs, weights=ws,
+                           lengths=ctx.to(torch.int32).to(device),
+                           row_req=torch.arange(B, dtype=torch.int32, device=device), Hi=Hi,
+                           stride=int(stride if stride is not None else ctx_hi))
+
+
+def indexer_decode(device, seed: int = 6, n_sets: int = 1) -> IndexerWorkload:
+    """B=64 decode rows, 64 index heads of width 128, contexts uniform in [8192, 65536] (the decode
+    rows the bf16 attention workload selects from), score rows of 65536 entries."""
+    return indexer_workload("indexer_B64_Hi64_L8K-64K", B=64, Hi=64, ctx_lo=8192, ctx_hi=65536, seed=seed,
+                            device=device, n_sets=n_sets)

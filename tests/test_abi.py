@@ -190,3 +190,36 @@ def test_kv_cache_write_validation(lib):
     st = f(P(0x1000), 576, P(0x2000), 4, P(0x3008), 1, 10, None)
     assert st == 4 and b"cache must be 16-byte aligned" in lib.smla_last_error()
     assert f(None, 576, None, 0, None, 1, 10, None) == 0        # T = 0: nothing to do
+
+
+def test_paged_mqa_logits_validation(lib):
+    f = lib.smla_paged_mqa_logits
+    P = _fake
+
+    def call(q=0x1000, qs=8192, w=0x2000, ws=64, k=0x3000, npages=10, bt=0x4000, bts=4, nreq=1, rreq=None,
+             lens=None, rows=2, Hi=64, out=0x5000, ostride=256):
+        return f(P(q) if q else None, qs, P(w) if w else None, ws, P(k) if k else None, npages,
+                 P(bt) if bt else None, bts, nreq, P(rreq) if rreq else None, P(lens) if lens else None, rows, Hi,
+                 P(out) if out else None, ostride, None)
+
+    assert call(Hi=8) == 2 and b"Hi=8" in lib.smla_last_error()
+    assert call(Hi=80) == 2 and b"Hi=80" in lib.smla_last_error()
+    assert call(rows=-1) == 1 and b"rows=-1" in lib.smla_last_error()
+    assert call(ostride=0) == 5 and b"out_stride=0" in lib.smla_last_error()
+    assert call(npages=0) == 1 and b"num_pages=0" in lib.smla_last_error()
+    assert call(bts=0) == 1 and b"bt_stride=0" in lib.smla_last_error()
+    assert call(nreq=0) == 1 and b"num_reqs=0" in lib.smla_last_error()
+    assert call(qs=100) == 1 and b"q_row_stride=100" in lib.smla_last_error()
+    assert call(ws=32) == 1 and b"w_row_stride=32" in lib.smla_last_error()
+    assert call(q=0) == 1 and b"q is NULL" in lib.smla_last_error()
+    assert call(w=0) == 1 and b"weights is NULL" in lib.smla_last_error()
+    assert call(k=0) == 1 and b"kidx is NULL" in lib.smla_last_error()
+    assert call(out=0) == 1 and b"out is NULL" in lib.smla_last_error()
+    assert call(q=0x1008) == 4 and b"q must be 16-byte aligned" in lib.smla_last_error()
+    assert call(qs=8196) == 4 and b"q_row_stride=8196" in lib.smla_last_error()
+    assert call(w=0x2004) == 4 and b"weights must be 16-byte aligned" in lib.smla_last_error()
+    assert call(ws=66) == 4 and b"w_row_stride=66" in lib.smla_last_error()
+    assert call(k=0x3008) == 4 and b"kidx must be 16-byte aligned" in lib.smla_last_error()
+    assert call(lens=0x6002) == 4 and b"lengths" in lib.smla_last_error()
+    assert call(out=0x5002) == 4 and b"out must be 4-byte aligned" in lib.smla_last_error()
+    assert call(rows=0, q=0, w=0, k=0, bt=0, out=0) == 0          # rows = 0: nothing to do
