@@ -121,6 +121,22 @@ def _graph_time(torch, s, fn, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
+def _eager_time(torch, s, fn, n, warmup):
+    """ms per call of fn over n eager calls on stream s (after warmup calls), timed with events on s."""
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for i in range(n):
+            fn(i)
+        e1.record(s)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def bench_kv_write(args):
     """FP8 cache write: T = 65536 new tokens (a 64K-token prefill) into a paged cache, four
     rotating token sets so the 75 MB of input per call is not cache-resident; plus T = 128 (one
@@ -305,7 +321,10 @@ def bench_indexer(args):
         call(i)
     torch.cuda.synchronize()
     s = torch.cuda.Stream(dev)
-    ms = _graph_time(torch, s, call, args.steps, args.warmup)
+    if args.no_graph:
+        ms = _eager_time(torch, s, call, args.steps, args.warmup)
+    else:
+        ms = _graph_time(torch, s, call, args.steps, args.warmup)
     keys = int(wl.ctx_lens.sum())
     pages = int(sum((int(L) + 63) // 64 for L in wl.ctx_lens))
     key_bytes = keys * 256
@@ -317,7 +336,7 @@ def bench_indexer(args):
         from threadpoolctl import threadpool_limits
 
         import oracle.reference as O
-        n = max(1, min(B, args.cpu_rows // 8))
+        n = max(1, min(B, args.cpu_rows // 4))
         qb = wl.q[0][:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         kb = wl.kidx.view(torch.int16).cpu().numpy().view(np.uint16)
         wn, btn = wl.weights[0][:n].cpu().numpy(), wl.block_table.cpu().numpy()
