@@ -50,14 +50,15 @@ def parse():
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_bf16_B64_H64_k2048_hbm_traffic.md")
+INDEXER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "indexer_B64_Hi64_L8K-64K_hbm_traffic.md")
 
 
-def measured_traffic():
-    """HBM bytes per sparse_mla_decode call from the committed counter record, or None when the
-    attention source has changed since the counters were taken."""
+def measured_traffic(record=TRAFFIC_RECORD):
+    """HBM bytes per call from a committed counter record, or None when the kernel source has
+    changed since the counters were taken."""
     import hashlib
     try:
-        line = [l for l in open(TRAFFIC_RECORD) if l.startswith("traffic-record:")][0]
+        line = [l for l in open(record) if l.startswith("traffic-record:")][0]
     except (OSError, IndexError):
         return None
     fields = dict(kv.split("=", 1) for kv in line.split()[1:])
@@ -325,6 +326,10 @@ def bench_indexer(args):
         ms = _eager_time(torch, s, call, args.steps, args.warmup)
     else:
         ms = _graph_time(torch, s, call, args.steps, args.warmup)
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
     keys = int(wl.ctx_lens.sum())
     pages = int(sum((int(L) + 63) // 64 for L in wl.ctx_lens))
     key_bytes = keys * 256
@@ -359,7 +364,8 @@ def bench_indexer(args):
         "key_GBps": key_bytes / (ms * 1e-3) / 1e9,
         "mfma_tflops": flops / (ms * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "paged_mqa_logits_kernel<4>",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(INDEXER_TRAFFIC_RECORD),
+                     "kernel": "paged_mqa_logits_kernel<4, true, true>",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
