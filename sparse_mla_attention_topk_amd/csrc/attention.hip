@@ -316,15 +316,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     for (int kk = 0; kk < 9; ++kk) asm volatile("" : "+v"(qv[kk]));   // opaque: Q is never re-loaded
     // The split being run (ls of the group): its tile count (tiles end at its last valid slot), a valid
     // record for the loads of its invalid slots (record 0 if it has none), and its slot offset.
-    int cur = 0, ntiles = 0, cur_slot0 = 0;
-    uint32_t dummy = 0u;
+    // Tile t of the split sits in ring stage (sbase + t) % kStages; sbase runs on from split to split,
+    // since a split with at least two tiles requests the next split's tiles 0 and 1 in the slots where
+    // its own tiles ntiles and ntiles + 1 would go (pf), so the next split starts with them in flight.
+    int cur = 0, ntiles = 0, cur_slot0 = 0, sbase = 0, nx_ntiles = 0;
+    uint32_t dummy = 0u, nx_dummy = 0u;
+    bool pf = false, pref_done = false;   // this split requests the next one's first tiles / was requested
+    auto split_tiles = [&](int ls) {
+        const int last = s_last[ls];
+        return __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / kTileTok + 1);
+    };
+    auto split_dummy = [&](int ls) {
+        const int last = s_last[ls];
+        return __builtin_amdgcn_readfirstlane(last < 0 ? 0u : phys[ls * kSplitSlots + s_first[ls]]);
+    };
     auto begin_split = [&](int ls) {
         cur = ls;
         cur_slot0 = ls * kSplitSlots;
-        const int last = s_last[ls];
-        ntiles = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / kTileTok + 1);
-        dummy = __builtin_amdgcn_readfirstlane(last < 0 ? 0u : phys[cur_slot0 + s_first[ls]]);
+        ntiles = split_tiles(ls);
+        dummy = split_dummy(ls);
+        nx_ntiles = ls + 1 < ns ? split_tiles(ls + 1) : 0;
+        nx_dummy = ls + 1 < ns ? split_dummy(ls + 1) : 0u;
+        pf = ntiles >= 2 && nx_ntiles >= 1;
     };
+    auto end_split = [&]() {
+        pref_done = pf;
+        sbase = (sbase + ntiles) % kStages;
+    };
+    auto stg = [&](int t) { return (sbase + t) % kStages; };
 
     // ---- A5: gather.  Load instruction i of a tile covers stage bytes 1024 i .. +1024; wave w issues
     // i = w, w + 16, w + 32 (those below the tile's count: 36 for bf16, 21 for FP8).  Lane l of
@@ -358,15 +377,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     };
     const uint32_t ring_lds = lds_offset(ring);
     const bool half_load = KV_FP8 && wid + kAttnWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
-    auto issue_tile = [&](int tile, int stage) {
-        const uint8_t* phys_tile = (const uint8_t*)(phys + cur_slot0 + tile * kTileTok);
+    auto issue_tile_of = [&](int slot0, uint32_t dmy, int tile, int stage) {
+        const uint8_t* phys_tile = (const uint8_t*)(phys + slot0 + tile * kTileTok);
         uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
         load_offsets(dtok, doff);
         const uint8_t* src[kMaxLoadsPerWave];
 #pragma unroll
         for (int r = 0; r < kMaxLoadsPerWave; ++r) {   // all slot reads first: the asm below is a compiler barrier
             uint32_t ph = *(const uint32_t*)(phys_tile + dtok[r]);
-            ph = ph == kNoToken ? dummy : ph;
+            ph = ph == kNoToken ? dmy : ph;
             src[r] = p.kv + (uint64_t)ph * kRecBytes + doff[r];
         }
         const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)wid;
@@ -385,6 +404,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 if (lane < kFp8TileChunks - kWave * (kFp8TileLoads - 1)) dma_b128(src[1], m0 + 1024u * kAttnWaves);
             }
         }
+    };
+    auto issue_tile = [&](int tile, int stage) { issue_tile_of(cur_slot0, dummy, tile, stage); };
+    // The request that would be tile `t` of this split (t >= ntiles) is tile t - ntiles of the next split.
+    auto issue_ahead = [&](int t) {
+        if (t < ntiles) issue_tile(t, stg(t));
+        else if (pf && t - ntiles < nx_ntiles) issue_tile_of(cur_slot0 + kSplitSlots, nx_dummy, t - ntiles, stg(t));
     };
     // bf16: zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
@@ -458,17 +483,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // tiles are requested and, for FP8, tile 0 is expanded.
     auto start_split = [&](int ls) {
         begin_split(ls);
-        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, t);
+        if (!pref_done)
+            for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, stg(t));
         if (KV_FP8 && ntiles > 0) {
-            if (ntiles > 1) {
+            if (ntiles > 1 && !pref_done) {   // tile 1 stays in flight
                 if (nload == 2) wait_vmcnt<2>();
                 else wait_vmcnt<1>();
-            } else {
+            } else {   // (requested by the previous split: the split's output stores may follow them)
                 wait_vmcnt<0>();
             }
             wait_lgkmcnt0();
             __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
-            dequant_tile(0, 0);
+            dequant_tile(0, stg(0));
         }
     };
 
@@ -480,9 +506,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
     //   the score waves expand tile it+1.
     auto tile_top = [&](int it) {
-        const int stage = it % kStages;
+        const int stage = stg(it);
         if (!KV_FP8) {
-            if (it + 1 < ntiles) {   // tile it+1 stays in flight
+            if (it == 0 && pref_done) {   // requested by the previous split: its output stores may follow
+                wait_vmcnt<0>();
+            } else if (it + 1 < ntiles || pf) {   // tile it+1 (or the next split's tile 0) stays in flight
                 if (nload == 3) wait_vmcnt<3>();
                 else wait_vmcnt<2>();
             } else {
@@ -492,19 +520,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (KV_FP8 && it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        if (KV_FP8) issue_ahead(it + kStages - 1);
         if (KV_FP8) return (const uint8_t*)btile_of(it);
         return (const uint8_t*)(ring + stage * kStageBytes);
     };
     // bf16: after the second barrier of tile it, the stage of tile it-1 (whose value product ends
     // before that barrier) receives tile it+2.
     auto issue_after_second = [&](int it) {
-        if (!KV_FP8 && it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+        if (!KV_FP8) issue_ahead(it + kStages - 1);
     };
     // FP8: before the third barrier of tile it, this wave's loads of tile it+1 have landed.
     auto wait_next_fp8 = [&](int it) {
         if (KV_FP8 && it + 1 < ntiles) {
-            if (it + 2 < ntiles) {   // tile it+2 stays in flight
+            if (it + 2 < ntiles || pf) {   // tile it+2 (or the next split's tile 0) stays in flight
                 if (nload == 2) wait_vmcnt<2>();
                 else wait_vmcnt<1>();
             } else {
@@ -645,7 +673,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             wait_next_fp8(it);
             wait_lgkmcnt0();
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);
+            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, stg(it + 1));
         }
         // ---- A10 (score waves): output multiplier and LSE of the first halves' heads.  With one
         // split the sink joins here: it adds e^sink to the denominator and nothing to the output.
@@ -681,6 +709,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 p.ws_lse[((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head] = lse_v;
             }
         }
+        end_split();
       }
     } else {
         f32x4_t oacc[4][4];                 // [head block][16-dim block of the wave's 64 dims]
@@ -769,7 +798,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             issue_after_second(it);
             wait_next_fp8(it);
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, (it + 1) % kStages);
+            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, stg(it + 1));
             sb_prev = sb;
         }
         if (ntiles > 0) value_product(ntiles - 1, sb_prev);
@@ -799,6 +828,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 }
             }
         }
+        end_split();
       }
     }
 }
@@ -911,7 +941,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     // which gathers the same records): a head's arithmetic does not depend on the heads it shares a
     // workgroup with, so the results are the same bits either way.
     int dev = 0, num_cu = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
     p.scale_log2 = a.softmax_scale * kLog2e;
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
