@@ -38,6 +38,15 @@ struct DirectScores {                 // a contiguous row
     __device__ __forceinline__ float at(int64_t j) const { return s[j]; }
     __device__ __forceinline__ int32_t index(int64_t j) const { return (int32_t)j; }
 };
+// Workgroup barrier that orders LDS accesses only.  Threads of a selecting workgroup share data
+// through LDS alone, so global loads still in flight (a row streaming into registers) need not be
+// waited for here; __syncthreads would wait for them, its fence covering global memory too.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Number of set bits of a wave mask below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -61,12 +70,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const uint32_t x = wave_inclusive_scan(v);
     if (lane == kWave - 1) scratch[wid] = x;
-    __syncthreads();
+    lds_barrier();
     const uint32_t w = lane < kTopkWaves ? scratch[lane] : 0u;
     const uint32_t z = wave_inclusive_scan(w);       // every wave scans the 16 wave totals itself
     const uint32_t before = __shfl(z - w, wid);       // exclusive prefix of this wave's total
     *total = __shfl(z, kTopkWaves - 1);
-    __syncthreads();
+    lds_barrier();
     return before + x - v;
 }
 
@@ -97,7 +106,7 @@ __device__ __forceinline__ void digit_histogram(const Src& src, int64_t L, uint3
     constexpr int kBins = 1 << BITS;
     constexpr int kShift = 32 - DEPTH - BITS;
     for (int i = threadIdx.x; i < kBins; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int64_t base = 0; base < L; base += kTopkChunk) {
         uint32_t key[kTopkUnroll];
         load_keys(src, L, base, key);
@@ -109,7 +118,7 @@ __device__ __forceinline__ void digit_histogram(const Src& src, int64_t L, uint3
             if (match) atomicAdd(&hist[(key[u] >> kShift) & (kBins - 1)], 1u);
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Finds the digit d holding the need-th largest candidate: above = #candidates with a larger digit,
@@ -138,7 +147,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
         }
         above += h[i];
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // LDS capacity of the filtered path.
@@ -255,10 +264,10 @@ struct TopkShared {
 __device__ __forceinline__ bool sample_threshold(const float* sv, int64_t L, int32_t n, uint32_t* hist,
                                                  uint32_t* scratch, uint32_t* res, float* tf) {
     for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i) atomicAdd(&hist[score_key(sv[i]) >> 20], 1u);
-    __syncthreads();
+    lds_barrier();
     const float expect = (float)n * (float)(1 << kSampleLog2) / (float)L;
     const uint32_t want = (uint32_t)(1.25f * expect + 4.f * sqrtf(expect) + 8.f);
     if (want >= (uint32_t)(1 << kSampleLog2)) return false;
@@ -300,7 +309,7 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
     uint32_t* cand_idx = sm.cand_idx;
     // ---- radix selection of the n-th key among the listed candidates ----
     for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
     const uint32_t c0 = threadIdx.x * per;
     const uint32_t c1 = c0 + per < total ? c0 + per : total;
@@ -309,27 +318,27 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
         cand_key[c] = key;
         atomicAdd(&hist[key >> 20], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     find_digit<12>(hist, (uint32_t)n, scratch, res);
     uint32_t p = res[0];
     uint32_t need = (uint32_t)n - res[1];
     int shift = 20;
     if (need != res[2]) {
         for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (uint32_t c = c0; c < c1; ++c)
             if ((cand_key[c] >> 20) == p) atomicAdd(&hist[(cand_key[c] >> 8) & 0xfffu], 1u);
-        __syncthreads();
+        lds_barrier();
         find_digit<12>(hist, need, scratch, res);
         p = (p << 12) | res[0];
         need -= res[1];
         shift = 8;
         if (need != res[2]) {
             for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0u;
-            __syncthreads();
+            lds_barrier();
             for (uint32_t c = c0; c < c1; ++c)
                 if ((cand_key[c] >> 8) == p) atomicAdd(&hist[cand_key[c] & 0xffu], 1u);
-            __syncthreads();
+            lds_barrier();
             find_digit<8>(hist, need, scratch, res);
             p = (p << 8) | res[0];
             need -= res[1];
@@ -411,12 +420,12 @@ __device__ __forceinline__ void select_general(const Src& src, int64_t L, int32_
             if (lane == 0)
                 tbl[u * kTopkWaves + wid] = ((uint32_t)__popcll(gtm[u]) << 16) | (uint32_t)__popcll(eqm[u]);
         }
-        __syncthreads();
+        lds_barrier();
         const uint32_t v = threadIdx.x < kTopkUnroll * kTopkWaves ? tbl[threadIdx.x] : 0u;
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan(v, scratch, &tot);   // (gt_before << 16) | eq_before
         if (threadIdx.x < kTopkUnroll * kTopkWaves) tbl[threadIdx.x] = ex;
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int u = 0; u < kTopkUnroll; ++u) {
             const int64_t j = base + (int64_t)u * kTopkThreads + threadIdx.x;
@@ -430,7 +439,7 @@ __device__ __forceinline__ void select_general(const Src& src, int64_t L, int32_
         }
         gt_run += tot >> 16;
         eq_run += tot & 0xffffu;
-        __syncthreads();
+        lds_barrier();
     }
     for (int i = n + threadIdx.x; i < k; i += kTopkThreads) o[i] = -1;
 }
@@ -492,12 +501,12 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
                     if (lane == 0) sm.wcnt[ch * kTopkWaves + wid] = c;
                 }
             }
-            __syncthreads();
+            lds_barrier();
             uint32_t total;
             const uint32_t mine = (int)threadIdx.x < nch * kTopkWaves ? sm.wcnt[threadIdx.x] : 0u;
             const uint32_t before = block_exclusive_scan(mine, sm.scratch, &total);
             if ((int)threadIdx.x < nch * kTopkWaves) sm.wcnt[threadIdx.x] = before;
-            __syncthreads();
+            lds_barrier();
             if (total >= (uint32_t)n && total <= (uint32_t)kCandCap) {   // uniform
                 if (resident) {
                     wave_append_ge<kResidentU, false>(v, L32, 0, tf, sm.wcnt[wid], sm.cand_key, sm.cand_idx);
@@ -509,12 +518,12 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
                                                        sm.cand_key, sm.cand_idx);
                     }
                 }
-                __syncthreads();
+                lds_barrier();
                 resolve_list(src, total, n, k, o, sm);
                 return;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     select_general(src, L, n, k, o, sm);
 }
@@ -589,11 +598,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* 
     }
     const uint32_t wc = wave_count_ge<kStreamU>(v, L32, base, tf);
     if (lane == 0) wcnt[wid] = wc;
-    __syncthreads();
+    lds_barrier();
     uint32_t total;
     const uint32_t before = block_exclusive_scan(threadIdx.x < kTopkWaves ? wcnt[threadIdx.x] : 0u, scratch, &total);
     if (threadIdx.x < kTopkWaves) wcnt[threadIdx.x] = before;
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) counts[c] = total;
     if (total > (uint32_t)kCandCap) return;   // uniform; the row's total is then out of range too
     uint32_t pos = wcnt[wid];
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
         const uint2* lists = (const uint2*)(rws + kSplitHeader);
         const int used = (int)((L + kStreamChunk - 1) / kStreamChunk);   // chunks the filter kernel ran
         if ((int)threadIdx.x < used) sm.wcnt[threadIdx.x] = counts[threadIdx.x];
-        __syncthreads();
+        lds_barrier();
         uint32_t total = 0;
         bool ok = true;
         for (int c = 0; c < used; ++c) {
@@ -647,11 +656,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
                 }
                 off += cc;
             }
-            __syncthreads();
+            lds_barrier();
             resolve_list(src, total, n, k, o, sm);
             return;
         }
-        __syncthreads();
+        lds_barrier();
         select_general(src, L, n, k, o, sm);
         return;
     }
