@@ -197,3 +197,24 @@ def test_scores_feed_the_selector():
     torch.cuda.synchronize()
     ref = O.topk_rows(scores.cpu().numpy(), wl.lengths.cpu().numpy(), 2048)
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+def test_rows_sharing_a_request():
+    """Several query rows of one request (MTP-style: each with its own causal length) read the same
+    block-table row; each equals the oracle and the same row computed alone."""
+    log("indexer rows sharing a request")
+    Hi, stride = 64, 2048
+    q, w, kidx, bt, _ = _workload(Hi, [2000, 1500], stride, seed=25)
+    row_req = torch.tensor([0, 0, 0, 1, 1], dtype=torch.int32, device=DEV)
+    lengths = torch.tensor([1997, 1998, 1999, 1400, 1500], dtype=torch.int32, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(26)
+    q5, w5 = W.indexer_queries(5, Hi, g, DEV)
+    out = smla.paged_mqa_logits(q5, w5, kidx, bt, lengths=lengths, row_req=row_req, out_stride=stride)
+    torch.cuda.synchronize()
+    ref, mag = _oracle(q5, w5, kidx, bt, row_req, lengths, stride)
+    _assert_close(out.cpu().numpy(), ref, mag, "rows sharing a request")
+    for r in range(5):
+        alone = smla.paged_mqa_logits(q5[r:r + 1], w5[r:r + 1], kidx, bt, lengths=lengths[r:r + 1],
+                                      row_req=row_req[r:r + 1], out_stride=stride)
+        assert bits_equal(alone[0], out[r]), r
