@@ -152,15 +152,8 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
 
 // LDS capacity of the filtered path.
 constexpr int kCandCap = 12288;      // candidates passing the filter, resolved in LDS
+static_assert(kCandCap < (1 << 16), "the emission scan packs two list counts into 16 bits each");
 constexpr int kSampleLog2 = 12;      // 4096 sampled candidates, 4 per thread
-
-// Block-wide exclusive scan of a 64-bit value (two 32-bit scans).
-__device__ __forceinline__ uint64_t block_exclusive_scan64(uint32_t a, uint32_t b, uint32_t* scratch, uint32_t* ta,
-                                                           uint32_t* tb) {
-    const uint32_t ea = block_exclusive_scan(a, scratch, ta);
-    const uint32_t eb = block_exclusive_scan(b, scratch, tb);
-    return ((uint64_t)ea << 32) | eb;
-}
 
 // The smallest value whose key has top-12 digit d (d >= 8): for every non-NaN v, v >= value <=>
 // score_key(v) >= d << 20.  Digits below 8 hold only -inf and NaN keys and have no such value.
@@ -354,9 +347,10 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
         ng += hi > p ? 1u : 0u;
         ne += hi == p ? 1u : 0u;
     }
-    uint32_t tg, te;
-    const uint64_t ex = block_exclusive_scan64(ng, ne, scratch, &tg, &te);
-    uint32_t gb = (uint32_t)(ex >> 32), eb = (uint32_t)ex;
+    // one scan of both counts, packed (list totals stay below 2^16: kCandCap = 12288)
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan((ng << 16) | ne, scratch, &tot);
+    uint32_t gb = ex >> 16, eb = ex & 0xffffu;
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t hi = cand_key[c] >> shift;
         uint32_t dst = 0xffffffffu;
