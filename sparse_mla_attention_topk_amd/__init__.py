@@ -225,8 +225,8 @@ def topk_workspace(rows: int, k: int, row_stride: int, device) -> Optional[torch
 
 
 def attention_workspace(rows: int, H: int, k: int, device, kv_dtype: int = KV_BF16) -> Optional[torch.Tensor]:
-    """A zeroed workspace big enough for `rows` rows in one launch (None if k needs none).  The
-    library keeps its arrival counters at zero between calls, so it can be reused as is."""
+    """A workspace big enough for `rows` rows in one launch (None if k needs none).  Its contents
+    on entry do not matter."""
     _, nbytes = workspace_size(Capacity.make(max(1, rows), k, H, 1, kv_dtype=kv_dtype))
     if nbytes == 0:
         return None
