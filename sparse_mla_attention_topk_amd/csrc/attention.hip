@@ -345,14 +345,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     };
     auto stg = [&](int t) { return (sbase + t) % kStages; };
 
-    // ---- A5: gather.  Load instruction i of a tile covers stage bytes 1024 i .. +1024; wave w issues
-    // i = w, w + 16, w + 32 (those below the tile's count: 36 for bf16, 21 for FP8).  Lane l of
-    // instruction i moves 16-byte chunk Q = 64 i + l of the stage.  bf16: token t = Q / 72 at 16-byte
-    // position Q % 72, which holds the record's chunk position ^ f(t).  FP8: token t = Q / 41, chunk
-    // Q % 41 in place; chunks past the tile (Q >= 1312, lanes 32..63 of load 20) are not loaded.
+    // ---- A5: gather.  Load instruction i of a tile covers stage bytes 1024 i .. +1024.  bf16: all 16
+    // waves load, wave w issues i = w, w + 16, w + 32 (below 36).  FP8: the 8 value waves load (after
+    // the second barrier, while the score waves run the softmax), value wave v issues i = v, v + 8,
+    // v + 16 (below 21).  Lane l of instruction i moves 16-byte chunk Q = 64 i + l of the stage.
+    // bf16: token t = Q / 72 at 16-byte position Q % 72, which holds the record's chunk position ^ f(t).
+    // FP8: token t = Q / 41, chunk Q % 41 in place; chunks past the tile (Q >= 1312, lanes 32..63 of
+    // load 20) are not loaded.
     constexpr int kLoads = KV_FP8 ? kFp8TileLoads : kTileLoads;
-    const int nload = (wid < kLoads ? 1 : 0) + (wid + kAttnWaves < kLoads ? 1 : 0) +
-                      (wid + 2 * kAttnWaves < kLoads ? 1 : 0);   // loads of this wave per tile (uniform)
+    constexpr int kLoadWaves = KV_FP8 ? kAttnWaves - kScoreWaves : kAttnWaves;
+    static_assert(kLoads <= kMaxLoadsPerWave * kLoadWaves, "loads per wave");
+    const int lw = KV_FP8 ? wid - kScoreWaves : wid;   // loading wave index (FP8 score waves: < 0)
+    const int nload = (KV_FP8 && lw < 0) ? 0
+                             : (lw < kLoads ? 1 : 0) + (lw + kLoadWaves < kLoads ? 1 : 0) +
+                                   (lw + 2 * kLoadWaves < kLoads ? 1 : 0);   // loads of this wave per tile (uniform)
     // Per-lane offsets of load r: the token's slot (4 bytes each) and the chunk's byte offset in the
     // record.  Recomputed at every issue from an opaque copy of the lane id, so that they are not held
     // in registers across the tile loop.
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int r = 0; r < kMaxLoadsPerWave; ++r) {
-            const int i = wid + kAttnWaves * r;
+            const int i = lw + kLoadWaves * r;
             const int qd = kWave * (i < kLoads ? i : 0) + ln;
             if (KV_FP8) {
                 const int qc = qd < kFp8TileChunks ? qd : kFp8TileChunks - 1;
@@ -376,8 +382,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
     };
     const uint32_t ring_lds = lds_offset(ring);
-    const bool half_load = KV_FP8 && wid + kAttnWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
+    const bool half_load = KV_FP8 && lw + kLoadWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
     auto issue_tile_of = [&](int slot0, uint32_t dmy, int tile, int stage) {
+        if (KV_FP8 && nload == 0) return;
         const uint8_t* phys_tile = (const uint8_t*)(phys + slot0 + tile * kTileTok);
         uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
         load_offsets(dtok, doff);
@@ -388,20 +395,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             ph = ph == kNoToken ? dmy : ph;
             src[r] = p.kv + (uint64_t)ph * kRecBytes + doff[r];
         }
-        const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)wid;
+        const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)lw;
         if (!KV_FP8) {
             dma_b128(src[0], m0);
             dma_b128(src[1], m0 + 1024u * kAttnWaves);
             if (nload == 3) dma_b128(src[2], m0 + 2048u * kAttnWaves);
-        } else {
-            if (nload == 1) {
-                dma_b128(src[0], m0);
-            } else if (!half_load) {
-                dma_b128(src[0], m0);
-                dma_b128(src[1], m0 + 1024u * kAttnWaves);
-            } else {
-                dma_b128(src[0], m0);
-                if (lane < kFp8TileChunks - kWave * (kFp8TileLoads - 1)) dma_b128(src[1], m0 + 1024u * kAttnWaves);
+        } else {   // value waves 0..4: 3 loads (the third of wave 4 is the 32-lane load), 5..7: 2
+            dma_b128(src[0], m0);
+            dma_b128(src[1], m0 + 1024u * kLoadWaves);
+            if (nload == 3) {
+                if (!half_load) dma_b128(src[2], m0 + 2048u * kLoadWaves);
+                else if (lane < kFp8TileChunks - kWave * (kFp8TileLoads - 1))
+                    dma_b128(src[2], m0 + 2048u * kLoadWaves);
             }
         }
     };
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
             for (int r = 0; r < kMaxLoadsPerWave; ++r) {
                 if (r < nload) {
-                    const int qd = kWave * (wid + kAttnWaves * r) + lane;
+                    const int qd = kWave * (lw + kLoadWaves * r) + lane;
                     if (!((vm >> (qd / 72)) & 1u)) *(uint4*)(sbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
                 }
             }
@@ -486,10 +491,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         if (!pref_done)
             for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, stg(t));
         if (KV_FP8 && ntiles > 0) {
-            if (ntiles > 1 && !pref_done) {   // tile 1 stays in flight
-                if (nload == 2) wait_vmcnt<2>();
-                else wait_vmcnt<1>();
-            } else {   // (requested by the previous split: the split's output stores may follow them)
+            if (ntiles > 1 && !pref_done) {   // tile 1 stays in flight (score waves load nothing)
+                if (nload == 3) wait_vmcnt<3>();
+                else if (nload == 2) wait_vmcnt<2>();
+            } else if (nload > 0) {   // (requested by the previous split: the split's output stores may follow them)
                 wait_vmcnt<0>();
             }
             wait_lgkmcnt0();
@@ -502,9 +507,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // bf16: wait for this wave's loads of the tile, zero its invalid chunks and make the tile visible
     //   (first barrier); tile it+1 stays in flight.
     // FP8: the tile was expanded into expansion buffer it % 2 after the third barrier of tile it-1 (or
-    //   before the loop); the first barrier makes it visible, then the load of tile it+2 starts.
-    //   Each wave waits for its loads of tile it+1 before the third barrier of tile it, after which
-    //   the score waves expand tile it+1.
+    //   before the loop); the first barrier makes it visible.  The value waves request tile it+2 after
+    //   the second barrier of tile it and wait for their loads of tile it+1 before the third, after
+    //   which all waves expand tile it+1.
     auto tile_top = [&](int it) {
         const int stage = stg(it);
         if (!KV_FP8) {
@@ -520,21 +525,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (KV_FP8) issue_ahead(it + kStages - 1);
         if (KV_FP8) return (const uint8_t*)btile_of(it);
         return (const uint8_t*)(ring + stage * kStageBytes);
     };
-    // bf16: after the second barrier of tile it, the stage of tile it-1 (whose value product ends
-    // before that barrier) receives tile it+2.
-    auto issue_after_second = [&](int it) {
-        if (!KV_FP8) issue_ahead(it + kStages - 1);
-    };
-    // FP8: before the third barrier of tile it, this wave's loads of tile it+1 have landed.
+    // After the second barrier of tile it, the stage of tile it-1 receives tile it+2: bf16, its value
+    // product ends before that barrier; FP8, it was expanded before the first barrier of tile it.
+    auto issue_after_second = [&](int it) { issue_ahead(it + kStages - 1); };
+    // FP8: before the third barrier of tile it, this (value) wave's loads of tile it+1 have landed.
     auto wait_next_fp8 = [&](int it) {
-        if (KV_FP8 && it + 1 < ntiles) {
+        if (KV_FP8 && nload > 0 && it + 1 < ntiles) {
             if (it + 2 < ntiles || pf) {   // tile it+2 (or the next split's tile 0) stays in flight
-                if (nload == 2) wait_vmcnt<2>();
-                else wait_vmcnt<1>();
+                if (nload == 3) wait_vmcnt<3>();
+                else wait_vmcnt<2>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -808,7 +810,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int b = 0; b < 4; ++b) {
             if (b >= nhb) break;
             const float inv = xmul[b][lane & 15];
-            const int head = head0 + 16 * b + (lane & 15);
+            int head = head0 + 16 * b + (lane & 15);
+            if (KV_FP8) asm volatile("" : "+v"(head));   // FP8: addresses computed per split (not held across splits)
             const int64_t pidx = (((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head) * kDv + vdim0 + 4 * g;
             if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
                 float* wo = (float*)p.ws_o + pidx;
