@@ -443,27 +443,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         // scratch memory, whose wait would also wait for the tile loads in flight).
         int u = tid;
         asm volatile("" : "+v"(u));   // recompute the unit's offsets per tile (not held across the loop)
-        {
-            const int t = u >> 5, c = u & 31;
-            const uint32_t keep = 0u - ((vm >> t) & 1u);
-            const int f = swz_key(t);
-            const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
-            if ((c & 7) == 0) tscale[tile & 1][t][c >> 3] = keep ? *(const float*)(st + t * kFp8Record + 512 + 4 * (c >> 3)) : 0.f;
-            uint8_t* dst = btile + t * kBf16Record;
-            // codes 0..7 of the chunk -> fp16 chunk 2c, codes 8..15 -> fp16 chunk 2c+1; the conversion
-            // with scale 1.0 is exact
-            *(uint4*)(dst + 16 * ((2 * c) ^ f)) =
-                make_uint4(fp8x2_to_f16x2<false>(codes.x) & keep, fp8x2_to_f16x2<true>(codes.x) & keep,
-                           fp8x2_to_f16x2<false>(codes.y) & keep, fp8x2_to_f16x2<true>(codes.y) & keep);
-            *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
-                make_uint4(fp8x2_to_f16x2<false>(codes.z) & keep, fp8x2_to_f16x2<true>(codes.z) & keep,
-                           fp8x2_to_f16x2<false>(codes.w) & keep, fp8x2_to_f16x2<true>(codes.w) & keep);
-        }
+        const int t = u >> 5, c = u & 31;
+        const int rt = (u & (kTileTok * 8 - 1)) >> 3, j = u & 7;   // rope unit (threads below 256 store it)
+        // Every LDS read is issued before any store and waited for once: the codes, the scale of the
+        // unit's group and a rope chunk (the last two read by every thread, stored by some).
+        const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
+        const uint32_t scale = *(const uint32_t*)(st + t * kFp8Record + 512 + 4 * (c >> 3));
+        uint4 r = *(const uint4*)(st + rt * kFp8Record + 528 + 16 * j);
+        const uint32_t keep = 0u - ((vm >> t) & 1u);
+        const int f = swz_key(t);
+        uint8_t* dst = btile + t * kBf16Record;
+        // codes 0..7 of the chunk -> fp16 chunk 2c, codes 8..15 -> fp16 chunk 2c+1; the conversion
+        // with scale 1.0 is exact
+        *(uint4*)(dst + 16 * ((2 * c) ^ f)) =
+            make_uint4(fp8x2_to_f16x2<false>(codes.x) & keep, fp8x2_to_f16x2<true>(codes.x) & keep,
+                       fp8x2_to_f16x2<false>(codes.y) & keep, fp8x2_to_f16x2<true>(codes.y) & keep);
+        *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
+            make_uint4(fp8x2_to_f16x2<false>(codes.z) & keep, fp8x2_to_f16x2<true>(codes.z) & keep,
+                       fp8x2_to_f16x2<false>(codes.w) & keep, fp8x2_to_f16x2<true>(codes.w) & keep);
+        if ((c & 7) == 0) tscale[tile & 1][t][c >> 3] = __uint_as_float(scale & keep);   // +0 when invalid
         if (u < kTileTok * 8) {
-            const int rt = u >> 3, j = u & 7;
-            const uint32_t keep = 0u - ((vm >> rt) & 1u);
-            uint4 r = *(const uint4*)(st + rt * kFp8Record + 528 + 16 * j);
-            r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
+            const uint32_t rkeep = 0u - ((vm >> rt) & 1u);
+            r.x &= rkeep; r.y &= rkeep; r.z &= rkeep; r.w &= rkeep;
             *(uint4*)(btile + rt * kBf16Record + 16 * ((64 + j) ^ swz_key(rt))) = r;
         }
     };
