@@ -15,7 +15,9 @@
 // to LDS with global_load_lds_dwordx4) is spread over all 16 waves: the rate at which random records
 // arrive grows with the number of waves per CU issuing loads, measured on MI355X.  Records are stored
 // unpadded (1152 B); the 16-byte chunks of tile-local token t are XOR-swizzled with f(t) = (t >> 1) & 7,
-// the mapping measured to keep the operand reads below free of LDS bank conflicts on gfx950.
+// the mapping measured to keep the operand reads below free of LDS bank conflicts on gfx950.  FP8
+// caches: a tile is 21 loads of 656-B records, issued by the 8 value waves alone in a phase where
+// they would otherwise wait; all 16 waves then expand it into an fp16 tile of the layout above.
 //
 // Roles (at most 128 registers per wave at 16 waves per CU):
 //   score waves 0..7:  wave (hb, half) computes the partial scores of heads hb*16 .. +16 over dims
@@ -37,8 +39,8 @@
 // combine kernel merges the splits of a row in split order.  Nothing uses floating-point atomics.
 //
 // Invalid slots (index < 0, request/page out of range) load a valid dummy record, are zeroed in
-// LDS after arrival and get score -inf, so every wave issues the same number of direct-to-LDS loads
-// for every tile and the vmcnt bookkeeping below stays exact.
+// LDS after arrival and get score -inf, so every loading wave issues the same number of direct-to-LDS
+// loads for every tile and the vmcnt bookkeeping below stays exact.
 #include <math.h>
 
 #include <type_traits>
