@@ -51,6 +51,7 @@ def parse():
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_bf16_B64_H64_k2048_hbm_traffic.md")
 INDEXER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "indexer_B64_Hi64_L8K-64K_hbm_traffic.md")
+FP8_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_fp8_B128_H64_k2048_hbm_traffic.md")
 
 
 def measured_traffic(record=TRAFFIC_RECORD):
@@ -497,7 +498,7 @@ def main():
         "step_gathered_kv_GBps": gathered / (ms_step * 1e-3) / 1e9,
         "attention_ms": attn_ms, "topk_ms": topk_ms, "wall_s": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None if fp8 else measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(FP8_TRAFFIC_RECORD if fp8 else TRAFFIC_RECORD),
                      "kernel": "sparse_mla_decode call: attention kernel + split-combine kernel",
                      "algorithmic_bytes_per_launch": gathered,
                      "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12},
