@@ -139,9 +139,9 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
  *   K_j[0:512] rounded to bf16 (RNE); lse[r,h] = ln D (fp32).  Without a sink (sink NULL, or
  *   sink[h] = -inf) the e^{sink} term is absent and p is the plain softmax.  A row with no valid
  *   token gets out = 0 and lse = sink[h] (-inf without a sink).  Slots are reduced in a fixed order
- *   that depends only on k: the k slots are cut into ceil(k/512) splits, each split accumulates its
- *   tiles in slot order with an fp32 online softmax, the splits are combined in split order, and
- *   the sink term comes last.
+ *   that depends only on k and kv_dtype: the k slots are cut into splits of 512 slots (FP8 caches:
+ *   1024), each split accumulates its tiles in slot order with an fp32 online softmax, the splits
+ *   are combined in split order, and the sink term comes last.
  *   sink:   fp32 [H] per-head attention-sink logits, in the units of the scaled scores, or NULL
  *           ("[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", section "MHC, CUDA
  *           graphs, and weight reload": sink weights keep -inf padding, i.e. -inf = no sink);
@@ -149,7 +149,8 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
  *   out: bf16 [rows, H, 512], 16-byte aligned; lse: fp32 [rows, H] or NULL.
  *   ws: attention workspace (256-byte aligned) of at least the size smla_workspace_size reports for
  *   a capacity with max_rows >= 1; rows beyond what it holds are processed in further launches.
- *   It holds the bf16 split partials and their fp32 LSEs (k > 512 only); calls that share a
+ *   It holds the split partials (bf16; FP8 caches: fp32) and their fp32 LSEs (only with more than
+ *   one split); calls that share a
  *   workspace must be ordered on one stream.
  * Requires H a multiple of 16 in [16, 128], 1 <= k <= 16384, rows >= 0, num_pages >= 1. */
 smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,

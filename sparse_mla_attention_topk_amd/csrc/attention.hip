@@ -9,8 +9,9 @@
 // for the tokens j listed in the row's index slots (entries < 0 skipped).
 //
 // Work decomposition.  One workgroup of 16 waves owns one (row, split, 64-head block) and is the only
-// workgroup on its CU.  A split is 512 consecutive index slots; the number of splits depends on k
-// only, so the reduction order of a row never depends on the batch.  The split's slots are processed
+// workgroup on its CU.  A split is 512 consecutive index slots (FP8 caches: 1024, two units of 512
+// run one after the other with one softmax state); the number of splits depends on k and the cache
+// type only, so the reduction order of a row never depends on the batch.  The split's slots are processed
 // in tiles of 32 tokens through a 3-stage LDS ring.  The gather of a tile (36 loads of 1 KB, direct
 // to LDS with global_load_lds_dwordx4) is spread over all 16 waves: the rate at which random records
 // arrive grows with the number of waves per CU issuing loads, measured on MI355X.  Records are stored
@@ -87,10 +88,11 @@ struct AttnParams {
     const int32_t* idx;
     int32_t k;
     int32_t H;
-    int32_t n_splits;
+    int32_t n_splits;       // splits of a row (one softmax state and one partial each)
+    int32_t n_units;        // 512-slot units of a row (a split is 1 unit, FP8: 2)
     int32_t n_hblocks;
     int32_t heads_per_wg;   // 64, 32 or 16: heads of one workgroup (each head's arithmetic is the same)
-    int32_t splits_per_wg;  // 1, 2 or 4 consecutive splits of a row run by one workgroup, one after the other
+    int32_t units_per_wg;   // 1, 2 or 4 consecutive units of a row run by one workgroup, one after the other
     float scale_log2;
     int32_t row0;
     uint16_t* out;
@@ -206,9 +208,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     const int item = xcd * per + (xcd < rem ? xcd : rem) + local;
     const int hb_item = item % p.n_hblocks;
     const int rs = item / p.n_hblocks;
-    const int n_groups = (p.n_splits + p.splits_per_wg - 1) / p.splits_per_wg;
-    const int split0 = (rs % n_groups) * p.splits_per_wg;      // first split of this workgroup
-    const int ns = min(p.splits_per_wg, p.n_splits - split0);  // its splits split0 .. split0 + ns - 1
+    // A workgroup runs units split0 .. split0 + ns - 1 of its row.  bf16: each unit is a split; FP8:
+    // units 2s and 2s + 1 form split s, one softmax state over both (the launch gives FP8 workgroups
+    // whole splits).
+    constexpr int kUnitsPerSplit = KV_FP8 ? kFp8UnitsPerSplit : 1;
+    const int n_groups = (p.n_units + p.units_per_wg - 1) / p.units_per_wg;
+    const int split0 = (rs % n_groups) * p.units_per_wg;      // first unit of this workgroup
+    const int ns = min(p.units_per_wg, p.n_units - split0);  // its units split0 .. split0 + ns - 1
     const int rloc = rs / n_groups;
     const int64_t row = (int64_t)p.row0 + rloc;
     const int head0 = hb_item * p.heads_per_wg;
@@ -550,11 +556,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // one role (Q, the score accumulators) and of the other (the output accumulators) can share storage.
     float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
     if (is_score) {
-      // The group's splits one after the other; each starts from a fresh softmax state.
+      // The group's units one after the other; each split starts from a fresh softmax state.
       for (int ls = 0; ls < ns; ++ls) {
         start_split(ls);
-        m_run = -INFINITY;
-        l_run = 0.f;
+        const int su = split0 + ls;   // unit of the row
+        if (su % kUnitsPerSplit == 0) {
+            m_run = -INFINITY;
+            l_run = 0.f;
+        }
         for (int it = 0; it < ntiles; ++it) {
             const uint8_t* sb = tile_top(it);
             // ---- A7: partial scores over this wave's half of the dims ----
@@ -680,9 +689,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
             if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, stg(it + 1));
         }
-        // ---- A10 (score waves): output multiplier and LSE of the first halves' heads.  With one
-        // split the sink joins here: it adds e^sink to the denominator and nothing to the output.
-        // With several splits the split results exclude it and the combine adds it last. ----
+        // ---- A10 (score waves), after the split's last unit: output multiplier and LSE of the first
+        // halves' heads.  With one split the sink joins here: it adds e^sink to the denominator and
+        // nothing to the output.  With several splits the split results exclude it and the combine adds
+        // it last. ----
+        if (ls == ns - 1 || su % kUnitsPerSplit == kUnitsPerSplit - 1) {
         const float l_tot = head_sum(l_run);
         float mult = 0.f, lse_v = -INFINITY;
         if (score_ok && !half && lane < 16) {
@@ -711,8 +722,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             if (p.n_splits == 1) {
                 if (p.lse) p.lse[row * p.H + head] = lse_v;
             } else {
-                p.ws_lse[((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head] = lse_v;
+                p.ws_lse[((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head] = lse_v;
             }
+        }
         }
         end_split();
       }
@@ -790,10 +802,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         // tile it+1, its 1152-byte tile (the ring stage, or the FP8 expansion buffer) only after that too.
       for (int ls = 0; ls < ns; ++ls) {
         start_split(ls);
+        const int su = split0 + ls;   // unit of the row
+        if (su % kUnitsPerSplit == 0) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        }
         const uint8_t* sb_prev = nullptr;
         for (int it = 0; it < ntiles; ++it) {
             const uint8_t* sb = tile_top(it);
@@ -807,7 +822,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             sb_prev = sb;
         }
         if (ntiles > 0) value_product(ntiles - 1, sb_prev);
-        // ---- A10 (value waves): wait for the weight sums, normalize and write ----
+        // ---- A10 (value waves), after the split's last unit: wait for the weight sums, normalize and
+        // write ----
+        if (ls == ns - 1 || su % kUnitsPerSplit == kUnitsPerSplit - 1) {
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -815,7 +832,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             const float inv = xmul[b][lane & 15];
             int head = head0 + 16 * b + (lane & 15);
             if (KV_FP8) asm volatile("" : "+v"(head));   // FP8: addresses computed per split (not held across splits)
-            const int64_t pidx = (((int64_t)rloc * p.n_splits + split0 + ls) * p.H + head) * kDv + vdim0 + 4 * g;
+            const int64_t pidx = (((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head) * kDv + vdim0 + 4 * g;
             if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
                 float* wo = (float*)p.ws_o + pidx;
 #pragma unroll
@@ -833,6 +850,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     *(uint2*)(orow + 16 * d) = w;
                 }
             }
+        }
         }
         end_split();
       }
@@ -942,7 +960,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.idx = a.idx;
     p.k = a.k;
     p.H = a.H;
-    p.n_splits = attn_num_splits(a.k);
+    p.n_splits = attn_num_splits(a.k, a.kv_dtype);
+    p.n_units = attn_num_units(a.k);
     // Launches with fewer (row, split) items than CUs split the heads over 2 or 4 workgroups (each of
     // which gathers the same records): a head's arithmetic does not depend on the heads it shares a
     // workgroup with, so the results are the same bits either way.
@@ -968,20 +987,25 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch *
                                                                attn_ws_o_bytes_per_row(a.H, a.k, a.kv_dtype))
                                : nullptr;
-        // Launches with at least twice as many (row, split) items as CUs run 2 or 4 consecutive splits of a
-        // row per workgroup (FP8: 2), one after the other: the index translation and Q serve them all.
-        // Each split reduces its own tiles in order with its own softmax state, so the bits are the same.
+        // bf16: launches with at least twice as many (row, split) items as CUs run 2 or 4 consecutive
+        // splits of a row per workgroup, one after the other: the index translation and Q serve them
+        // all.  Each split reduces its own tiles in order with its own softmax state, so the bits are the
+        // same.  FP8: a workgroup runs one whole split (its 2 units) in every launch.
         p.heads_per_wg = kHeadsPerBlock;
         const int hb64 = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
-        const int max_group = fp8 ? 2 : 4;
-        p.splits_per_wg = 1;
-        while (2 * p.splits_per_wg <= max_group && 2 * p.splits_per_wg <= p.n_splits &&
-               (int64_t)n * ((p.n_splits + 2 * p.splits_per_wg - 1) / (2 * p.splits_per_wg)) * hb64 >= num_cu)
-            p.splits_per_wg *= 2;
-        while (p.heads_per_wg > 16 && (int64_t)n * p.n_splits * ((a.H + p.heads_per_wg - 1) / p.heads_per_wg) < num_cu)
+        if (fp8) {
+            p.units_per_wg = min(kFp8UnitsPerSplit, p.n_units);
+        } else {
+            p.units_per_wg = 1;
+            while (2 * p.units_per_wg <= 4 && 2 * p.units_per_wg <= p.n_units &&
+                   (int64_t)n * ((p.n_units + 2 * p.units_per_wg - 1) / (2 * p.units_per_wg)) * hb64 >= num_cu)
+                p.units_per_wg *= 2;
+        }
+        const int groups = (p.n_units + p.units_per_wg - 1) / p.units_per_wg;
+        while (p.heads_per_wg > 16 && (int64_t)n * groups * ((a.H + p.heads_per_wg - 1) / p.heads_per_wg) < num_cu)
             p.heads_per_wg /= 2;
         p.n_hblocks = (a.H + p.heads_per_wg - 1) / p.heads_per_wg;
-        const int grid = n * ((p.n_splits + p.splits_per_wg - 1) / p.splits_per_wg) * p.n_hblocks;
+        const int grid = n * groups * p.n_hblocks;
         if (fp8) hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         else hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream, p);
         hipError_t e = hipGetLastError();

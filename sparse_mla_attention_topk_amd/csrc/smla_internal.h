@@ -8,21 +8,31 @@
 namespace smla {
 
 // Geometry of the attention kernels (also used by the host to size workspaces).
-constexpr int kSplitSlots = 512;   // index slots reduced by one workgroup before the split combine
+constexpr int kSplitSlots = 512;   // index slots of one unit: one pass of the tile loop
 constexpr int kHeadsPerBlock = 64; // heads handled by one workgroup (4 waves x 16)
+constexpr int kFp8UnitsPerSplit = 2;   // FP8 caches: a split (one softmax state, one partial) is 2 units
 
-inline int attn_num_splits(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
+inline int attn_num_units(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
+// Splits of a row, each reduced by one workgroup before the split combine: units of 512 slots (bf16
+// caches) or pairs of them (FP8 caches, whose fp32 partials cost twice the bytes).  A function of k and
+// the cache type only, never of the batch.
+inline int attn_num_splits(int k, int kv_dtype) {
+    const int u = attn_num_units(k);
+    return kv_dtype == 1 ? (u + kFp8UnitsPerSplit - 1) / kFp8UnitsPerSplit : u;
+}
 
 // Workspace of the attention entry points, per query row (0 when k fits one split): the partial
 // outputs of every (split, head) -- bf16 for bf16 caches, fp32 for FP8 caches, whose group scales
 // make outputs large enough that bf16 partials would cost visible accuracy -- then their fp32 LSEs.
 inline size_t attn_ws_o_bytes_per_row(int H, int k, int kv_dtype) {
-    return (size_t)attn_num_splits(k) * H * 512 * (kv_dtype == 1 ? 4 : 2);
+    return (size_t)attn_num_splits(k, kv_dtype) * H * 512 * (kv_dtype == 1 ? 4 : 2);
 }
-inline size_t attn_ws_lse_bytes_per_row(int H, int k) { return (size_t)attn_num_splits(k) * H * 4; }
+inline size_t attn_ws_lse_bytes_per_row(int H, int k, int kv_dtype) {
+    return (size_t)attn_num_splits(k, kv_dtype) * H * 4;
+}
 inline size_t attn_ws_bytes_per_row(int H, int k, int kv_dtype) {
-    if (attn_num_splits(k) <= 1) return 0;
-    return attn_ws_o_bytes_per_row(H, k, kv_dtype) + attn_ws_lse_bytes_per_row(H, k);
+    if (attn_num_splits(k, kv_dtype) <= 1) return 0;
+    return attn_ws_o_bytes_per_row(H, k, kv_dtype) + attn_ws_lse_bytes_per_row(H, k, kv_dtype);
 }
 
 struct AttnArgs {
