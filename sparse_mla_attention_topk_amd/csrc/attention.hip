@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
     constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
-    // Splits run by one workgroup (FP8: at most 2, for LDS) and their slots' physical records.
+    // Units run by one workgroup (FP8: the 2 units of its split) and their slots' physical records.
     constexpr int kMaxGroup = KV_FP8 ? 2 : 4;
     __shared__ uint32_t phys[kMaxGroup * kSplitSlots];
     __shared__ uint32_t tile_valid[kMaxGroup * kTilesPerSplit];
