@@ -55,10 +55,18 @@ design notes):
   entry d is e4m3(code_d) * scale_{d // 128}; e4m3 is the OCP E4M3FN format;
 * the cache write quantizes group g of a token's 512 latent values so that
   the group's largest magnitude amax maps to 448: the stored fp32 scale is
-  s = amax / 448 and the codes are e4m3(x * r) with the fp32 multiplier
-  r = 448 / amax (each division and the product rounded to nearest-even in
-  fp32; the code rounded to nearest-even and saturated at +-448); an all-zero
-  group gets s = 0 and zero codes; the 64 rope values are stored unchanged;
+  s = amax / 448 and the codes are e4m3(x / s), the inverse of the
+  dequantization, which multiplies a code by s (each division rounded to
+  nearest-even in fp32; the code rounded to nearest-even and saturated at
+  +-448); an all-zero group gets s = 0 and zero codes;
+* the cache write's "inverse-RoPE" ("Port DeepSeek-V4 optimization PR #174
+  ...", table "Optimizations carried from PR #174", row "Attention cache
+  write") undoes the rotary embedding of the 64 rope values before they are
+  stored: with the caller's tables cos[pos, i], sin[pos, i] (i < 32, fp32)
+  and the pairs (x_2i, x_2i+1), the stored pair is
+  (x_2i cos + x_2i+1 sin, -x_2i sin + x_2i+1 cos), evaluated exactly and
+  rounded to bf16 once (nearest-even); without tables the rope values are
+  stored unchanged; the rope inputs must be finite;
 * indexer scores ("MQA logits" of the DSA indexer: the pages name the operation and its
   paged form -- "[SM120] Sync DS4 with upstream main + validated perf backports", sections
   "September 12 follow-up" and "2026-09-12 live validation and promotion update" -- but give
@@ -71,6 +79,7 @@ design notes):
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -150,24 +159,71 @@ def f32_to_e4m3fn(x) -> np.ndarray:
 
 def quantize_group(x_bits: np.ndarray) -> Tuple[np.ndarray, np.float32]:
     """One 128-entry scale group of bf16 latent values -> (e4m3 codes [128], fp32 scale).
-    s = fp32(amax / 448), r = fp32(448 / amax), codes = e4m3(fp32(x * r)); an all-zero group has
-    s = 0, codes 0."""
+    s = fp32(amax / 448), codes = e4m3(fp32(x / s)): the dequantization multiplies a code by s,
+    so the quantization divides by it.  An all-zero group has s = 0, codes 0.  (For any nonzero
+    bf16 amax, s is a nonzero fp32 number, so the quotient is always defined.)"""
     x = bf16_to_f64(x_bits).astype(np.float32)                        # exact widening
     amax = np.float32(np.max(np.abs(x)))
     if amax == 0:
         return np.zeros(len(x), dtype=np.uint8), np.float32(0.0)
     s = np.float32(amax / np.float32(448.0))                          # IEEE fp32 division
-    r = np.float32(np.float32(448.0) / amax)                          # IEEE fp32 division
-    y = (x * r).astype(np.float32)                                    # IEEE fp32 product
+    y = (x / s).astype(np.float32)                                    # IEEE fp32 division
     return f32_to_e4m3fn(y), s
 
 
-def encode_record(token_bits: np.ndarray, kv_dtype: int) -> np.ndarray:
+def exact_to_bf16_rne(v: Fraction) -> int:
+    """An exact rational value -> the bf16 bit pattern of the nearest bf16 value, ties to the even
+    pattern: the plain round-to-nearest-even of the exact value, with no intermediate rounding.
+    Values that would round beyond the largest bf16 raise."""
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()      # 2^(e-1) < a < 2^(e+1)
+    if Fraction(2) ** e > a:
+        e -= 1                                                     # now 2^e <= a < 2^(e+1)
+    e = max(e, -126)                                               # subnormals share the minimum exponent
+    ulp = Fraction(2) ** (e - 7)                                   # 8 significant bits
+    q = a / ulp
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * ulp
+    if val >= Fraction(2) ** 128:
+        raise OverflowError("bf16 overflow")
+    bits = int(np.array(float(val), dtype=np.float32).view(np.uint32)) >> 16   # val is bf16-exact
+    return sign | bits
+
+
+def inverse_rope(rope_bits: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """The 64 rope values of one token (bf16 patterns) with the rotary embedding undone: pair i
+    is (x_2i, x_2i+1); with c = cos[i], s = sin[i] (fp32 table entries of the token's position)
+    the result is (x_2i c + x_2i+1 s, -x_2i s + x_2i+1 c), the rotation by minus the angle,
+    evaluated exactly (rational arithmetic) and rounded once to bf16 (nearest-even)."""
+    x = bf16_to_f64(rope_bits)
+    c = np.asarray(cos, dtype=np.float32).astype(np.float64)
+    s = np.asarray(sin, dtype=np.float32).astype(np.float64)
+    out = np.empty(64, dtype=np.uint16)
+    for i in range(32):
+        a, b = Fraction(float(x[2 * i])), Fraction(float(x[2 * i + 1]))
+        ci, si = Fraction(float(c[i])), Fraction(float(s[i]))
+        out[2 * i] = exact_to_bf16_rne(a * ci + b * si)
+        out[2 * i + 1] = exact_to_bf16_rne(-a * si + b * ci)
+    return out
+
+
+def encode_record(token_bits: np.ndarray, kv_dtype: int, cos: Optional[np.ndarray] = None,
+                  sin: Optional[np.ndarray] = None) -> np.ndarray:
     """One token's 576 bf16 values (bit patterns: 512 latent, 64 rope) -> its cache record
     (uint8).  bf16 caches store the 1152 bytes as they are; FP8 caches store the 512 codes, the
-    4 group scales and the 64 rope values."""
-    t = np.ascontiguousarray(token_bits, dtype=np.uint16)
+    4 group scales and the 64 rope values.  With ``cos``/``sin`` (the 32 fp32 table entries of the
+    token's position) the rope values are stored with the rotary embedding undone
+    (``inverse_rope``)."""
+    t = np.array(token_bits, dtype=np.uint16, copy=True)
     assert t.shape == (D_QK,)
+    if cos is not None:
+        t[512:] = inverse_rope(t[512:], cos, sin)
     if kv_dtype == KV_BF16:
         return t.view(np.uint8).copy()
     rec = np.zeros(FP8_RECORD_BYTES, dtype=np.uint8)
@@ -182,16 +238,22 @@ def encode_record(token_bits: np.ndarray, kv_dtype: int) -> np.ndarray:
 
 
 def cache_write(cache: np.ndarray, kv_dtype: int, tokens_bits: np.ndarray,
-                slot_mapping: Sequence[int]) -> np.ndarray:
+                slot_mapping: Sequence[int], positions: Optional[Sequence[int]] = None,
+                cos_table: Optional[np.ndarray] = None, sin_table: Optional[np.ndarray] = None) -> np.ndarray:
     """Writes token t's record to physical slot slot_mapping[t] (block id * 64 + offset) of the
-    paged cache [num_pages, 64, record]; slots < 0 or past the cache are skipped.  Returns the
-    updated copy of the cache."""
+    paged cache [num_pages, 64, record]; slots < 0 or past the cache are skipped.  With
+    ``positions`` and the tables [max_pos, 32], token t's rope values are stored with the rotation
+    of position positions[t] undone.  Returns the updated copy of the cache."""
     out = np.array(cache, dtype=np.uint8, copy=True)
     flat = out.reshape(-1, out.shape[-1])
     for t, slot in enumerate(slot_mapping):
         slot = int(slot)
         if 0 <= slot < flat.shape[0]:
-            flat[slot] = encode_record(tokens_bits[t], kv_dtype)
+            if positions is None:
+                flat[slot] = encode_record(tokens_bits[t], kv_dtype)
+            else:
+                p = int(positions[t])
+                flat[slot] = encode_record(tokens_bits[t], kv_dtype, cos_table[p], sin_table[p])
     return out
 
 

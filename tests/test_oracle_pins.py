@@ -131,6 +131,50 @@ def test_topk_heavy_ties_invariants():
     assert (taken == eq_idx[:len(taken)]).all()          # ties at the cut: lowest indices
 
 
+# Rows addressed through 64-bit element offsets into one flat buffer (unaligned and overlapping).
+ROW_OFFSET_FLAT = [0.5, 3.0, -1.0, 2.0, 2.0, 7.0, 1.0, 1.0, 9.0, 0.0, -2.0, 4.0]
+ROW_OFFSET_CASE = {"offsets": [3, 0, 6, 2], "stride": 5, "lengths": [5, 3, 5, 4], "k": 2,
+                   # worked by hand:
+                   #   row 0 = flat[3:8] = [2, 2, 7, 1, 1]: 7 (j=2), then the tie 2/2 -> j=0   -> [0, 2]
+                   #   row 1 = flat[0:5], L=3 -> [0.5, 3, -1]: 3 (j=1), 0.5 (j=0)              -> [0, 1]
+                   #   row 2 = flat[6:11] = [1, 1, 9, 0, -2]: 9 (j=2), tie 1/1 -> j=0          -> [0, 2]
+                   #   row 3 = flat[2:7], L=4 -> [-1, 2, 2, 7]: 7 (j=3), tie 2/2 -> j=1        -> [1, 3]
+                   "expected": [[0, 2], [0, 1], [0, 2], [1, 3]]}
+
+
+def _row_offsets_case_holds(topk_rows_fn):
+    c = ROW_OFFSET_CASE
+    flat = np.array(ROW_OFFSET_FLAT, np.float32)
+    got = topk_rows_fn(flat, c["lengths"], c["k"], row_offsets=np.array(c["offsets"], np.int64),
+                       row_stride=c["stride"])
+    if got.tolist() != c["expected"]:
+        return False
+    sub = topk_rows_fn(flat, c["lengths"], c["k"], row_offsets=np.array(c["offsets"], np.int64),
+                       row_stride=c["stride"], rows=[3, 0])
+    return sub.tolist() == [c["expected"][3], c["expected"][0]]
+
+
+def test_topk_rows_row_offsets_hand_case():
+    assert _row_offsets_case_holds(O.topk_rows)
+
+
+def _ro_mutant_ignores_offsets(scores, lengths, k, row_offsets=None, row_stride=None, rows=None):
+    flat = np.asarray(scores).reshape(-1)
+    stride = int(row_stride)
+    sel = list(range(len(lengths))) if rows is None else list(rows)
+    return np.stack([O.topk_row(flat[r * stride:(r + 1) * stride], lengths[r], k) for r in sel])
+
+
+def _ro_mutant_off_by_one(scores, lengths, k, row_offsets=None, row_stride=None, rows=None):
+    return O.topk_rows(scores, lengths, k, row_offsets=np.asarray(row_offsets) + 1, row_stride=row_stride,
+                       rows=rows)
+
+
+@pytest.mark.parametrize("mutant", [_ro_mutant_ignores_offsets, _ro_mutant_off_by_one])
+def test_pins_catch_row_offset_mutants(mutant):
+    assert not _row_offsets_case_holds(mutant)
+
+
 # Mutants: plausible mistakes, planted in copies of the oracle's top-k on the CPU, must fail a pin.
 
 def _mutant_reverse_ties(row, length, k):
@@ -266,19 +310,39 @@ def test_quantize_group_hand_case():
     assert (codes[6:] == 0).all()
 
 
-def test_quantize_group_multiplier_reading():
-    # The codes are e4m3(x * r) with r = fp32(448 / amax), not e4m3(x / s).  amax = 416: r rounds up
-    # (fp32(448/416) > 448/416), so x = -312 gives x * r just beyond -336, the midpoint of -320 (0xFA)
-    # and -352 (0xFB), and the code is 0xFB; the quotient x / s would land on -336 exactly and tie to
-    # the even 0xFA.
-    r = np.float32(448.0) / np.float32(416.0)
-    assert float(r) > 448.0 / 416.0
-    assert float(np.float32(np.float32(-312.0) * r)) < -336.0
+def test_quantize_group_quotient_reading():
+    # The codes are e4m3(x / s), the inverse of the dequantization (code * s).  amax = 416: s =
+    # fp32(416/448) rounds down, and x = -312 gives the fp32 quotient -336 exactly, the midpoint of
+    # -320 (0xFA, mantissa 2) and -352 (0xFB, mantissa 3); the tie goes to the even mantissa, 0xFA.
+    # A multiplier form x * fp32(448/416) would land just beyond -336 and give 0xFB.
+    s_exp = np.float32(np.float32(416.0) / np.float32(448.0))
+    assert float(s_exp) < 416.0 / 448.0
+    assert np.float32(np.float32(-312.0) / s_exp) == np.float32(-336.0)
     x = np.zeros(128, np.float32)
     x[0], x[1] = 416.0, -312.0
     codes, s = O.quantize_group(_bf16_bits(x))
-    assert s == np.float32(np.float32(416.0) / np.float32(448.0))
-    assert codes[0] == 0x7E and codes[1] == 0xFB
+    assert s == s_exp
+    assert codes[0] == 0x7E and codes[1] == 0xFA
+
+
+def test_quantize_group_tiny_amax():
+    # The smallest bf16 magnitudes: amax = 2^-133 (the least bf16 subnormal) and 2^-126.  s stays
+    # a nonzero fp32 number (2^-133 / 448 is about 2^-141.8, above the least fp32 subnormal 2^-149),
+    # every code is finite (no NaN code 0x7F / 0xFF), the largest magnitude maps to +-448 (0x7E),
+    # and zeros in the group stay zero codes.
+    for amax in (2.0 ** -133, 2.0 ** -126, 3.0 * 2.0 ** -131):
+        x = np.zeros(128, np.float32)
+        x[0], x[1], x[2] = amax, -amax, amax / 2
+        bits = _bf16_bits(x)
+        assert O.bf16_to_f64(bits)[0] == amax
+        codes, s = O.quantize_group(bits)
+        assert s > 0 and s == np.float32(np.float32(amax) / np.float32(448.0))
+        assert codes[0] == 0x7E and codes[1] == 0xFE
+        assert (codes & 0x7F != 0x7F).all()
+        assert (codes[3:] == 0).all()
+        # the half-amax entry: 224 when s is a normal fp32 number (amax / s is then 448)
+        if s >= np.float32(2.0 ** -126):
+            assert codes[2] == 0x76
 
 
 def test_quantize_group_scale_max_code_and_error_bound():
@@ -300,6 +364,23 @@ def test_quantize_group_scale_max_code_and_error_bound():
         bound = np.where(y >= 2 ** -6, np.abs(xv) * 2 ** -4, float(s) * 2 ** -10) + np.abs(xv) * 2 ** -22 + 1e-300
         assert (np.abs(deq - xv) <= bound).all(), trial
         assert (np.signbit(deq[xv != 0]) == np.signbit(xv[xv != 0])).all()
+
+
+def _quant_mutant_multiplier(x_bits):
+    """The multiplier form e4m3(x * fp32(448 / amax)): must fail the quotient pin."""
+    x = O.bf16_to_f64(x_bits).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    if amax == 0:
+        return np.zeros(len(x), dtype=np.uint8), np.float32(0.0)
+    s = np.float32(amax / np.float32(448.0))
+    r = np.float32(np.float32(448.0) / amax)
+    return O.f32_to_e4m3fn((x * r).astype(np.float32)), s
+
+
+def test_pins_catch_quantizer_multiplier_mutant(monkeypatch):
+    monkeypatch.setattr(O, "quantize_group", _quant_mutant_multiplier)
+    with pytest.raises(AssertionError):
+        test_quantize_group_quotient_reading()
 
 
 def test_quantize_all_zero_group():
@@ -339,6 +420,119 @@ def test_cache_write_slots():
     untouched[[5, 130]] = False
     assert (flat[untouched] == 0xAB).all()
     assert (cache == 0xAB).all()                                       # input not modified
+
+
+def _rope_tables(angles):
+    a = np.asarray(angles, np.float64)
+    return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+
+
+def test_inverse_rope_closed_forms():
+    rng = np.random.default_rng(21)
+    x = _bf16_rne_bits(rng.standard_normal(64).astype(np.float32))
+    xv = O.bf16_to_f64(x)
+    one, zero = np.ones(32, np.float32), np.zeros(32, np.float32)
+    # angle 0: identity
+    np.testing.assert_array_equal(O.inverse_rope(x, one, zero), x)
+    # angle pi/2 (cos 0, sin 1 exactly): (a, b) -> (b, -a)
+    y = O.bf16_to_f64(O.inverse_rope(x, zero, one))
+    np.testing.assert_array_equal(y[0::2], xv[1::2])
+    np.testing.assert_array_equal(y[1::2], -xv[0::2])
+    # angle pi (cos -1, sin 0): negation
+    np.testing.assert_array_equal(O.bf16_to_f64(O.inverse_rope(x, -one, zero)), -xv)
+    # angle -pi/2 (cos 0, sin -1): (a, b) -> (-b, a), i.e. the inverse of the pi/2 case
+    y = O.bf16_to_f64(O.inverse_rope(x, zero, -one))
+    np.testing.assert_array_equal(y[0::2], -xv[1::2])
+    np.testing.assert_array_equal(y[1::2], xv[0::2])
+    # angle pi/3: cos 1/2 exact in fp32; a pair (1, 0) -> (1/2, -sin)
+    c = np.full(32, 0.5, np.float32)
+    sn = np.full(32, np.sqrt(3) / 2, np.float32)
+    e = np.zeros(64, np.uint16)
+    e[0::2] = _bf16_bits(np.ones(32, np.float32))
+    y = O.bf16_to_f64(O.inverse_rope(e, c, sn))
+    assert (y[0::2] == 0.5).all()
+    assert (y[1::2] == O.bf16_to_f64(_bf16_rne_bits(-sn))).all()
+
+
+def test_inverse_rope_undoes_a_forward_rotation():
+    """Rotating by +angle (done here in float64, written out independently of the oracle) and then
+    applying the oracle's inverse recovers the input to within the two bf16 roundings."""
+    rng = np.random.default_rng(22)
+    for trial in range(20):
+        ang = rng.uniform(-np.pi, np.pi, 32) * (trial + 1)
+        c, s = _rope_tables(ang)
+        x = rng.standard_normal(64)
+        a, b = x[0::2], x[1::2]
+        fwd = np.empty(64)
+        fwd[0::2] = a * c.astype(np.float64) - b * s.astype(np.float64)
+        fwd[1::2] = a * s.astype(np.float64) + b * c.astype(np.float64)
+        fb = _bf16_rne_bits(fwd.astype(np.float32))
+        back = O.bf16_to_f64(O.inverse_rope(fb, c, s))
+        scale = np.repeat(np.hypot(a, b), 2)
+        assert (np.abs(back - x) <= scale * 2.0 ** -6).all(), trial
+
+
+def test_inverse_rope_rounds_once_to_nearest_even():
+    # Exact values on bf16 midpoints (bf16 has 8 significant bits: the spacing above 1 is 2^-7).
+    # c = 1, s = 2^-8: the pair (1, 1) gives a*c + b*s = 1 + 2^-8, the midpoint of 1 (0x3F80, even)
+    # and 1 + 2^-7 (0x3F81), so 0x3F80; the pair (1, 3) gives 1 + 3 * 2^-8, the midpoint of
+    # 1 + 2^-7 (0x3F81) and 1 + 2^-6 (0x3F82, even), so 0x3F82.
+    c = np.ones(32, np.float32)
+    s = np.full(32, 2.0 ** -8, np.float32)
+    x = np.zeros(64, np.float32)
+    x[0::2] = 1.0
+    x[1::2] = 1.0
+    x[2], x[3] = 1.0, 3.0
+    y = O.inverse_rope(_bf16_bits(x), c, s)
+    assert y[0] == 0x3F80                        # 1 + 2^-8 -> 1.0 (tie, even)
+    assert y[2] == 0x3F82                        # 1 + 3 * 2^-8 -> 1.015625 (tie, even)
+    # the second entry of the first pair: -1 * 2^-8 + 1 = 0.99609375, exactly a bf16 value (0x3F7F)
+    assert y[1] == 0x3F7F
+
+
+def test_cache_write_with_inverse_rope():
+    rng = np.random.default_rng(23)
+    toks = _bf16_rne_bits(rng.standard_normal((3, 576)).astype(np.float32))
+    ang = rng.uniform(0, 6, (8, 32))
+    cos_t, sin_t = _rope_tables(ang)
+    pos = [5, 0, 7]
+    for kvd, rec in ((O.KV_FP8, 656), (O.KV_BF16, 1152)):
+        cache = np.zeros((1, 64, rec), np.uint8)
+        out = O.cache_write(cache, kvd, toks, [1, 2, 3], positions=pos, cos_table=cos_t, sin_table=sin_t)
+        flat = out.reshape(-1, rec)
+        for t in range(3):
+            dec = O.decode_record(flat[1 + t], kvd)
+            exp_rope = O.bf16_to_f64(O.inverse_rope(toks[t, 512:], cos_t[pos[t]], sin_t[pos[t]]))
+            np.testing.assert_array_equal(dec[512:], exp_rope)
+            plain = O.decode_record(O.encode_record(toks[t], kvd), kvd)
+            np.testing.assert_array_equal(dec[:512], plain[:512])     # the latent part is not rotated
+
+
+_INVERSE_ROPE = O.inverse_rope
+
+
+def _rope_mutant_forward(rope_bits, cos, sin):            # rotates by +angle instead of undoing it
+    return _INVERSE_ROPE(rope_bits, cos, -np.asarray(sin, np.float32))
+
+
+def _rope_mutant_half_pairs(rope_bits, cos, sin):         # pairs (i, i + 32) instead of (2i, 2i + 1)
+    x = np.asarray(rope_bits, np.uint16)
+    inter = np.empty(64, np.uint16)
+    inter[0::2], inter[1::2] = x[:32], x[32:]
+    y = _INVERSE_ROPE(inter, cos, sin)
+    return np.concatenate([y[0::2], y[1::2]])
+
+
+@pytest.mark.parametrize("mutant", [_rope_mutant_forward, _rope_mutant_half_pairs])
+def test_pins_catch_rope_mutants(mutant, monkeypatch):
+    monkeypatch.setattr(O, "inverse_rope", mutant)
+    caught = 0
+    for t in (test_inverse_rope_closed_forms, test_inverse_rope_undoes_a_forward_rotation):
+        try:
+            t()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
 
 
 def _enc_mutant_truncate(x):
@@ -776,3 +970,94 @@ def _idx_mutant_no_clamp(q, w, kidx, bt, length, stride, page=64):          # ne
                                     _idx_mutant_identity_pages, _idx_mutant_no_clamp])
 def test_pins_catch_indexer_mutants(mutant, golden_dir):
     assert not _indexer_hand_case_holds(mutant, golden_dir)
+
+
+# indexer_error_scale: M[r, p] = sum_h |w_h| sum_d |q_hd| |k_pd|, the magnitude that bounds the GPU
+# scores' rounding error.
+
+def _scale_inputs():
+    """One row, two index heads of width 128, one page; worked by hand below."""
+    q = np.zeros((1, 2, 128), np.float32)
+    q[0, 0, :2] = [1.0, -2.0]
+    q[0, 1, 1:3] = [3.0, -1.0]
+    w = np.array([[-0.5, 2.0]], np.float32)
+    k = np.zeros((1, 64, 128), np.float32)
+    k[0, 0, :3] = [-4.0, 1.0, 2.0]          # position 0
+    k[0, 1, :3] = [1.0, 1.0, 1.0]           # position 1
+    bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    return bits(q), w, bits(k), np.array([[0]], np.int32)
+
+
+def _error_scale_case_holds(fn):
+    qb, w, kb, bt = _scale_inputs()
+    M = fn(qb, w, kb, bt, [0], [3], 4)
+    # position 0: head 0: |1||-4| + |-2||1| = 6; head 1: |3||1| + |-1||2| = 5; M = 0.5*6 + 2*5 = 13
+    # position 1: head 0: 1 + 2 = 3; head 1: 3 + 1 = 4; M = 0.5*3 + 2*4 = 9.5
+    # position 2: the zero key -> 0; position 3: past the length -> 0
+    return M.shape == (1, 4) and M[0].tolist() == [13.0, 9.5, 0.0, 0.0]
+
+
+def test_indexer_error_scale_hand_case():
+    assert _error_scale_case_holds(O.indexer_error_scale)
+
+
+def test_indexer_error_scale_bounds_scores_and_is_tight_for_nonnegative_terms():
+    rng = np.random.default_rng(31)
+    Hi, pages = 4, 3
+    q = _rand_bf16_bits(rng, (2, Hi, 128))
+    k = _rand_bf16_bits(rng, (pages, 64, 128))
+    w = rng.standard_normal((2, Hi)).astype(np.float32)
+    bt = np.array([[2, 0, 1]], np.int32)
+    args = (q, w, k, bt, [0, 0], [150, 190], 192)
+    sc, M = O.indexer_scores(*args), O.indexer_error_scale(*args)
+    fin = np.isfinite(sc)
+    assert (np.abs(sc[fin]) <= M[fin] * (1 + 1e-12)).all()          # triangle inequality
+    assert (M[~fin] == 0).all()
+    # all-nonnegative inputs: relu is the identity and every term adds up, so score == M
+    qa, ka = q & 0x7FFF, k & 0x7FFF
+    wa = np.abs(w)
+    args = (qa, wa, ka, bt, [0, 0], [150, 190], 192)
+    sc, M = O.indexer_scores(*args), O.indexer_error_scale(*args)
+    fin = np.isfinite(sc)
+    np.testing.assert_allclose(sc[fin], M[fin], rtol=1e-12)
+
+
+def _es_apply(q_bits, w, kidx_bits, block_table, lengths, stride, f, abs_w=True, abs_qk=True):
+    """A planted variant of the error scale on the CPU: f(|w|, |q|, |k|) per scored position."""
+    K = O.bf16_to_f64(kidx_bits)
+    Q = O.bf16_to_f64(q_bits)
+    out = np.zeros((len(lengths), stride))
+    for r in range(len(lengths)):
+        L = min(max(int(lengths[r]), 0), stride)
+        qa = np.abs(Q[r]) if abs_qk else Q[r]
+        wa = np.abs(w[r]) if abs_w else np.asarray(w[r], np.float64)
+        for p in range(L):
+            pg = int(block_table[0][p // 64])
+            ka = np.abs(K[pg, p % 64]) if abs_qk else K[pg, p % 64]
+            out[r, p] = f(wa, qa, ka)
+    return out
+
+
+def _es_mutant_signed_weights(q_bits, w, kidx_bits, block_table, row_req, lengths, stride, rows=None):
+    return _es_apply(q_bits, w, kidx_bits, block_table, lengths, stride, lambda wa, qa, ka: wa @ (qa @ ka),
+                     abs_w=False)
+
+
+def _es_mutant_no_abs_qk(q_bits, w, kidx_bits, block_table, row_req, lengths, stride, rows=None):
+    return _es_apply(q_bits, w, kidx_bits, block_table, lengths, stride, lambda wa, qa, ka: wa @ (qa @ ka),
+                     abs_qk=False)
+
+
+def _es_mutant_max_not_sum(q_bits, w, kidx_bits, block_table, row_req, lengths, stride, rows=None):
+    return _es_apply(q_bits, w, kidx_bits, block_table, lengths, stride,
+                     lambda wa, qa, ka: wa @ (qa * ka).max(axis=1))
+
+
+def _es_mutant_heads_unweighted(q_bits, w, kidx_bits, block_table, row_req, lengths, stride, rows=None):
+    return _es_apply(q_bits, w, kidx_bits, block_table, lengths, stride, lambda wa, qa, ka: (qa @ ka).sum())
+
+
+@pytest.mark.parametrize("mutant", [_es_mutant_signed_weights, _es_mutant_no_abs_qk, _es_mutant_max_not_sum,
+                                    _es_mutant_heads_unweighted])
+def test_pins_catch_error_scale_mutants(mutant):
+    assert not _error_scale_case_holds(mutant)
