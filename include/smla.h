@@ -9,8 +9,9 @@
  *   4. runs MQA attention in which every head reads the same 576-wide latent record
  *      (512 latent + 64 rope; values are the first 512 entries), with one fixed reduction order
  *                                                [smla_sparse_mla_decode, smla_sparse_mla_prefill_chunk]
- * and writes new tokens' records into the paged cache, quantizing them for FP8 caches
- *                                                [smla_kv_cache_write]
+ * and writes new tokens' records into the paged cache, quantizing them for FP8 caches and
+ * optionally undoing the rotary embedding of the rope part
+ *                                                [smla_kv_cache_write, smla_kv_cache_write_rope]
  * and produces the indexer scores the selector ranks  [smla_paged_mqa_logits]
  * The result for a row never depends on the other rows of the call.
  *
@@ -184,14 +185,34 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
  *           listed slots change.
  *   SMLA_KV_BF16: the record is the 1152 input bytes.
  *   SMLA_KV_FP8_E4M3_G128: for each 128-entry group g of the latent, amax = largest |x|; the
- *           stored scale is s_g = amax / 448 and code = e4m3(x * r_g) with r_g = 448 / amax (IEEE
- *           fp32 divisions and product, round-to-nearest-even), the product saturated to
- *           [-448, 448] and rounded to the nearest e4m3 value (ties to even mantissa); a group of
- *           zeros stores s_g = 0 and zero codes; the rope is stored unchanged.  Latent values must be finite (the codes of a group holding inf or NaN are
- *           unspecified).
+ *           stored scale is s_g = amax / 448 and code = e4m3(x / s_g), the inverse of the
+ *           dequantization code * s_g (IEEE fp32 divisions, round-to-nearest-even), the quotient
+ *           saturated to [-448, 448] and rounded to the nearest e4m3 value (ties to even mantissa);
+ *           a group of zeros stores s_g = 0 and zero codes; the rope is stored unchanged.  Latent
+ *           values must be finite (the codes of a group holding inf or NaN are unspecified).
  * Tokens mapped to the same slot race: which record remains is unspecified.  T = 0 enqueues nothing. */
 smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,
                                 void* cache, int32_t kv_dtype, int64_t num_pages, void* stream);
+
+/* KV insert with the rotary embedding of the rope part undone ("inverse-RoPE" cache write).
+ * Source: "Port DeepSeek-V4 optimization PR #174 to v0.26 ..." (MooreThreads/vllm-musa PR 178), table
+ * "Optimizations carried from PR #174", row "Attention cache write" (inverse-RoPE FP8 cache write,
+ * chunks in parallel); "[JJ] Preallocate DeepSeek V4 padded-query output", "Operation contract" (the
+ * fused RoPE and KV-insert operator).  The pages do not define the rotation; the convention here:
+ *   positions: int64 [T], the position of each token; 8-byte aligned.
+ *   cos_sin:   fp32 [max_pos, 64]: row p holds cos(theta_p,i) for i < 32, then sin(theta_p,i);
+ *              16-byte aligned.  Rope pair i is (rope[2i], rope[2i+1]).
+ *   The stored rope pair is (a c + b s, -a s + b c) for the input pair (a, b), c = cos_sin[p][i],
+ *   s = cos_sin[p][32 + i]: the rotation by -theta, which undoes a rotation by +theta.  It is
+ *   evaluated with exact products and one fp64 sum, then rounded to bf16 (nearest even); the result
+ *   is within one bf16 unit of the exactly rounded rotation (equal to it unless the fp64 sum itself
+ *   was inexact next to a bf16 rounding boundary).  A zero result is stored as +0.  Rope inputs must
+ *   be finite and the rotated values must fit bf16.
+ *   A token whose position lies outside [0, max_pos) is not written (like an invalid slot).
+ * Everything else is exactly smla_kv_cache_write; the latent part is not rotated. */
+smla_status smla_kv_cache_write_rope(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping,
+                                     const int64_t* positions, const float* cos_sin, int64_t max_pos, int32_t T,
+                                     void* cache, int32_t kv_dtype, int64_t num_pages, void* stream);
 
 /* Indexer scores (paged MQA logits): the per-position scores smla_topk_per_row consumes.
  * Sources: "[SM120] Sync DS4 with upstream main + validated perf backports", sections "September 12

@@ -29,7 +29,7 @@ _LIB: Optional[ctypes.CDLL] = None
 exported_symbols = (
     "smla_last_error", "smla_version", "smla_is_supported", "smla_workspace_size",
     "smla_fill_causal_lengths", "smla_topk_per_row", "smla_sparse_mla_decode",
-    "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write", "smla_paged_mqa_logits",
+    "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write", "smla_kv_cache_write_rope", "smla_paged_mqa_logits",
 )
 
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_WORKSPACE",
@@ -55,7 +55,7 @@ class Capacity(ctypes.Structure):
 
 
 def library_path() -> str:
-    return os.environ.get("SMLA_LIBRARY", os.path.join(_PKG_DIR, "libsmla.so"))
+    return os.path.join(_PKG_DIR, "libsmla.so")
 
 
 def load_library() -> ctypes.CDLL:
@@ -80,6 +80,7 @@ def load_library() -> ctypes.CDLL:
         "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, P, SZ, P],
                                           ctypes.c_int),
         "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
+        "smla_kv_cache_write_rope": ([P, I64, P, P, P, I64, I32, P, I32, I64, P], ctypes.c_int),
         "smla_paged_mqa_logits": ([P, I64, P, I64, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -297,10 +298,13 @@ def sparse_mla_prefill_chunk(q: torch.Tensor, kv: torch.Tensor, block_table_row:
 
 
 def kv_cache_write(kv_in: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
-                   kv_dtype: Optional[int] = None) -> torch.Tensor:
+                   kv_dtype: Optional[int] = None, positions: Optional[torch.Tensor] = None,
+                   cos_sin: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Writes the records of the tokens ``kv_in`` [T, 576] (bf16; rows may be strided) to the
     physical slots ``slot_mapping`` [T] (int64; < 0 skipped) of ``cache`` (uint8 [num_pages, 64,
-    record]), quantizing to FP8 records for FP8 caches.  Returns ``cache``."""
+    record]), quantizing to FP8 records for FP8 caches.  With ``positions`` (int64 [T]) and
+    ``cos_sin`` (fp32 [max_pos, 64]: 32 cosines then 32 sines per position) the rope part is stored
+    with the rotation of each token's position undone (smla_kv_cache_write_rope).  Returns ``cache``."""
     lib = load_library()
     _require(kv_in, "kv_in", torch.bfloat16, contiguous=False)
     if kv_in.dim() != 2 or kv_in.shape[1] != 576 or kv_in.stride(1) != 1:
@@ -315,8 +319,21 @@ def kv_cache_write(kv_in: torch.Tensor, slot_mapping: torch.Tensor, cache: torch
     rec = 1152 if dt == KV_BF16 else 656
     if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != rec:
         raise ValueError(f"cache must be [num_pages, 64, {rec}] for kv_dtype {dt}")
-    _check(lib.smla_kv_cache_write(_ptr(kv_in), kv_in.stride(0), _ptr(slot_mapping), T, _ptr(cache), dt,
-                                   cache.shape[0], _stream(dev)))
+    if (positions is None) != (cos_sin is None):
+        raise ValueError("positions and cos_sin go together")
+    if positions is None:
+        _check(lib.smla_kv_cache_write(_ptr(kv_in), kv_in.stride(0), _ptr(slot_mapping), T, _ptr(cache), dt,
+                                       cache.shape[0], _stream(dev)))
+        return cache
+    _require(positions, "positions", torch.int64, dev)
+    _require(cos_sin, "cos_sin", torch.float32, dev)
+    if positions.numel() < T:
+        raise ValueError("positions is shorter than T")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
+        raise ValueError("cos_sin must be [max_pos, 64] (32 cosines then 32 sines per position)")
+    _check(lib.smla_kv_cache_write_rope(_ptr(kv_in), kv_in.stride(0), _ptr(slot_mapping), _ptr(positions),
+                                        _ptr(cos_sin), cos_sin.shape[0], T, _ptr(cache), dt, cache.shape[0],
+                                        _stream(dev)))
     return cache
 
 

@@ -108,6 +108,30 @@ smla_status check_attention(const void* q, int64_t q_row_stride, const void* kv,
     return SMLA_OK;
 }
 
+// Shared validation of the cache-write entry points.
+smla_status check_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,
+                              void* cache, int32_t kv_dtype, int64_t num_pages) {
+    smla_status st;
+    if ((st = check_kv_dtype(kv_dtype)) != SMLA_OK) return st;
+    if (T < 0) return fail(SMLA_ERR_INVALID_ARG, "T=%d must be >= 0", T);
+    if (num_pages < 1) return fail(SMLA_ERR_INVALID_ARG, "num_pages=%lld must be >= 1", (long long)num_pages);
+    if (num_pages > kMaxPages)
+        return fail(SMLA_ERR_CAPACITY, "num_pages=%lld exceeds the supported maximum %lld", (long long)num_pages,
+                    (long long)kMaxPages);
+    if (in_row_stride < 576)
+        return fail(SMLA_ERR_INVALID_ARG, "in_row_stride=%lld must be >= 576", (long long)in_row_stride);
+    if (in_row_stride % 8 != 0)
+        return fail(SMLA_ERR_ALIGNMENT, "in_row_stride=%lld must be a multiple of 8 elements", (long long)in_row_stride);
+    if (T == 0) return ok();
+    if (!kv_in) return fail(SMLA_ERR_INVALID_ARG, "kv_in is NULL");
+    if (!slot_mapping) return fail(SMLA_ERR_INVALID_ARG, "slot_mapping is NULL");
+    if (!cache) return fail(SMLA_ERR_INVALID_ARG, "cache is NULL");
+    if (!aligned(kv_in, 16)) return fail(SMLA_ERR_ALIGNMENT, "kv_in must be 16-byte aligned");
+    if (!aligned(slot_mapping, 8)) return fail(SMLA_ERR_ALIGNMENT, "slot_mapping must be 8-byte aligned");
+    if (!aligned(cache, 16)) return fail(SMLA_ERR_ALIGNMENT, "cache must be 16-byte aligned");
+    return SMLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,27 +239,27 @@ smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, c
 
 smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping, int32_t T,
                                 void* cache, int32_t kv_dtype, int64_t num_pages, void* stream) {
-    smla_status st;
-    if ((st = check_kv_dtype(kv_dtype)) != SMLA_OK) return st;
-    if (T < 0) return fail(SMLA_ERR_INVALID_ARG, "T=%d must be >= 0", T);
-    if (num_pages < 1) return fail(SMLA_ERR_INVALID_ARG, "num_pages=%lld must be >= 1", (long long)num_pages);
-    if (num_pages > kMaxPages)
-        return fail(SMLA_ERR_CAPACITY, "num_pages=%lld exceeds the supported maximum %lld", (long long)num_pages,
-                    (long long)kMaxPages);
-    if (in_row_stride < 576)
-        return fail(SMLA_ERR_INVALID_ARG, "in_row_stride=%lld must be >= 576", (long long)in_row_stride);
-    if (in_row_stride % 8 != 0)
-        return fail(SMLA_ERR_ALIGNMENT, "in_row_stride=%lld must be a multiple of 8 elements", (long long)in_row_stride);
-    if (T == 0) return ok();
-    if (!kv_in) return fail(SMLA_ERR_INVALID_ARG, "kv_in is NULL");
-    if (!slot_mapping) return fail(SMLA_ERR_INVALID_ARG, "slot_mapping is NULL");
-    if (!cache) return fail(SMLA_ERR_INVALID_ARG, "cache is NULL");
-    if (!aligned(kv_in, 16)) return fail(SMLA_ERR_ALIGNMENT, "kv_in must be 16-byte aligned");
-    if (!aligned(slot_mapping, 8)) return fail(SMLA_ERR_ALIGNMENT, "slot_mapping must be 8-byte aligned");
-    if (!aligned(cache, 16)) return fail(SMLA_ERR_ALIGNMENT, "cache must be 16-byte aligned");
-    return hip_status(smla::launch_kv_cache_write(kv_in, in_row_stride, slot_mapping, T, cache, kv_dtype, num_pages,
-                                                  (hipStream_t)stream),
+    smla_status st = check_cache_write(kv_in, in_row_stride, slot_mapping, T, cache, kv_dtype, num_pages);
+    if (st != SMLA_OK || T == 0) return st;
+    return hip_status(smla::launch_kv_cache_write(kv_in, in_row_stride, slot_mapping, nullptr, nullptr, 0, T, cache,
+                                                  kv_dtype, num_pages, (hipStream_t)stream),
                       "kv_cache_write");
+}
+
+smla_status smla_kv_cache_write_rope(const void* kv_in, int64_t in_row_stride, const int64_t* slot_mapping,
+                                     const int64_t* positions, const float* cos_sin, int64_t max_pos, int32_t T,
+                                     void* cache, int32_t kv_dtype, int64_t num_pages, void* stream) {
+    smla_status st = check_cache_write(kv_in, in_row_stride, slot_mapping, T, cache, kv_dtype, num_pages);
+    if (st != SMLA_OK) return st;
+    if (max_pos < 1) return fail(SMLA_ERR_INVALID_ARG, "max_pos=%lld must be >= 1", (long long)max_pos);
+    if (T == 0) return ok();
+    if (!positions) return fail(SMLA_ERR_INVALID_ARG, "positions is NULL");
+    if (!cos_sin) return fail(SMLA_ERR_INVALID_ARG, "cos_sin is NULL");
+    if (!aligned(positions, 8)) return fail(SMLA_ERR_ALIGNMENT, "positions must be 8-byte aligned");
+    if (!aligned(cos_sin, 16)) return fail(SMLA_ERR_ALIGNMENT, "cos_sin must be 16-byte aligned");
+    return hip_status(smla::launch_kv_cache_write(kv_in, in_row_stride, slot_mapping, positions, cos_sin, max_pos, T,
+                                                  cache, kv_dtype, num_pages, (hipStream_t)stream),
+                      "kv_cache_write_rope");
 }
 
 smla_status smla_paged_mqa_logits(const void* q, int64_t q_row_stride, const float* weights, int64_t w_row_stride,

@@ -734,6 +734,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        // FP8: biased exponent of the scale normalization the accumulators carry (0: none yet); the
+        // accumulators hold the output times 2^(127 - e_run).
+        int e_run = 0;
         // ---- A9: O^T += V^T P^T for the 4 head blocks over this wave's 64 dims (tile it in LDS at sb) ----
         auto value_product = [&](int it, const uint8_t* sb) {
             float a_blk[4];
@@ -752,9 +755,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     sc8[i] = tscale[it & 1][4 * g + i][gv];
                     sc8[4 + i] = tscale[it & 1][16 + 4 * g + i][gv];
                 }
+                // Power-of-two normalization of the scales: every scale of the tile lies below
+                // 2^(eb - 126) for the biased exponent eb of the tile's largest scale (lanes l, l^16,
+                // l^32, l^48 hold all 32 tokens, so the max is wave-uniform).  The running exponent
+                // e_run only grows: when a tile's eb exceeds it the accumulators are scaled by the
+                // exact factor 2^(e_run - eb), folded into the rescale factors below.  The scaled
+                // weights p * s * 2^(127 - e_run) then stay below 2^9 (p <= 2^8 under the lazy
+                // rescale) and far above the fp16 subnormals for the scales that matter, whatever the
+                // magnitude of the group scales.
+                float mx = fmaxf(fmaxf(fmaxf(sc8[0], sc8[1]), fmaxf(sc8[2], sc8[3])),
+                                 fmaxf(fmaxf(sc8[4], sc8[5]), fmaxf(sc8[6], sc8[7])));
+                mx = head_max(mx);
+                int eb = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(mx) >> 23) & 0xffu));
+                if (eb == 0 && mx > 0.f) eb = 1;            // subnormal scales share exponent field 1
+                float f = 1.f;
+                if (eb > e_run) {
+                    if (e_run > 0) f = __builtin_ldexpf(1.f, e_run - eb);
+                    e_run = eb;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sc8[i] = __builtin_ldexpf(sc8[i], 127 - e_run);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    a_blk[b] = xalpha[b][lane & 15];
+                    a_blk[b] = xalpha[b][lane & 15] * f;
                     const f32x4_t p0 = pw32(b, 0)[lane], p1 = pw32(b, 1)[lane];
                     pb[b] = make_uint4(pack_f16x2_rne(p0[0] * sc8[0], p0[1] * sc8[1]),
                                        pack_f16x2_rne(p0[2] * sc8[2], p0[3] * sc8[3]),
@@ -808,6 +831,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) oacc[b][d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            e_run = 0;
         }
         const uint8_t* sb_prev = nullptr;
         for (int it = 0; it < ntiles; ++it) {
@@ -829,7 +853,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if (b >= nhb) break;
-            const float inv = xmul[b][lane & 15];
+            float inv = xmul[b][lane & 15];
+            if (KV_FP8 && e_run > 0) inv = __builtin_ldexpf(inv, e_run - 127);   // undo the scale normalization
             int head = head0 + 16 * b + (lane & 15);
             if (KV_FP8) asm volatile("" : "+v"(head));   // FP8: addresses computed per split (not held across splits)
             const int64_t pidx = (((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head) * kDv + vdim0 + 4 * g;

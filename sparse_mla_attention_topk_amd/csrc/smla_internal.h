@@ -84,7 +84,10 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
 hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_paged_mqa_logits(const IdxArgs& a, hipStream_t stream);
-hipError_t launch_kv_cache_write(const void* in, int64_t in_row_stride, const int64_t* slots, int32_t T, void* cache,
-                                 int kv_dtype, int64_t num_pages, hipStream_t stream);
+// positions == nullptr: the rope values are stored as given; else token t's rope is rotated back by the
+// angles of row positions[t] of cos_sin ([max_pos][64] fp32: 32 cosines, then 32 sines).
+hipError_t launch_kv_cache_write(const void* in, int64_t in_row_stride, const int64_t* slots, const int64_t* positions,
+                                 const float* cos_sin, int64_t max_pos, int32_t T, void* cache, int kv_dtype,
+                                 int64_t num_pages, hipStream_t stream);
 
 }  // namespace smla

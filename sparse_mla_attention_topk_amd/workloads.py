@@ -100,13 +100,14 @@ def page_table(ctx_lens: torch.Tensor, g: torch.Generator, device):
 
 
 def make_paged_cache(ctx_lens: torch.Tensor, kv_dtype: int, g: torch.Generator, device,
-                     chunk_pages: int = 4096) -> PagedCache:
+                     chunk_pages: int = 4096, fp8_scale_log2=(-4.0, 4.0)) -> PagedCache:
     """Allocate a paged cache holding one context per entry of ``ctx_lens``.
 
     Physical pages 1..N are handed out through a seeded random permutation;
     page 0 is the NaN null page.  Values: bf16 N(0,1) for the bf16 cache; for
     the FP8 cache, e4m3 codes of N(0,1) (round to nearest even), fp32 scales
-    2**U(-4, 4) per (token, 128-group) and bf16 N(0,1) rope.
+    2**U(lo, hi) per (token, 128-group) with (lo, hi) = ``fp8_scale_log2``
+    (default (-4, 4)) and bf16 N(0,1) rope.
     """
     ctx_lens = ctx_lens.to(torch.int64).cpu()
     bt, total = page_table(ctx_lens, g, device)
@@ -122,7 +123,8 @@ def make_paged_cache(ctx_lens: torch.Tensor, kv_dtype: int, g: torch.Generator, 
         else:
             lat = torch.randn((ntok, 512), generator=g, device=device, dtype=torch.float32)
             codes = lat.to(torch.float8_e4m3fn).view(torch.uint8)
-            expo = torch.rand((ntok, 4), generator=g, device=device, dtype=torch.float32) * 8.0 - 4.0
+            lo, hi = fp8_scale_log2
+            expo = torch.rand((ntok, 4), generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
             scales = torch.exp2(expo).contiguous().view(torch.uint8).view(ntok, 16)
             rope = torch.randn((ntok, D_ROPE), generator=g, device=device, dtype=torch.float32)
             rope_b = rope.to(torch.bfloat16).view(torch.uint8).view(ntok, 128)
@@ -198,7 +200,7 @@ class DecodeWorkload:
 
 def decode_workload(name: str, B: int, H: int, k: int, ctx_lo: int, ctx_hi: int, kv_dtype: int,
                     seed: int, device, n_sets: int = 1, score_kind: str = "normal",
-                    stride: Optional[int] = None) -> DecodeWorkload:
+                    stride: Optional[int] = None, fp8_scale_log2=(-4.0, 4.0)) -> DecodeWorkload:
     """B decode rows, one request each, context lengths uniform in [ctx_lo, ctx_hi].
 
     ``n_sets`` independent (Q, scores) sets share one cache; timing loops rotate
@@ -206,7 +208,7 @@ def decode_workload(name: str, B: int, H: int, k: int, ctx_lo: int, ctx_hi: int,
     """
     g = _gen(seed, device)
     ctx = uniform_int(ctx_lo, ctx_hi, B, g, device).cpu()
-    cache = make_paged_cache(ctx, kv_dtype, g, device)
+    cache = make_paged_cache(ctx, kv_dtype, g, device, fp8_scale_log2=fp8_scale_log2)
     stride = int(stride if stride is not None else ctx_hi)
     row_req = torch.arange(B, dtype=torch.int32)
     sets = [make_rowset(cache, row_req, ctx.to(torch.int32), H, stride, g, device, score_kind)
@@ -303,6 +305,15 @@ def cache_write_tokens(device, T: int, num_pages: int, seed: int = 5, spread: fl
         raise ValueError("more tokens than slots")
     slots = torch.randperm(nslots, generator=g, device=device)[:T] + PAGE
     return CacheWriteWorkload(tokens=tokens, slots=slots.to(torch.int64), num_pages=num_pages)
+
+
+def rope_cos_sin(max_pos: int, device, base: float = 10000.0) -> torch.Tensor:
+    """A rotary table of the usual frequency schedule, fp32 [max_pos, 64]: row p holds cos(p f_i) for
+    i < 32, then sin(p f_i), with f_i = base^(-i/32) (computed in float64, rounded to fp32)."""
+    p = torch.arange(max_pos, dtype=torch.float64).view(-1, 1)
+    f = base ** (-torch.arange(32, dtype=torch.float64) / 32.0)
+    ang = p * f.view(1, -1)
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).to(device)
 
 
 def swa_draft_indices(ctx_lens: torch.Tensor, window: int = 128, draft: int = 5, width: int = 192) -> torch.Tensor:

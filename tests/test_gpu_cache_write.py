@@ -133,3 +133,76 @@ def test_written_records_feed_the_fp8_decode():
     O_ref, lse_ref = O.attention_rows(bf16_bits_np(q), kv_np(cache), O.KV_FP8, bt.cpu().numpy(), None,
                                       idx.cpu().numpy(), 1 / 24)
     assert_attention_close(out, lse, O_ref, lse_ref, "fp8 decode over written records", relative=True)
+
+
+def test_fp8_tiny_amax_groups():
+    # Groups whose largest magnitude is among the smallest bf16 values (down to the least subnormal
+    # 2^-133): the quotient x / s stays defined (s is a nonzero fp32 number), every code is finite and
+    # the bytes equal the oracle's.
+    T = 6
+    tok = np.zeros((T, 576), np.float32)
+    amaxes = [2.0 ** -133, 2.0 ** -130, 3.0 * 2.0 ** -131, 2.0 ** -126, 2.0 ** -120, 2.0 ** -100]
+    rng = np.random.default_rng(12)
+    for t, a in enumerate(amaxes):
+        for g in range(4):
+            m = rng.integers(-8, 9, 128).astype(np.float64) / 8.0        # multiples of 1/8 in [-1, 1]
+            m[0] = 1.0
+            tok[t, 128 * g:128 * (g + 1)] = (m * a).astype(np.float32)
+        tok[t, 512:] = rng.standard_normal(64).astype(np.float32)
+    bits = (tok.view(np.uint32) >> 16).astype(np.uint16)
+    tokens = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    slots = torch.arange(T, dtype=torch.int64, device=DEV) + 64
+    cache = _cache(2, W.KV_FP8)
+    before = kv_np(cache)
+    smla.kv_cache_write(tokens, slots, cache, kv_dtype=W.KV_FP8)
+    torch.cuda.synchronize()
+    got = kv_np(cache)
+    exp = _expected(before, W.KV_FP8, bits, slots.cpu().numpy())
+    np.testing.assert_array_equal(got, exp)
+    codes = got.reshape(-1, 656)[64:64 + T, :512]
+    assert ((codes & 0x7F) != 0x7F).all()
+
+
+def _bf16_order(bits):
+    b = np.asarray(bits, np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+@pytest.mark.parametrize("kv_dtype", [W.KV_FP8, W.KV_BF16])
+def test_inverse_rope_cache_write(kv_dtype):
+    T, pages, max_pos = 384, 12, 70000
+    log(f"inverse-rope cache write kv_dtype={kv_dtype} T={T}")
+    wl = W.cache_write_tokens(DEV, T=T, num_pages=pages, seed=15, spread=3.0)
+    g = torch.Generator(device="cpu").manual_seed(16)
+    pos = torch.randint(0, max_pos, (T,), generator=g, dtype=torch.int64)
+    pos[5], pos[6] = -1, max_pos                          # outside the table: not written
+    pos = pos.to(DEV)
+    cs = W.rope_cos_sin(max_pos, DEV)
+    cache = _cache(pages, kv_dtype)
+    before = kv_np(cache)
+    smla.kv_cache_write(wl.tokens, wl.slots, cache, kv_dtype=kv_dtype, positions=pos, cos_sin=cs)
+    torch.cuda.synchronize()
+    got = kv_np(cache).reshape(-1, cache.shape[-1])
+    bits = bf16_bits_np(wl.tokens)
+    csn = cs.cpu().numpy()
+    slots = wl.slots.cpu().numpy()
+    pn = pos.cpu().numpy()
+    rope_off = 528 if kv_dtype == W.KV_FP8 else 1024
+    exact = 0
+    worst = 0
+    for t in range(T):
+        rec = got[slots[t]]
+        if pn[t] < 0 or pn[t] >= max_pos:
+            assert (rec == FILL).all(), t
+            continue
+        ref = O.encode_record(bits[t], kv_dtype, csn[pn[t], :32], csn[pn[t], 32:])
+        np.testing.assert_array_equal(rec[:rope_off], ref[:rope_off], err_msg=f"token {t}: latent part")
+        d = np.abs(_bf16_order(rec[rope_off:].view(np.uint16)) - _bf16_order(ref[rope_off:].view(np.uint16)))
+        worst = max(worst, int(d.max()))
+        exact += int((d == 0).sum())
+    log(f"[cache write rope] kv_dtype={kv_dtype}: {exact} of {(T - 2) * 64} rope values bit-exact, "
+        f"largest difference {worst} bf16 units")
+    assert worst <= 1
+    untouched = np.ones(got.shape[0], bool)
+    untouched[slots] = False
+    assert (got[untouched] == FILL).all()

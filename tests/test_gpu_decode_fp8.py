@@ -42,15 +42,17 @@ def fp8():
     return wl, kv_np(wl.cache.kv)
 
 
-def test_fp8_full_size_sampled_rows(fp8):
+def test_fp8_full_size_all_rows(fp8):
+    """Every row of the B=128 FP8 batch against the oracle (exact dequantization in fp64)."""
     wl, kvh = fp8
     rs = wl.sets[0]
     idx, out, lse = _run(wl, rs)
-    rows = sample_rows(128, 8, 13)
+    rows = list(range(128))
     ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, rows, kvh)
     assert np.array_equal(idx.cpu().numpy()[rows], ref_idx)
-    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, "fp8 B128 H64 k2048", relative=True)
-    log(f"[fp8] full-size sampled {st}")
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, "decode fp8 B128 H64 k2048 (all 128 rows)",
+                                relative=True)
+    log(f"[fp8] full-size all rows {st}")
 
 
 def test_fp8_batch_invariance(fp8):
@@ -127,3 +129,33 @@ def test_fp8_q_beyond_fp16_range():
                                       rs.row_req.cpu().numpy(), idx.cpu().numpy(), wl.scale)
     st = assert_attention_close(out, lse, O_ref, lse_ref, "fp8 large q", relative=True)
     log(f"[fp8] large q {st}")
+
+
+@pytest.mark.parametrize("lo,hi,out_log2", [(-20.0, -20.0, 20), (16.0, 16.0, -16), (-20.0, 16.0, -16),
+                                             (-40.0, -30.0, 35)])
+def test_fp8_extreme_group_scales(lo, hi, out_log2):
+    """Group scales far from 1 (2^-20 and 2^16, a mix of both across tokens and groups, and 2^-40..2^-30):
+    the scaled weights of the value product are normalized by a power of two per tile, so neither fp16
+    overflow (large scales) nor fp16 subnormal weights (small scales) reach the output.  Outputs are
+    compared after multiplying both sides by 2^out_log2 (exact), which brings them to unit scale.  The LSE
+    bound is derived from the score magnitudes: an fp32 evaluation of a 576-term score s_j differs
+    from the exact one by at most 2^-14 * M_j with M_j = scale * sum_d |q_d| |K_jd| (576 * 2^-24 < 2^-14),
+    and the LSE moves by at most the largest score error; 2^-20 |LSE| covers its own fp32 evaluation."""
+    B = 6
+    wl = W.decode_workload(f"fp8_scales_{lo}_{hi}", B=B, H=64, k=2048, ctx_lo=3000, ctx_hi=9000, kv_dtype=W.KV_FP8,
+                           seed=40, device=DEV, fp8_scale_log2=(lo, hi))
+    rs = wl.sets[0]
+    idx, out, lse = _run(wl, rs)
+    kvh = kv_np(wl.cache.kv)
+    ref_idx, O_ref, lse_ref = _oracle_rows(wl, rs, list(range(B)), kvh)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    qf = O.bf16_to_f64(bf16_bits_np(rs.q))
+    bt = wl.cache.block_table.cpu().numpy()
+    M = np.zeros((B, 64))
+    for r in range(B):
+        K = O.gather_tokens(kvh, W.KV_FP8, bt[int(rs.row_req[r])], [int(p) for p in ref_idx[r] if p >= 0])
+        M[r] = wl.scale * (np.abs(qf[r]) @ np.abs(K).T).max(axis=1)
+    lse_tol = 1e-3 + 2.0 ** -14 * M + 2.0 ** -20 * np.abs(lse_ref)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, f"decode fp8 group scales 2^U({lo:g},{hi:g})",
+                                relative=True, out_scale=2.0 ** out_log2, lse_tol=lse_tol)
+    log(f"[fp8] scales 2^U({lo},{hi}) {st}")

@@ -35,17 +35,18 @@ def test_causal_lengths(pf):
 
 
 def test_prefill_sampled_rows_match_oracle(pf):
+    """256 seeded rows of the 4096 (plus the first and the last) against the oracle."""
     wl, lengths, idx, out, lse = pf
     T = wl.q.shape[0]
-    rows = sorted(set(sample_rows(T, 24, 4) + [0, T - 1]))
+    rows = sorted(set(sample_rows(T, 256, 4) + [0, T - 1]))
     scores_rows = wl.scores[rows].cpu().numpy()
     ref_idx = O.topk_rows(scores_rows, lengths.cpu().numpy()[rows], wl.k)
     assert np.array_equal(idx.cpu().numpy()[rows], ref_idx)
     kvh = kv_np(wl.cache.kv)
     O_ref, lse_ref = O.attention_rows(bf16_bits_np(wl.q[rows]), kvh, W.KV_BF16, wl.cache.block_table.cpu().numpy(),
                                       [0] * len(rows), ref_idx, wl.scale)
-    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, "prefill")
-    log(f"[prefill] sampled {st}")
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, f"prefill T=4096 ({len(rows)} seeded rows)")
+    log(f"[prefill] {len(rows)} seeded rows {st}")
 
 
 def test_mixed_batch_bit_identical(pf):

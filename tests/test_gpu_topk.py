@@ -50,12 +50,12 @@ def test_decode_shape_rows():
     _check(s, lens, 2048, what="64 rows L~U[8K,64K]")
 
 
-def test_fp8_decode_shape_rows_sampled():
+def test_fp8_decode_shape_all_rows():
     g = torch.Generator(device=DEV).manual_seed(33)
     lens = W.uniform_int(32768, 131072, 128, g, DEV).to(torch.int32)
     s = torch.randn((128, 131072), generator=g, device=DEV)
     W.poison_score_tails(s, lens)
-    _check(s, lens, 2048, rows=sample_rows(128, 48, 3), what="128 rows L~U[32K,128K]")
+    _check(s, lens, 2048, what="128 rows L~U[32K,128K] (all rows)")
 
 
 @pytest.mark.parametrize("k", [1, 2, 63, 192, 256, 2000, 2048, 4096, 16384])
