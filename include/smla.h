@@ -160,6 +160,21 @@ smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const vo
                                    int32_t rows, int32_t H, int32_t k, float softmax_scale, const float* sink,
                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* smla_sparse_mla_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments,
+ * arithmetic, results (bit for bit) and errors are those of smla_sparse_mla_decode; the split partials
+ * go to a static 32 MiB device array of the library instead (one per GPU, held until the process ends;
+ * its address is looked up once per device).  The call allocates nothing.  Every workspace-free call on
+ * a GPU shares that array: such calls must be ordered on one stream (calls that overlap on one GPU
+ * race).  Rows beyond what the array holds per launch are processed in further launches; a shape whose
+ * single row needs more than 32 MiB of partials is rejected with SMLA_ERR_CAPACITY (no supported shape
+ * does: at most 4.2 MB per row). */
+smla_status smla_sparse_mla_decode_noalloc(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
+                                           int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                           int32_t num_reqs, const int32_t* row_req, const int32_t* idx,
+                                           int32_t rows, int32_t H, int32_t k, float softmax_scale,
+                                           const float* sink, void* out, float* lse, void* stream);
+
 /* Prefill chunk of one request: T query rows that all read the request whose block table row is
  * block_table_row (bt_len entries).  Same arithmetic and the same kernels as smla_sparse_mla_decode
  * (row t of a chunk and the same row inside a mixed decode batch give bit-identical results). */

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "SmlaError", "KV_BF16", "KV_FP8", "Capacity", "library_path", "load_library", "exported_symbols",
     "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row", "topk_workspace",
-    "sparse_mla_decode", "sparse_mla_prefill_chunk", "kv_cache_write", "paged_mqa_logits",
+    "sparse_mla_decode", "sparse_mla_decode_noalloc", "sparse_mla_prefill_chunk", "kv_cache_write",
+    "paged_mqa_logits",
 ]
 
 KV_BF16 = 0
@@ -30,6 +31,7 @@ exported_symbols = (
     "smla_last_error", "smla_version", "smla_is_supported", "smla_workspace_size",
     "smla_fill_causal_lengths", "smla_topk_per_row", "smla_sparse_mla_decode",
     "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write", "smla_kv_cache_write_rope", "smla_paged_mqa_logits",
+    "smla_sparse_mla_decode_noalloc",
 )
 
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_WORKSPACE",
@@ -79,6 +81,8 @@ def load_library() -> ctypes.CDLL:
                                     P], ctypes.c_int),
         "smla_sparse_mla_prefill_chunk": ([P, I64, P, I32, I64, P, I64, P, I32, I32, I32, F32, P, P, P, P, SZ, P],
                                           ctypes.c_int),
+        "smla_sparse_mla_decode_noalloc": ([P, I64, P, I32, I64, P, I64, I32, P, P, I32, I32, I32, F32, P, P, P, P],
+                                           ctypes.c_int),
         "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
         "smla_kv_cache_write_rope": ([P, I64, P, P, P, I64, I32, P, I32, I64, P], ctypes.c_int),
         "smla_paged_mqa_logits": ([P, I64, P, I64, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P], ctypes.c_int),
@@ -267,6 +271,37 @@ def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tens
                                       _ptr(bt2), bt2.shape[1], bt2.shape[0], _ptr(row_req), _ptr(idx), rows, H, k,
                                       float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace),
                                       ws_bytes, _stream(dev)))
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, idx: torch.Tensor,
+                              softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                              row_req: Optional[torch.Tensor] = None, kv_dtype: Optional[int] = None,
+                              sink: Optional[torch.Tensor] = None):
+    """sparse_mla_decode through the workspace-free entry point (the split partials live in the
+    library's static per-GPU scratch array): the caller passes every output; nothing is allocated.
+    Workspace-free calls on one GPU must be ordered on one stream."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, contiguous=False)
+    if q.dim() != 3 or q.shape[2] != 576 or q.stride(2) != 1 or q.stride(1) != 576:
+        raise ValueError("q must be [rows, H, 576] with contiguous heads")
+    dev = q.device
+    _require(kv, "kv", torch.uint8, dev)
+    _require(block_table, "block_table", torch.int32, dev)
+    _require(idx, "idx", torch.int32, dev)
+    rows, H = q.shape[0], q.shape[1]
+    k = idx.shape[-1]
+    if idx.numel() < rows * k:
+        raise ValueError("idx is smaller than rows*k")
+    if row_req is not None:
+        _require(row_req, "row_req", torch.int32, dev)
+    _check_sink(sink, H, dev)
+    _attn_outputs(rows, H, dev, out, lse)
+    bt2 = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    _check(lib.smla_sparse_mla_decode_noalloc(_ptr(q), q.stride(0), _ptr(kv), _kv_dtype_of(kv, kv_dtype), kv.shape[0],
+                                              _ptr(bt2), bt2.shape[1], bt2.shape[0], _ptr(row_req), _ptr(idx), rows,
+                                              H, k, float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse),
+                                              _stream(dev)))
     return out, lse
 
 

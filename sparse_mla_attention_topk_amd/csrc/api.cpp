@@ -221,6 +221,37 @@ smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const vo
     return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_decode");
 }
 
+smla_status smla_sparse_mla_decode_noalloc(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
+                                           int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                           int32_t num_reqs, const int32_t* row_req, const int32_t* idx,
+                                           int32_t rows, int32_t H, int32_t k, float softmax_scale,
+                                           const float* sink, void* out, float* lse, void* stream) {
+    const size_t per_row = smla::attn_ws_bytes_per_row(H, k, kv_dtype);
+    if (per_row > smla::kNoAllocScratchBytes)
+        return fail(SMLA_ERR_CAPACITY,
+                    "one row needs %zu bytes of split partials (H=%d, k=%d) but the static scratch holds %zu", per_row,
+                    H, k, smla::kNoAllocScratchBytes);
+    // validated as the workspace form with a stand-in workspace of the scratch size; the real address
+    // is looked up below (no allocation either way)
+    static const size_t kStandIn = 256;
+    smla_status st = check_attention(q, q_row_stride, kv, kv_dtype, num_pages, block_table, bt_stride, num_reqs, idx,
+                                     rows, H, k, softmax_scale, out, lse, (void*)kStandIn,
+                                     smla::kNoAllocScratchBytes);
+    if (st != SMLA_OK) return st;
+    if (rows == 0) return ok();
+    if (row_req && !aligned(row_req, 4)) return fail(SMLA_ERR_ALIGNMENT, "row_req must be 4-byte aligned");
+    if (sink && !aligned(sink, 4)) return fail(SMLA_ERR_ALIGNMENT, "sink must be 4-byte aligned");
+    void* ws = nullptr;
+    if (per_row > 0) {
+        hipError_t e = smla::noalloc_scratch(&ws);
+        if (e != hipSuccess) return hip_status(e, "sparse_mla_decode_noalloc: scratch lookup");
+    }
+    smla::AttnArgs a{q,   q_row_stride, kv,  kv_dtype,      num_pages, block_table, bt_stride, num_reqs, row_req,
+                     idx, rows,         H,   k,             softmax_scale, sink,    out,       lse,      ws,
+                     per_row > 0 ? smla::kNoAllocScratchBytes : 0};
+    return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_decode_noalloc");
+}
+
 smla_status smla_sparse_mla_prefill_chunk(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                           int64_t num_pages, const int32_t* block_table_row, int64_t bt_len,
                                           const int32_t* idx, int32_t T, int32_t H, int32_t k, float softmax_scale,

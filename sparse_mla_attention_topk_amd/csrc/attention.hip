@@ -44,6 +44,7 @@
 // loads for every tile and the vmcnt bookkeeping below stays exact.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "smla_device.h"
@@ -969,6 +970,39 @@ __global__ __launch_bounds__(64 * kCombineHeads) void split_combine_kernel(const
     o.w = pack_bf16x2_hw(acc[6], acc[7]);
     *(uint4*)(out + orow * kDv + d) = o;
     if (d == 0 && lse) lse[orow] = LSE;
+}
+
+// ---- Workspace-free decode: the split partials live in a static device array ----
+// For callers that cannot allocate (code under HIP graph capture, serving loops, harnesses that forbid
+// allocation).  Each GPU the library runs on holds its own copy of `scratch` until the process ends;
+// every workspace-free call on a GPU shares it, so such calls must be ordered on one stream (calls
+// that overlap on one GPU race).  Nothing in it needs clearing: every (row, split, head) partial and
+// LSE a launch reads is written by that launch.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+// The device address of the current device's `scratch`, looked up once per device with that
+// device current (host code never passes the array's own name, a host-side stand-in).
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {

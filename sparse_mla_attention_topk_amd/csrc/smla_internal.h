@@ -83,6 +83,10 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
                        hipStream_t stream);
 hipError_t launch_causal_lengths(int64_t first_pos, int32_t T, int32_t* lengths, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// Workspace-free decode: bytes of the static per-device scratch array, and its device address on the
+// current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_paged_mqa_logits(const IdxArgs& a, hipStream_t stream);
 // positions == nullptr: the rope values are stored as given; else token t's rope is rotated back by the
 // angles of row positions[t] of cos_sin ([max_pos][64] fp32: 32 cosines, then 32 sines).
