@@ -487,6 +487,32 @@ def attention_rows(q_bits: np.ndarray, kv: np.ndarray, kv_dtype: int, block_tabl
     return O, LSE
 
 
+def attention_rows_with_window(q_bits: np.ndarray, kv: np.ndarray, kv_dtype: int, block_table: np.ndarray,
+                               idx: np.ndarray, kv_win: np.ndarray, block_table_win: np.ndarray,
+                               idx_win: np.ndarray, row_req: Optional[Sequence[int]], scale: float,
+                               rows: Optional[Sequence[int]] = None,
+                               sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode attention over compressed and sliding-window KV in one softmax ("[DeepSeek-V4][Preview]
+    Batch-invariant kernels for 0-diff RL", section "Sparse MLA and FlashMLA": decode gathers
+    compressed and sliding-window KV; "[Bugfix] Make DSV4 sparse MLA work end-to-end ...", section
+    "Purpose", item "SWA widths": the window + draft index width is padded to a multiple of the
+    64-entry tile).  Row r attends to the tokens listed in ``idx[r]`` (logical positions in the
+    paged cache ``kv`` of its request, through ``block_table``) together with the tokens listed in
+    ``idx_win[r]`` (logical positions in the paged window cache ``kv_win``, through
+    ``block_table_win``): one set of keys, one softmax, entries -1 skipped.  Same arithmetic as
+    ``attention`` over that set."""
+    sel = list(range(idx.shape[0])) if rows is None else list(rows)
+    H = q_bits.shape[1]
+    O = np.zeros((len(sel), H, D_V))
+    LSE = np.zeros((len(sel), H))
+    for o, r in enumerate(sel):
+        req = 0 if row_req is None else int(row_req[r])
+        K1 = gather_tokens(kv, kv_dtype, block_table[req], [int(p) for p in idx[r] if p >= 0])
+        K2 = gather_tokens(kv_win, kv_dtype, block_table_win[req], [int(p) for p in idx_win[r] if p >= 0])
+        O[o], LSE[o] = attention(bf16_to_f64(q_bits[r]), np.concatenate([K1, K2], axis=0), scale, sink)
+    return O, LSE
+
+
 def decode_rows(q_bits, kv, kv_dtype, block_table, row_req, scores, lengths, k, scale,
                 rows=None, row_offsets=None, row_stride=None):
     """The whole decode path for the requested rows: (indices, O, LSE)."""

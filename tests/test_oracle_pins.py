@@ -764,6 +764,88 @@ def test_decode_rows_composes_selection_gather_and_attention():
     np.testing.assert_allclose(Oo[0], p @ Kd[:, :512], atol=1e-13)
 
 
+# Attention over compressed + sliding-window KV (two paged caches, one softmax).
+
+def _two_cache_case(seed=51, H=4):
+    """A main cache and a window cache, one request, small index lists."""
+    rng = np.random.default_rng(seed)
+    def cache(pages):
+        vals = rng.standard_normal((pages, 64, 576)).astype(np.float32)
+        return _bf16_rne_bits(vals).view(np.uint8).reshape(pages, 64, 1152)
+    kv, kvw = cache(4), cache(4)
+    bt = np.array([[2, 0, 3, 1]], np.int32)
+    btw = np.array([[0, 0, 2, 1]], np.int32)                 # logical pages 0, 1 evicted (null page 0)
+    q = _bf16_rne_bits(rng.standard_normal((1, H, 576)).astype(np.float32))
+    idx = np.array([[3, 70, 130, 200, -1, -1]], np.int32)
+    idxw = np.array([[150, 151, 190, 250, -1, -1, -1, -1]], np.int32)
+    return q, kv, bt, idx, kvw, btw, idxw
+
+
+def test_window_attention_is_attention_over_the_union():
+    q, kv, bt, idx, kvw, btw, idxw = _two_cache_case()
+    Ow, L = O.attention_rows_with_window(q, kv, O.KV_BF16, bt, idx, kvw, btw, idxw, [0], 1 / 24)
+    K1 = np.stack([O.bf16_to_f64(kv.reshape(-1, 1152)[bt[0][p // 64] * 64 + p % 64].view(np.uint16))
+                   for p in idx[0] if p >= 0])
+    K2 = np.stack([O.bf16_to_f64(kvw.reshape(-1, 1152)[btw[0][p // 64] * 64 + p % 64].view(np.uint16))
+                   for p in idxw[0] if p >= 0])
+    K = np.concatenate([K1, K2])
+    # dense softmax attention written out with torch in float64
+    qt = torch.from_numpy(O.bf16_to_f64(q[0]))
+    Kt = torch.from_numpy(K)
+    s = (qt @ Kt.T) / 24
+    p = torch.softmax(s, dim=1)
+    np.testing.assert_allclose(Ow[0], (p @ Kt[:, :512]).numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L[0], torch.logsumexp(s, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_window_attention_special_cases():
+    q, kv, bt, idx, kvw, btw, idxw = _two_cache_case(52)
+    # an empty window list is the plain sparse attention over the main cache
+    none_w = np.full_like(idxw, -1)
+    a = O.attention_rows_with_window(q, kv, O.KV_BF16, bt, idx, kvw, btw, none_w, [0], 1 / 24)
+    b = O.attention_rows(q, kv, O.KV_BF16, bt, [0], idx, 1 / 24)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    # an empty main list is attention over the window cache alone
+    none = np.full_like(idx, -1)
+    a = O.attention_rows_with_window(q, kv, O.KV_BF16, bt, none, kvw, btw, idxw, [0], 1 / 24)
+    b = O.attention_rows(q, kvw, O.KV_BF16, btw, [0], idxw, 1 / 24)
+    np.testing.assert_array_equal(a[0], b[0])
+    # the union splits into two disjoint parts whose LSE-weighted combination is the whole
+    w = O.attention_rows_with_window(q, kv, O.KV_BF16, bt, idx, kvw, btw, idxw, [0], 1 / 24)
+    p1 = O.attention_rows(q, kv, O.KV_BF16, bt, [0], idx, 1 / 24)
+    p2 = O.attention_rows(q, kvw, O.KV_BF16, btw, [0], idxw, 1 / 24)
+    c = O.split_combine([(p1[0][0], p1[1][0]), (p2[0][0], p2[1][0])])
+    np.testing.assert_allclose(w[0][0], c[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(w[1][0], c[1], rtol=1e-12, atol=1e-13)
+    # a token moved from the window cache into the main cache (its index moved with it) changes nothing
+    kv2 = kv.copy()
+    src = btw[0][150 // 64] * 64 + 150 % 64
+    kv2.reshape(-1, 1152)[bt[0][4 // 64] * 64 + 4 % 64] = kvw.reshape(-1, 1152)[src]
+    idx2 = idx.copy(); idx2[0, 4] = 4
+    idxw2 = idxw.copy(); idxw2[0, 0] = -1
+    m = O.attention_rows_with_window(q, kv2, O.KV_BF16, bt, idx2, kvw, btw, idxw2, [0], 1 / 24)
+    np.testing.assert_allclose(m[0], w[0], rtol=1e-12, atol=1e-13)
+
+
+def _win_mutant_window_through_main_table(q, kv, kvd, bt, idx, kvw, btw, idxw, rq, scale):
+    return O.attention_rows_with_window(q, kv, kvd, bt, idx, kvw, bt, idxw, rq, scale)
+
+
+def _win_mutant_separate_softmax(q, kv, kvd, bt, idx, kvw, btw, idxw, rq, scale):
+    a = O.attention_rows(q, kv, kvd, bt, rq, idx, scale)
+    b = O.attention_rows(q, kvw, kvd, btw, rq, idxw, scale)
+    return (a[0] + b[0]) / 2, np.logaddexp(a[1], b[1])
+
+
+@pytest.mark.parametrize("mutant", [_win_mutant_window_through_main_table, _win_mutant_separate_softmax])
+def test_pins_catch_window_mutants(mutant):
+    q, kv, bt, idx, kvw, btw, idxw = _two_cache_case()
+    good = O.attention_rows_with_window(q, kv, O.KV_BF16, bt, idx, kvw, btw, idxw, [0], 1 / 24)
+    bad = mutant(q, kv, O.KV_BF16, bt, idx, kvw, btw, idxw, [0], 1 / 24)
+    assert not np.allclose(bad[0], good[0], rtol=1e-6, atol=1e-9)
+
+
 # Attention mutants, planted in copies of the oracle's attention on the CPU: each must fail a pin.
 
 def _att_mutant_v_tail(q, K, scale):            # value taken from the last 512 entries
