@@ -36,7 +36,7 @@ METRIC = "sparse-MLA decode rows/s + gathered-KV HBM GB/s (H=64, topk=2048, 1 GP
 METRIC_FP8 = "sparse-MLA decode rows/s + gathered-KV HBM GB/s (FP8 KV, B=128, H=64, topk=2048, 1 GPU)"
 HBM_PEAK_GBPS = 8000.0
 N_SETS = 4
-WORKLOADS = ["decode_bf16", "decode_fp8", "topk_c1", "kv_write_fp8", "decode_swa192", "prefill_c4", "indexer"]
+WORKLOADS = ["decode_bf16", "decode_fp8", "topk_c1", "kv_write_fp8", "decode_window", "prefill_c4", "indexer"]
 
 
 def parse():
@@ -56,8 +56,8 @@ def parse():
                          "topk_c1: top-k alone, 64 x 65536 fp32 rows of 256 distinct levels, k=2048, 32 rotating "
                          "copies (512 MiB, beyond the last-level cache); "
                          "kv_write_fp8: FP8 cache write of 65536 new tokens (and of 128, a decode step); "
-                         "decode_swa192: B=64 draft rows over 128 sliding-window + 5 draft positions, index "
-                         "width 192 (and the same rows at width 256); "
+                         "decode_window: the decode_bf16 rows plus 128 sliding-window + 5 draft positions "
+                         "per row from a separate window cache in one softmax, window width 192 (and 256); "
                          "prefill_c4: one request, T=4096 query tokens at positions 126976..131071 of a "
                          "131072-token context, causal top-k 2048 + prefill attention; "
                          "indexer: indexer scores (paged MQA logits) of B=64 decode rows, 64 index heads of "
@@ -561,10 +561,11 @@ def bench_kv_write(args):
     print(json.dumps(line), flush=True)
 
 
-def bench_swa(args):
-    """Attention over sliding-window + draft index rows: B = 64 rows, H = 64, each row 133 valid
-    positions (128 window + 5 draft) padded with -1 to width 192, and the same rows padded to 256.
-    Four rotating (Q, indices) sets over one bf16 KV pool of contexts U[8192, 65536]."""
+def bench_window(args):
+    """Decode over compressed and sliding-window KV: the decode_bf16 rows (B = 64, H = 64, top-k 2048 of
+    contexts U[8192, 65536]) plus, per row, its 128 window + 5 draft positions from a separate window
+    cache, one softmax (smla_sparse_mla_decode_with_window), window width 192 and the same rows at 256.
+    Four rotating (Q, scores) sets."""
     import torch
 
     import sparse_mla_attention_topk_amd as smla
@@ -572,38 +573,51 @@ def bench_swa(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B, H = 64, 64
     wl = W.decode_bf16(dev, n_sets=N_SETS)
-    ctx = wl.cache.ctx_lens.to(dev)
-    idx192 = W.swa_draft_indices(ctx)
-    idx256 = torch.full((B, 256), -1, dtype=torch.int32, device=dev)
-    idx256[:, :192] = idx192
+    B, H, k = wl.sets[0].q.shape[0], wl.H, wl.k
+    win = W.window_cache(wl.cache.ctx_lens, W.KV_BF16, dev, seed=61, max_pages=int(wl.cache.block_table.shape[1]))
+    idxw256 = torch.full((B, 256), -1, dtype=torch.int32, device=dev)
+    idxw256[:, :192] = win.idx
+    idx = [smla.topk_per_row(rs.scores, k, lengths=rs.lengths) for rs in wl.sets]
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    s = torch.cuda.Stream(dev)
+    ws = smla.attention_workspace(B, H, k + 256, dev)
+    tws = smla.topk_workspace(B, k, wl.sets[0].scores.shape[1], dev)
 
-    def call(idx):
-        return lambda i: smla.sparse_mla_decode(wl.sets[i % N_SETS].q, wl.cache.kv, wl.cache.block_table, idx,
-                                                wl.scale, row_req=wl.sets[i % N_SETS].row_req, out=out, lse=lse)
+    def attn(iw):
+        def f(i):
+            rs = wl.sets[i % N_SETS]
+            smla.sparse_mla_decode_with_window(rs.q, wl.cache.kv, wl.cache.block_table, idx[i % N_SETS], win.kv,
+                                              win.block_table, iw, wl.scale, row_req=rs.row_req, out=out, lse=lse,
+                                              workspace=ws)
+        return f
+
+    def step(i):
+        rs = wl.sets[i % N_SETS]
+        smla.topk_per_row(rs.scores, k, lengths=rs.lengths, out=idx[i % N_SETS], workspace=tws)
+        attn(win.idx)(i)
     for i in range(N_SETS):
-        call(idx192)(i)
-        call(idx256)(i)
+        step(i)
+        attn(idxw256)(i)
     torch.cuda.synchronize()
+    s = torch.cuda.Stream(dev)
     g = not args.no_graph
-    ms192, reps = _timed_calls(torch, s, call(idx192), args.steps, args.warmup, args.min_timed_ms, g)
-    ms256, _ = _timed_calls(torch, s, call(idx256), args.steps, args.warmup, args.min_timed_ms, g)
-    valid = int((idx192 >= 0).sum())
-    gathered = valid * W.BF16_RECORD_BYTES
+    step_ms, reps = _timed_calls(torch, s, step, args.steps, args.warmup, args.min_timed_ms, g)
+    ms192, _ = _timed_calls(torch, s, attn(win.idx), args.steps, args.warmup, args.min_timed_ms, g)
+    ms256, _ = _timed_calls(torch, s, attn(idxw256), args.steps, args.warmup, args.min_timed_ms, g)
+    valid_w = int((win.idx >= 0).sum())
+    gathered = (B * k + valid_w) * W.BF16_RECORD_BYTES
     achieved = gathered / (ms192 * 1e-3) / 1e9
-    line = _base_line(args, "sparse-MLA decode rows/s, sliding-window + draft rows (128 + 5 valid, index width 192, "
-                            "H=64, 1 GPU)", B / (ms192 * 1e-3), "rows/s", ms192, reps, "bf16",
-                      {"workload": "decode_swa192_B64_H64", "rows": B, "heads": H, "index_width": 192,
-                       "valid_per_row": 133, "rotating_sets": N_SETS, "launch": "hip_graph_of_K_calls"})
+    line = _base_line(args, "sparse-MLA decode rows/s over top-k 2048 + sliding-window 128 + draft 5 KV (width 192, "
+                            "H=64, 1 GPU)", B / (step_ms * 1e-3), "rows/s", step_ms, reps, "bf16",
+                      {"workload": "decode_window_B64_H64_k2048_w192", "rows": B, "heads": H, "topk": k,
+                       "window_width": 192, "window_valid_per_row": 133, "rotating_sets": N_SETS,
+                       "launch": "hip_graph_of_K_steps"})
     line.update({
         "attention_us_width192": ms192 * 1e3, "attention_us_width256": ms256 * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "sparse_mla_decode call (one split: attention kernel only)",
+                     "kernel": "sparse_mla_decode_with_window call: attention kernel + split-combine kernel",
                      "algorithmic_bytes_per_launch": gathered},
         "cpu_baseline": None,
     })
@@ -749,8 +763,8 @@ def main():
     try:
         if args.workload == "kv_write_fp8":
             return bench_kv_write(args)
-        if args.workload == "decode_swa192":
-            return bench_swa(args)
+        if args.workload == "decode_window":
+            return bench_window(args)
         if args.workload == "prefill_c4":
             return bench_prefill(args)
         if args.workload == "indexer":

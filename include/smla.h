@@ -128,6 +128,7 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
                               void* ws, size_t ws_bytes, void* stream);
 
 /* A4-A11, sparse MLA attention over canonical indices (decode rows, or any mix of rows).
+ * (smla_sparse_mla_decode_with_window below adds a sliding-window cache to the same call.)
  *   q:      bf16 [rows, H, 576], row r at q + r*q_row_stride elements (q_row_stride >= H*576,
  *           multiple of 8); 16-byte aligned.
  *   kv:     paged cache, [num_pages, 64, record] bytes per kv_dtype; 16-byte aligned.
@@ -159,6 +160,28 @@ smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const vo
                                    int32_t num_reqs, const int32_t* row_req, const int32_t* idx,
                                    int32_t rows, int32_t H, int32_t k, float softmax_scale, const float* sink,
                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode over compressed and sliding-window KV in one softmax.
+ * Sources: "[DeepSeek-V4][Preview] Batch-invariant kernels for 0-diff RL", section "Sparse MLA and
+ * FlashMLA" (decode gathers compressed and sliding-window KV); "[Bugfix] Make DSV4 sparse MLA work
+ * end-to-end ...", section "Purpose", item "SWA widths" (the window + draft width pads to a multiple of
+ * the 64-entry tile: 192 for 128 window + 5 draft entries).
+ *   Row r attends to the k positions idx[r*k ...] of the main paged cache kv (through block_table) and
+ *   to the k_win positions idx_win[r*k_win ...] of the window cache kv_win (through block_table_win,
+ *   [num_reqs, bt_win_stride], num_pages_win pages, the same record type and request ids row_req):
+ *   one set of keys, one softmax, entries < 0 skipped; everything else (arithmetic, sink, lse, invalid
+ *   entries, batch invariance) as smla_sparse_mla_decode over a row of k + k_win slots, the window slots
+ *   last.  The reduction order depends on k, k_win and kv_dtype only.
+ *   Requires k >= 1, k_win a positive multiple of 64, k + k_win <= 16384; the workspace is that of
+ *   smla_sparse_mla_decode at width k + k_win (smla_workspace_size with max_k >= k + k_win). */
+smla_status smla_sparse_mla_decode_with_window(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
+                                              int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                              const int32_t* idx, int32_t k, const void* kv_win,
+                                              int64_t num_pages_win, const int32_t* block_table_win,
+                                              int64_t bt_win_stride, const int32_t* idx_win, int32_t k_win,
+                                              int32_t num_reqs, const int32_t* row_req, int32_t rows, int32_t H,
+                                              float softmax_scale, const float* sink, void* out, float* lse,
+                                              void* ws, size_t ws_bytes, void* stream);
 
 /* smla_sparse_mla_decode without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments,

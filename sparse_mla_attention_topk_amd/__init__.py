@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "SmlaError", "KV_BF16", "KV_FP8", "Capacity", "library_path", "load_library", "exported_symbols",
     "version", "is_supported", "workspace_size", "fill_causal_lengths", "topk_per_row", "topk_workspace",
-    "sparse_mla_decode", "sparse_mla_decode_noalloc", "sparse_mla_prefill_chunk", "kv_cache_write",
+    "sparse_mla_decode", "sparse_mla_decode_noalloc", "sparse_mla_decode_with_window", "sparse_mla_prefill_chunk",
+    "kv_cache_write",
     "paged_mqa_logits",
 ]
 
@@ -31,7 +32,7 @@ exported_symbols = (
     "smla_last_error", "smla_version", "smla_is_supported", "smla_workspace_size",
     "smla_fill_causal_lengths", "smla_topk_per_row", "smla_sparse_mla_decode",
     "smla_sparse_mla_prefill_chunk", "smla_kv_cache_write", "smla_kv_cache_write_rope", "smla_paged_mqa_logits",
-    "smla_sparse_mla_decode_noalloc",
+    "smla_sparse_mla_decode_noalloc", "smla_sparse_mla_decode_with_window",
 )
 
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED", 3: "SMLA_ERR_WORKSPACE",
@@ -83,6 +84,8 @@ def load_library() -> ctypes.CDLL:
                                           ctypes.c_int),
         "smla_sparse_mla_decode_noalloc": ([P, I64, P, I32, I64, P, I64, I32, P, P, I32, I32, I32, F32, P, P, P, P],
                                            ctypes.c_int),
+        "smla_sparse_mla_decode_with_window": ([P, I64, P, I32, I64, P, I64, P, I32, P, I64, P, I64, P, I32, I32, P,
+                                                I32, I32, F32, P, P, P, P, SZ, P], ctypes.c_int),
         "smla_kv_cache_write": ([P, I64, P, I32, P, I32, I64, P], ctypes.c_int),
         "smla_kv_cache_write_rope": ([P, I64, P, P, P, I64, I32, P, I32, I64, P], ctypes.c_int),
         "smla_paged_mqa_logits": ([P, I64, P, I64, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P], ctypes.c_int),
@@ -271,6 +274,48 @@ def sparse_mla_decode(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tens
                                       _ptr(bt2), bt2.shape[1], bt2.shape[0], _ptr(row_req), _ptr(idx), rows, H, k,
                                       float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace),
                                       ws_bytes, _stream(dev)))
+    return out, lse
+
+
+def sparse_mla_decode_with_window(q: torch.Tensor, kv: torch.Tensor, block_table: torch.Tensor, idx: torch.Tensor,
+                                  kv_win: torch.Tensor, block_table_win: torch.Tensor, idx_win: torch.Tensor,
+                                  softmax_scale: float, row_req: Optional[torch.Tensor] = None,
+                                  kv_dtype: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                  sink: Optional[torch.Tensor] = None):
+    """Sparse MLA attention of each row over the tokens ``idx`` [rows, k] of the main cache ``kv`` and
+    the tokens ``idx_win`` [rows, k_win] (k_win a multiple of 64) of the window cache ``kv_win``, in one
+    softmax.  ``block_table`` / ``block_table_win`` int32 [num_reqs, *]; ``row_req`` indexes both.
+    Returns (out bf16 [rows, H, 512], lse fp32 [rows, H] or None)."""
+    lib = load_library()
+    _require(q, "q", torch.bfloat16, contiguous=False)
+    if q.dim() != 3 or q.shape[2] != 576 or q.stride(2) != 1 or q.stride(1) != 576:
+        raise ValueError("q must be [rows, H, 576] with contiguous heads")
+    dev = q.device
+    for t, nm in ((kv, "kv"), (kv_win, "kv_win")):
+        _require(t, nm, torch.uint8, dev)
+    for t, nm in ((block_table, "block_table"), (block_table_win, "block_table_win"), (idx, "idx"),
+                  (idx_win, "idx_win")):
+        _require(t, nm, torch.int32, dev)
+    rows, H = q.shape[0], q.shape[1]
+    k, k_win = idx.shape[-1], idx_win.shape[-1]
+    if idx.numel() < rows * k or idx_win.numel() < rows * k_win:
+        raise ValueError("idx / idx_win are smaller than rows*k / rows*k_win")
+    if block_table.dim() != 2 or block_table_win.dim() != 2 or block_table.shape[0] != block_table_win.shape[0]:
+        raise ValueError("block_table and block_table_win must be 2-D with one row per request")
+    if row_req is not None:
+        _require(row_req, "row_req", torch.int32, dev)
+    _check_sink(sink, H, dev)
+    out, lse = _attn_outputs(rows, H, dev, out, lse)
+    dt = _kv_dtype_of(kv, kv_dtype)
+    if workspace is None:
+        workspace = attention_workspace(rows, H, k + k_win, dev, dt)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.smla_sparse_mla_decode_with_window(
+        _ptr(q), q.stride(0), _ptr(kv), dt, kv.shape[0], _ptr(block_table), block_table.shape[1], _ptr(idx), k,
+        _ptr(kv_win), kv_win.shape[0], _ptr(block_table_win), block_table_win.shape[1], _ptr(idx_win), k_win,
+        block_table.shape[0], _ptr(row_req), rows, H, float(softmax_scale), _ptr(sink), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(dev)))
     return out, lse
 
 

@@ -221,6 +221,51 @@ smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const vo
     return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_decode");
 }
 
+smla_status smla_sparse_mla_decode_with_window(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
+                                              int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
+                                              const int32_t* idx, int32_t k, const void* kv_win,
+                                              int64_t num_pages_win, const int32_t* block_table_win,
+                                              int64_t bt_win_stride, const int32_t* idx_win, int32_t k_win,
+                                              int32_t num_reqs, const int32_t* row_req, int32_t rows, int32_t H,
+                                              float softmax_scale, const float* sink, void* out, float* lse,
+                                              void* ws, size_t ws_bytes, void* stream) {
+    if (k_win < 64 || k_win % 64 != 0)
+        return fail(SMLA_ERR_UNSUPPORTED, "k_win=%d is not supported; supported: a positive multiple of 64 (the "
+                    "64-entry tile: 192 for 128 window + 5 draft entries)", k_win);
+    if (k < 1 || (int64_t)k + k_win > kMaxK)
+        return fail(SMLA_ERR_UNSUPPORTED, "k=%d with k_win=%d is not supported; supported: k >= 1 and k + k_win <= %d",
+                    k, k_win, kMaxK);
+    // the whole row (k + k_win slots) is validated as one index list of the main cache ...
+    smla_status st = check_attention(q, q_row_stride, kv, kv_dtype, num_pages, block_table, bt_stride, num_reqs, idx,
+                                     rows, H, k + k_win, softmax_scale, out, lse, ws, ws_bytes);
+    if (st != SMLA_OK) return st;
+    // ... and the window cache on its own
+    if (num_pages_win < 1) return fail(SMLA_ERR_INVALID_ARG, "num_pages_win=%lld must be >= 1", (long long)num_pages_win);
+    if (num_pages_win > kMaxPages)
+        return fail(SMLA_ERR_CAPACITY, "num_pages_win=%lld exceeds the supported maximum %lld", (long long)num_pages_win,
+                    (long long)kMaxPages);
+    if (bt_win_stride < 1) return fail(SMLA_ERR_INVALID_ARG, "bt_win_stride=%lld must be >= 1", (long long)bt_win_stride);
+    if (rows == 0) return ok();
+    if (!kv_win) return fail(SMLA_ERR_INVALID_ARG, "kv_win is NULL");
+    if (!block_table_win) return fail(SMLA_ERR_INVALID_ARG, "block_table_win is NULL");
+    if (!idx_win) return fail(SMLA_ERR_INVALID_ARG, "idx_win is NULL");
+    if (!aligned(kv_win, 16)) return fail(SMLA_ERR_ALIGNMENT, "kv_win must be 16-byte aligned");
+    if (!aligned(block_table_win, 4)) return fail(SMLA_ERR_ALIGNMENT, "block_table_win must be 4-byte aligned");
+    if (!aligned(idx_win, 4)) return fail(SMLA_ERR_ALIGNMENT, "idx_win must be 4-byte aligned");
+    if (row_req && !aligned(row_req, 4)) return fail(SMLA_ERR_ALIGNMENT, "row_req must be 4-byte aligned");
+    if (sink && !aligned(sink, 4)) return fail(SMLA_ERR_ALIGNMENT, "sink must be 4-byte aligned");
+    smla::AttnArgs a{q,   q_row_stride, kv,  kv_dtype,      num_pages, block_table, bt_stride, num_reqs, row_req,
+                     idx, rows,         H,   k,             softmax_scale, sink,    out,       lse,      ws,
+                     ws_bytes};
+    a.kv_win = kv_win;
+    a.num_pages_win = num_pages_win;
+    a.block_table_win = block_table_win;
+    a.bt_win_stride = bt_win_stride;
+    a.idx_win = idx_win;
+    a.k_win = k_win;
+    return hip_status(smla::launch_attention(a, (hipStream_t)stream), "sparse_mla_decode_with_window");
+}
+
 smla_status smla_sparse_mla_decode_noalloc(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,
                                            int64_t num_pages, const int32_t* block_table, int64_t bt_stride,
                                            int32_t num_reqs, const int32_t* row_req, const int32_t* idx,

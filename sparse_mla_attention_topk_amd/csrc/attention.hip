@@ -39,7 +39,7 @@
 // each writes its normalized partial (O_s rounded to bf16, lse_s in fp32) to the workspace, and a
 // combine kernel merges the splits of a row in split order.  Nothing uses floating-point atomics.
 //
-// Invalid slots (index < 0, request/page out of range) load a valid dummy record, are zeroed in
+// Invalid slots (index < 0, request/page out of range) load record 0 of their cache, are zeroed in
 // LDS after arrival and get score -inf, so every loading wave issues the same number of direct-to-LDS
 // loads for every tile and the vmcnt bookkeeping below stays exact.
 #include <math.h>
@@ -57,6 +57,7 @@ constexpr int kAttnThreads = kAttnWaves * kWave;               // 1024
 constexpr int kScoreWaves = 8;
 constexpr int kTileTok = 32;
 constexpr int kTilesPerSplit = kSplitSlots / kTileTok;         // 16
+constexpr int kMaxUnitTiles = kMaxUnitSlots / kTileTok;        // 24
 constexpr int kStageBytes = kTileTok * kBf16Record;             // 36864
 constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-LDS loads of 1 KB per tile
 static_assert(kTileLoads * 16 * kWave == kStageBytes, "tile must split into whole wave loads");
@@ -87,10 +88,17 @@ struct AttnParams {
     int32_t num_reqs;
     const int32_t* row_req;
     const int32_t* idx;
-    int32_t k;
+    int32_t k;              // slots of a row: k_main from idx over kv, then k - k_main from idx_win over kv_win
+    int32_t k_main;
+    const uint8_t* kv_win;  // sliding-window cache (null: none)
+    int64_t num_pages_win;
+    const int32_t* block_table_win;
+    int64_t bt_win_stride;
+    const int32_t* idx_win;
     int32_t H;
     int32_t n_splits;       // splits of a row (one softmax state and one partial each)
-    int32_t n_units;        // 512-slot units of a row (a split is 1 unit, FP8: 2)
+    int32_t n_units;        // units of a row (a split is 1 unit, FP8: 2)
+    int32_t unit_slots;     // slots of a unit: 512, or a larger multiple of 64 (<= 768) with a window part
     int32_t n_hblocks;
     int32_t heads_per_wg;   // 64, 32 or 16: heads of one workgroup (each head's arithmetic is the same)
     int32_t units_per_wg;   // 1, 2 or 4 consecutive units of a row run by one workgroup, one after the other
@@ -182,8 +190,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
     // Units run by one workgroup (FP8: the 2 units of its split) and their slots' physical records.
     constexpr int kMaxGroup = KV_FP8 ? 2 : 4;
-    __shared__ uint32_t phys[kMaxGroup * kSplitSlots];
-    __shared__ uint32_t tile_valid[kMaxGroup * kTilesPerSplit];
+    __shared__ uint32_t phys[kMaxGroup * kMaxUnitSlots];
+    __shared__ uint32_t tile_valid[kMaxGroup * kMaxUnitTiles];
     // Weights of each head block: bf16 B-operand fragments (bf16 caches), or the lane's 8 fp32
     // weights (FP8 caches; each value wave scales them by its group's token scales).
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
@@ -241,42 +249,52 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // ---- A4: translate the slots of this workgroup's splits to physical token records: local slot j
     // (split j / 512 of the group) is slot 512 split0 + j of the row.  Each thread owns local slots tid
     // and tid + 1024; both index loads go out before either page-table load. ----
-    const int slot_base = split0 * kSplitSlots;
-    const int nslot = min(ns * kSplitSlots, p.k - slot_base);
+    const int U = p.unit_slots;                  // slots per unit (a multiple of 64)
+    const int slot_base = split0 * U;
+    const int nslot = min(ns * U, p.k - slot_base);
     const int req = p.row_req ? p.row_req[row] : 0;
     const bool req_ok = req >= 0 && req < p.num_reqs;
-    if (tid < kMaxGroup) { s_first[tid] = kSplitSlots; s_last[tid] = -1; }
-    if (tid < kMaxGroup * kTilesPerSplit) tile_valid[tid] = 0u;
+    if (tid < kMaxGroup) { s_first[tid] = U; s_last[tid] = -1; }
+    if (tid < kMaxGroup * kMaxUnitTiles) tile_valid[tid] = 0u;
     __syncthreads();
     {
-        constexpr int kRounds = (kMaxGroup * kSplitSlots + kAttnThreads - 1) / kAttnThreads;   // 1 or 2
+        // Row slots [0, k_main) list positions of the main cache (idx, block_table); slots [k_main, k)
+        // list positions of the window cache (idx_win, block_table_win).
+        constexpr int kRounds = (kMaxGroup * kMaxUnitSlots + kAttnThreads - 1) / kAttnThreads;   // 2 or 3
+        const int k_win = p.k - p.k_main;
         int32_t pos[kRounds];
 #pragma unroll
         for (int r = 0; r < kRounds; ++r) {
             const int j = tid + kAttnThreads * r;
-            pos[r] = p.idx[row * p.k + slot_base + (j < nslot ? j : 0)];
+            const int gs = slot_base + (j < nslot ? j : 0);
+            const int32_t* ip = gs < p.k_main ? p.idx + row * p.k_main + gs : p.idx_win + row * k_win + (gs - p.k_main);
+            pos[r] = *ip;
         }
 #pragma unroll
         for (int r = 0; r < kRounds; ++r) {
             const int j = tid + kAttnThreads * r;
-            if (j >= ns * kSplitSlots) break;   // uniform in the wave (64 divides 512)
+            if (j >= ns * U) break;   // uniform in the wave (64 divides U)
             int32_t ps = pos[r];
             if (!(j < nslot && req_ok)) ps = -1;
+            const bool win = slot_base + j >= p.k_main;
+            const int32_t* bt = win ? p.block_table_win : p.block_table;
+            const int64_t bts = win ? p.bt_win_stride : p.bt_stride;
+            const int64_t npg = win ? p.num_pages_win : p.num_pages;
             uint32_t ph = kNoToken;
             const int64_t lp = ps >> 6;
-            if (ps >= 0 && lp < p.bt_stride) {
-                const int32_t pg = p.block_table[(int64_t)req * p.bt_stride + lp];
-                if (pg >= 0 && (int64_t)pg < p.num_pages) ph = (uint32_t)pg * kPage + (uint32_t)(ps & (kPage - 1));
+            if (ps >= 0 && lp < bts) {
+                const int32_t pg = bt[(int64_t)req * bts + lp];
+                if (pg >= 0 && (int64_t)pg < npg) ph = (uint32_t)pg * kPage + (uint32_t)(ps & (kPage - 1));
             }
             phys[j] = ph;
             const uint64_t vbits = __ballot(ph != kNoToken);
             if (lane == 0 && vbits) {
                 const int jw = j - lane;                        // first slot of this wave's 64
-                const int ls = jw / kSplitSlots, jl = jw % kSplitSlots;
+                const int ls = jw / U, jl = jw % U;
                 atomicMin(&s_first[ls], jl + (int)__builtin_ctzll(vbits));
                 atomicMax(&s_last[ls], jl + 63 - (int)__builtin_clzll(vbits));
-                atomicOr(&tile_valid[ls * kTilesPerSplit + jl / kTileTok], (uint32_t)vbits);
-                atomicOr(&tile_valid[ls * kTilesPerSplit + jl / kTileTok + 1], (uint32_t)(vbits >> 32));
+                atomicOr(&tile_valid[ls * kMaxUnitTiles + jl / kTileTok], (uint32_t)vbits);
+                atomicOr(&tile_valid[ls * kMaxUnitTiles + jl / kTileTok + 1], (uint32_t)(vbits >> 32));
             }
         }
     }
@@ -329,23 +347,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // since a split with at least two tiles requests the next split's tiles 0 and 1 in the slots where
     // its own tiles ntiles and ntiles + 1 would go (pf), so the next split starts with them in flight.
     int cur = 0, ntiles = 0, cur_slot0 = 0, sbase = 0, nx_ntiles = 0;
-    uint32_t dummy = 0u, nx_dummy = 0u;
     bool pf = false, pref_done = false;   // this split requests the next one's first tiles / was requested
     auto split_tiles = [&](int ls) {
         const int last = s_last[ls];
         return __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / kTileTok + 1);
     };
-    auto split_dummy = [&](int ls) {
-        const int last = s_last[ls];
-        return __builtin_amdgcn_readfirstlane(last < 0 ? 0u : phys[ls * kSplitSlots + s_first[ls]]);
-    };
     auto begin_split = [&](int ls) {
         cur = ls;
-        cur_slot0 = ls * kSplitSlots;
+        cur_slot0 = ls * U;
         ntiles = split_tiles(ls);
-        dummy = split_dummy(ls);
         nx_ntiles = ls + 1 < ns ? split_tiles(ls + 1) : 0;
-        nx_dummy = ls + 1 < ns ? split_dummy(ls + 1) : 0u;
         pf = ntiles >= 2 && nx_ntiles >= 1;
     };
     auto end_split = [&]() {
@@ -392,17 +403,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     };
     const uint32_t ring_lds = lds_offset(ring);
     const bool half_load = KV_FP8 && lw + kLoadWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
-    auto issue_tile_of = [&](int slot0, uint32_t dmy, int tile, int stage) {
+    // Slots at or past k_main of the row (the window part) read the window cache; an invalid slot loads
+    // record 0 of its cache (always present: num_pages >= 1), whose bytes are replaced by zeros.
+    // (slot0 + tile * 32 is the tile's first slot in the group; the group starts at row slot slot_base.)
+    auto issue_tile_of = [&](int slot0, int tile, int stage) {
         if (KV_FP8 && nload == 0) return;
         const uint8_t* phys_tile = (const uint8_t*)(phys + slot0 + tile * kTileTok);
         uint32_t dtok[kMaxLoadsPerWave], doff[kMaxLoadsPerWave];
         load_offsets(dtok, doff);
         const uint8_t* src[kMaxLoadsPerWave];
+        const int win_from = p.k_main - (slot_base + slot0 + tile * kTileTok);   // tile tokens >= this: window
 #pragma unroll
         for (int r = 0; r < kMaxLoadsPerWave; ++r) {   // all slot reads first: the asm below is a compiler barrier
             uint32_t ph = *(const uint32_t*)(phys_tile + dtok[r]);
-            ph = ph == kNoToken ? dmy : ph;
-            src[r] = p.kv + (uint64_t)ph * kRecBytes + doff[r];
+            ph = ph == kNoToken ? 0u : ph;
+            src[r] = ((int)(dtok[r] >> 2) >= win_from ? p.kv_win : p.kv) + (uint64_t)ph * kRecBytes + doff[r];
         }
         const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)lw;
         if (!KV_FP8) {
@@ -419,15 +434,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             }
         }
     };
-    auto issue_tile = [&](int tile, int stage) { issue_tile_of(cur_slot0, dummy, tile, stage); };
+    auto issue_tile = [&](int tile, int stage) { issue_tile_of(cur_slot0, tile, stage); };
     // The request that would be tile `t` of this split (t >= ntiles) is tile t - ntiles of the next split.
     auto issue_ahead = [&](int t) {
         if (t < ntiles) issue_tile(t, stg(t));
-        else if (pf && t - ntiles < nx_ntiles) issue_tile_of(cur_slot0 + kSplitSlots, nx_dummy, t - ntiles, stg(t));
+        else if (pf && t - ntiles < nx_ntiles) issue_tile_of(cur_slot0 + U, t - ntiles, stg(t));
     };
     // bf16: zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
-        const uint32_t vm = tile_valid[cur * kTilesPerSplit + tile];
+        const uint32_t vm = tile_valid[cur * kMaxUnitTiles + tile];
         if (vm != 0xffffffffu) {
             uint8_t* sbase = ring + stage * kStageBytes;
 #pragma unroll
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     auto dequant_tile = [&](int tile, int stage) {
         const uint8_t* st = ring + stage * kFp8StageBytes;
         uint8_t* const btile = btile_of(tile);
-        const uint32_t vm = tile_valid[cur * kTilesPerSplit + tile];
+        const uint32_t vm = tile_valid[cur * kMaxUnitTiles + tile];
         // Invalid tokens are cleared with a bit mask (a select between vectors would go through
         // scratch memory, whose wait would also wait for the tile loads in flight).
         int u = tid;
@@ -633,7 +648,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             // ---- A8: online softmax of the first-half waves' 16 heads ----
             if (score_ok && !half) {
                 const f32x4_t t0 = xs(shb, 0)[lane], t1 = xs(shb, 1)[lane];
-                const uint32_t vmask = tile_valid[cur * kTilesPerSplit + it];
+                const uint32_t vmask = tile_valid[cur * kMaxUnitTiles + it];
                 // lane: head (lane & 15), tokens 4g + i (block 0) and 16 + 4g + i (block 1)
                 float sv[8];
 #pragma unroll
@@ -1017,10 +1032,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.num_reqs = a.num_reqs;
     p.row_req = a.row_req;
     p.idx = a.idx;
-    p.k = a.k;
+    p.k = a.k + a.k_win;
+    p.k_main = a.k;
+    // Without a window cache the window fields repeat the main cache's (no slot selects them).
+    const bool has_win = a.k_win > 0;
+    p.kv_win = (const uint8_t*)(has_win ? a.kv_win : a.kv);
+    p.num_pages_win = has_win ? a.num_pages_win : a.num_pages;
+    p.block_table_win = has_win ? a.block_table_win : a.block_table;
+    p.bt_win_stride = has_win ? a.bt_win_stride : a.bt_stride;
+    p.idx_win = has_win ? a.idx_win : a.idx;
     p.H = a.H;
-    p.n_splits = attn_num_splits(a.k, a.kv_dtype);
-    p.n_units = attn_num_units(a.k);
+    const bool fp8 = a.kv_dtype == 1;
+    p.unit_slots = attn_unit_slots(a.k, a.k_win);
+    p.n_units = (p.k + p.unit_slots - 1) / p.unit_slots;
+    p.n_splits = fp8 ? (p.n_units + kFp8UnitsPerSplit - 1) / kFp8UnitsPerSplit : p.n_units;
     // Launches with fewer (row, split) items than CUs split the heads over 2 or 4 workgroups (each of
     // which gathers the same records): a head's arithmetic does not depend on the heads it shares a
     // workgroup with, so the results are the same bits either way.
@@ -1030,22 +1055,22 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
     p.sink = a.sink;
-    const size_t per_row = attn_ws_bytes_per_row(a.H, a.k, a.kv_dtype);
+    // Workspace per row: partials of every (split, head), then their LSEs (none with one split).  The
+    // host validation sizes it for 512-slot units, at least as many splits as any unit size here.
+    const size_t o_per_row = p.n_splits > 1 ? (size_t)p.n_splits * a.H * kDv * (fp8 ? 4 : 2) : 0;
+    const size_t per_row = p.n_splits > 1 ? o_per_row + (size_t)p.n_splits * a.H * sizeof(float) : 0;
     int rows_per_launch = a.rows;
     if (per_row > 0) {
         const size_t fit = a.ws_bytes / per_row;
         rows_per_launch = (int)(fit < (size_t)a.rows ? fit : (size_t)a.rows);
         if (rows_per_launch < 1) return hipErrorInvalidValue;   // host validation prevents this
     }
-    const bool fp8 = a.kv_dtype == 1;
     for (int row0 = 0; row0 < a.rows; row0 += rows_per_launch) {
         const int n = min(rows_per_launch, a.rows - row0);
         p.row0 = row0;
         // Workspace regions for a launch of rows_per_launch rows: partials, then LSEs.
         p.ws_o = per_row > 0 ? a.ws : nullptr;
-        p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch *
-                                                               attn_ws_o_bytes_per_row(a.H, a.k, a.kv_dtype))
-                               : nullptr;
+        p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch * o_per_row) : nullptr;
         // bf16: launches with at least twice as many (row, split) items as CUs run 2 or 4 consecutive
         // splits of a row per workgroup, one after the other: the index translation and Q serve them
         // all.  Each split reduces its own tiles in order with its own softmax state, so the bits are the

@@ -13,6 +13,18 @@ constexpr int kHeadsPerBlock = 64; // heads handled by one workgroup (4 waves x 
 constexpr int kFp8UnitsPerSplit = 2;   // FP8 caches: a split (one softmax state, one partial) is 2 units
 
 inline int attn_num_units(int k) { return (k + kSplitSlots - 1) / kSplitSlots; }
+// Calls with a sliding-window part (k_win > 0 slots after the k main ones) stretch the unit so that the
+// row keeps the unit count of its main part: units of ceil((k + k_win) / n / 64) * 64 slots for
+// n = ceil(k / 512) units (more units if that exceeds kMaxUnitSlots).  A function of k and k_win only.
+constexpr int kMaxUnitSlots = 768;
+inline int attn_unit_slots(int k, int k_win) {
+    if (k_win <= 0) return kSplitSlots;
+    const int total = k + k_win;
+    for (int n = (k + kSplitSlots - 1) / kSplitSlots;; ++n) {
+        const int u = ((total + n - 1) / n + 63) / 64 * 64;
+        if (u <= kMaxUnitSlots) return u;
+    }
+}
 // Splits of a row, each reduced by one workgroup before the split combine: units of 512 slots (bf16
 // caches) or pairs of them (FP8 caches, whose fp32 partials cost twice the bytes).  A function of k and
 // the cache type only, never of the batch.
@@ -55,6 +67,14 @@ struct AttnArgs {
     float* lse;
     void* ws;
     size_t ws_bytes;
+    // Optional sliding-window cache: row slots [k, k + k_win) list positions (idx_win [rows, k_win]) of
+    // kv_win through block_table_win; the same request ids (row_req, num_reqs) and record type.
+    const void* kv_win = nullptr;
+    int64_t num_pages_win = 0;
+    const int32_t* block_table_win = nullptr;
+    int64_t bt_win_stride = 0;
+    const int32_t* idx_win = nullptr;
+    int32_t k_win = 0;
 };
 
 // Indexer scores (paged MQA logits).

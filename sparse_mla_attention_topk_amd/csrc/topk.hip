@@ -242,14 +242,37 @@ __device__ __forceinline__ void wave_append_ge(const float* v, int32_t L, int32_
 }
 
 // LDS of one selecting workgroup.
+constexpr uint32_t kSmallBin = 128;  // a boundary bin of at most this many keys is resolved by ranking
+
 struct TopkShared {
     uint32_t hist[1 << 12];
     uint32_t scratch[kTopkWaves + 2];
     uint32_t res[3];
+    uint32_t krange[4];                      // min / max key of the list, then of the boundary bin
     uint32_t tbl[kTopkUnroll * kTopkWaves];
     uint32_t wcnt[kTopkThreads];             // per-wave candidate counts, then list offsets
+    uint32_t mem[kSmallBin];                 // keys of a small boundary bin
+    uint32_t mem_n;
     uint32_t cand_key[kCandCap], cand_idx[kCandCap];
 };
+
+// Minimum / maximum over the 64 lanes of a wave (every lane gets the result): DPP exchanges within
+// each row of 16 lanes (swap neighbours, swap pairs, mirror halves of 8, mirror the row), then the
+// cross-row swaps of lanes l <-> l^32 and l <-> l^16; VALU only, no LDS traffic.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = op(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return op(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_reduce_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_u32<true>(v); }
 
 // Filter threshold from the four sampled values per thread: a value tf such that, judging by the
 // sample, about 1.25 n + 4 sigma candidates of the row have v >= tf.  Returns false when the sample
@@ -290,8 +313,11 @@ __device__ __forceinline__ bool filter_eligible(int64_t L, int32_t n) {
 
 // Finishes a selection from the candidate list sm.cand_key (value bits) / sm.cand_idx (positions),
 // entries [0, total), which holds every selected candidate, in ascending position order, with
-// n <= total <= kCandCap: radix selection of the n-th key, then the output slot of each selected
-// candidate is the number of selected candidates before it in the list.
+// n <= total <= kCandCap.  The n-th key is found by radix selection on the keys relative to the
+// list's smallest key, with a first digit fitted to the list's key range (so the listed keys spread
+// over the 4096 bins instead of piling into a few LDS counters); a boundary bin whose keys are all
+// equal, or that holds at most kSmallBin keys, is settled directly (equal keys; ranking).  Then the
+// output slot of each selected candidate is the number of selected candidates before it in the list.
 template <class Src>
 __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int32_t n, int32_t k,
                                              int32_t* __restrict__ o, TopkShared& sm) {
@@ -299,65 +325,121 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
     uint32_t* scratch = sm.scratch;
     uint32_t* res = sm.res;
     uint32_t* cand_key = sm.cand_key;
-    uint32_t* cand_idx = sm.cand_idx;
-    // ---- radix selection of the n-th key among the listed candidates ----
+    const int lane = threadIdx.x & (kWave - 1);
     for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-    lds_barrier();
+    if (threadIdx.x == 0) {
+        sm.krange[0] = sm.krange[2] = 0xffffffffu;
+        sm.krange[1] = sm.krange[3] = 0u;
+        sm.mem_n = 0u;
+    }
     const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
     const uint32_t c0 = threadIdx.x * per;
     const uint32_t c1 = c0 + per < total ? c0 + per : total;
+    lds_barrier();                                   // the list is complete; hist cleared, range words set
+    // keys and their range
+    uint32_t lo = 0xffffffffu, hi = 0u;
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t key = score_key(__uint_as_float(cand_key[c]));
         cand_key[c] = key;
-        atomicAdd(&hist[key >> 20], 1u);
+        lo = min(lo, key);
+        hi = max(hi, key);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        atomicMin(&sm.krange[0], lo);
+        atomicMax(&sm.krange[1], hi);
     }
     lds_barrier();
+    const uint32_t kmin = sm.krange[0];
+    const uint32_t span = sm.krange[1] - kmin;
+    int s = span == 0u ? 0 : 32 - (int)__builtin_clz(span) - 12;
+    s = s < 0 ? 0 : s;                               // digit = (key - kmin) >> s lies in [0, 4095]
+    for (uint32_t c = c0; c < c1; ++c) atomicAdd(&hist[(cand_key[c] - kmin) >> s], 1u);
+    lds_barrier();
     find_digit<12>(hist, (uint32_t)n, scratch, res);
-    uint32_t p = res[0];
+    uint32_t p = res[0];                             // boundary prefix of (key - kmin) >> s
     uint32_t need = (uint32_t)n - res[1];
-    int shift = 20;
-    if (need != res[2]) {
-        for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+    uint32_t cnt = res[2];
+    if (need != cnt) {                               // uniform: the bin holds more keys than are needed
+        // the bin's own key range
+        uint32_t blo = 0xffffffffu, bhi = 0u;
+        for (uint32_t c = c0; c < c1; ++c) {
+            const uint32_t key = cand_key[c];
+            if (((key - kmin) >> s) == p) {
+                blo = min(blo, key);
+                bhi = max(bhi, key);
+                if (cnt <= kSmallBin) sm.mem[atomicAdd(&sm.mem_n, 1u)] = key;
+            }
+        }
+        blo = wave_min_u32(blo);
+        bhi = wave_max_u32(bhi);
+        if (lane == 0) {
+            atomicMin(&sm.krange[2], blo);
+            atomicMax(&sm.krange[3], bhi);
+        }
         lds_barrier();
-        for (uint32_t c = c0; c < c1; ++c)
-            if ((cand_key[c] >> 20) == p) atomicAdd(&hist[(cand_key[c] >> 8) & 0xfffu], 1u);
-        lds_barrier();
-        find_digit<12>(hist, need, scratch, res);
-        p = (p << 12) | res[0];
-        need -= res[1];
-        shift = 8;
-        if (need != res[2]) {
-            for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0u;
+        if (sm.krange[2] == sm.krange[3]) {          // every key of the bin is equal
+            p = sm.krange[2] - kmin;
+            s = 0;
+        } else if (cnt <= kSmallBin) {               // rank the bin's keys: the need-th largest is T
+            if (threadIdx.x < cnt) {
+                const uint32_t my = sm.mem[threadIdx.x];
+                uint32_t gt = 0, eq = 0;
+                for (uint32_t j = 0; j < cnt; ++j) {
+                    const uint32_t v = sm.mem[j];
+                    gt += v > my ? 1u : 0u;
+                    eq += v == my ? 1u : 0u;
+                }
+                if (gt < need && need <= gt + eq) {  // every thread holding T writes the same values
+                    res[0] = my;
+                    res[1] = gt;
+                }
+            }
             lds_barrier();
-            for (uint32_t c = c0; c < c1; ++c)
-                if ((cand_key[c] >> 8) == p) atomicAdd(&hist[cand_key[c] & 0xffu], 1u);
-            lds_barrier();
-            find_digit<8>(hist, need, scratch, res);
-            p = (p << 8) | res[0];
+            p = res[0] - kmin;
             need -= res[1];
-            shift = 0;
+            s = 0;
+        } else {                                     // radix passes below the first digit
+            while (s > 0) {
+                const int ns = s > 12 ? s - 12 : 0;
+                const uint32_t mask = (1u << (s - ns)) - 1u;
+                for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+                lds_barrier();
+                for (uint32_t c = c0; c < c1; ++c) {
+                    const uint32_t rel = cand_key[c] - kmin;
+                    if ((rel >> s) == p) atomicAdd(&hist[(rel >> ns) & mask], 1u);
+                }
+                lds_barrier();
+                find_digit<12>(hist, need, scratch, res);
+                p = (p << (s - ns)) | res[0];
+                need -= res[1];
+                s = ns;
+                if (need == res[2]) break;           // the whole digit bin is selected
+            }
         }
     }
-    // ---- emission: selected are the keys above the boundary value p and the first `need`
-    // (in list, i.e. position, order) equal to it; a selected candidate's output slot is the
-    // number of selected candidates before it in the list ----
+    // ---- emission: with cv = (key - kmin) >> s, selected are cv > p and the first `need` (in list,
+    // i.e. position, order) with cv == p; a selected candidate's output slot is the number of
+    // selected candidates before it in the list ----
     uint32_t ng = 0, ne = 0;
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t hi = cand_key[c] >> shift;
-        ng += hi > p ? 1u : 0u;
-        ne += hi == p ? 1u : 0u;
+        const uint32_t cv = (cand_key[c] - kmin) >> s;
+        ng += cv > p ? 1u : 0u;
+        ne += cv == p ? 1u : 0u;
     }
     // one scan of both counts, packed (list totals stay below 2^16: kCandCap = 12288)
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan((ng << 16) | ne, scratch, &tot);
     uint32_t gb = ex >> 16, eb = ex & 0xffffu;
+    uint32_t* cand_idx = sm.cand_idx;
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t hi = cand_key[c] >> shift;
+        const uint32_t cv = (cand_key[c] - kmin) >> s;
         uint32_t dst = 0xffffffffu;
-        if (hi > p) {
+        if (cv > p) {
             dst = gb + (eb < need ? eb : need);
             ++gb;
-        } else if (hi == p) {
+        } else if (cv == p) {
             if (eb < need) dst = gb + eb;
             ++eb;
         }
@@ -640,15 +722,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
         }
         ok = ok && total >= (uint32_t)n && total <= (uint32_t)kCandCap;   // uniform
         if (ok) {
-            uint32_t off = 0;
-            for (int c = 0; c < used; ++c) {
-                const uint32_t cc = sm.wcnt[c];
-                for (uint32_t i = threadIdx.x; i < cc; i += kTopkThreads) {
-                    const uint2 e = lists[(size_t)c * kCandCap + i];
-                    sm.cand_key[off + i] = e.x;
-                    sm.cand_idx[off + i] = e.y;
+            // Entry e of the concatenated lists (chunk order = position order) goes to list slot e.
+            // Thread t moves entries t, t + 1024, ...: the chunk offsets are read into registers
+            // first, so that every list load is issued before any is waited for.
+            constexpr int kPerThread = kCandCap / kTopkThreads;   // 12
+            uint32_t ends[kMaxSplitChunks];                        // end of chunk c's entries
+            uint32_t run = 0;
+#pragma unroll
+            for (int c = 0; c < kMaxSplitChunks; ++c) {
+                run += c < used ? sm.wcnt[c] : 0u;
+                ends[c] = run;
+            }
+            uint2 v[kPerThread];
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const uint32_t e = threadIdx.x + (uint32_t)j * kTopkThreads;
+                uint32_t c = 0, off = 0;
+#pragma unroll
+                for (int cc = 0; cc + 1 < kMaxSplitChunks; ++cc) {   // chunk of entry e: ends[c-1] <= e < ends[c]
+                    if (e >= ends[cc]) {
+                        c = cc + 1;
+                        off = ends[cc];
+                    }
                 }
-                off += cc;
+                const bool live = e < total;
+                v[j] = lists[(size_t)(live ? c : 0u) * kCandCap + (live ? e - off : 0u)];
+            }
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const uint32_t e = threadIdx.x + (uint32_t)j * kTopkThreads;
+                if (e < total) {
+                    sm.cand_key[e] = v[j].x;
+                    sm.cand_idx[e] = v[j].y;
+                }
             }
             lds_barrier();
             resolve_list(src, total, n, k, o, sm);
@@ -674,9 +780,10 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
     if (rows == 0) return hipSuccess;
     const size_t per_row = topk_ws_bytes_per_row(row_stride, k);
     // Few very long rows leave most of the GPU idle at one workgroup per row, each streaming its row
-    // twice: split the filter pass over the rows' chunks when the workspace allows.  Measured on
-    // 64 rows of 65536 candidates the split is slower (its fixed costs are paid twice), so it starts
-    // at rows of 8 chunks.  The result is identical either way.
+    // twice: split the filter pass over the rows' chunks when the workspace allows (rows of at least
+    // 8 chunks, fewer than 256 rows).  Measured on 64 rows of up to 65536 candidates (4 chunks) the
+    // split is slower, 25.2 against 18.8 us: the kernel boundary costs about 2.5 us and the select
+    // kernel's load of the freshly written lists about 5 us.  The result is identical either way.
     const int nch = (int)((row_stride + kStreamChunk - 1) / kStreamChunk);
     if (per_row > 0 && nch >= kMinSplitChunks && rows < 256 && ws && ws_bytes >= per_row) {
         const int per_batch = (int)min((size_t)rows, ws_bytes / per_row);

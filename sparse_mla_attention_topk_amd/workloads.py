@@ -307,6 +307,66 @@ def cache_write_tokens(device, T: int, num_pages: int, seed: int = 5, spread: fl
     return CacheWriteWorkload(tokens=tokens, slots=slots.to(torch.int64), num_pages=num_pages)
 
 
+@dataclasses.dataclass
+class WindowCache:
+    """A sliding-window paged cache next to a main cache: each request keeps only the pages that hold
+    its last window + draft positions; the block-table entries of its other logical pages are 0, the
+    NaN null page (evicted)."""
+    kv: torch.Tensor            # uint8 [num_pages, 64, record]
+    block_table: torch.Tensor   # int32 [num_requests, max_pages]
+    idx: torch.Tensor           # int32 [rows, width]: window + draft positions, ascending, -1 padded
+
+
+def window_cache(ctx_lens: torch.Tensor, kv_dtype: int, device, seed: int, window: int = 128, draft: int = 5,
+                 width: int = 192, max_pages: Optional[int] = None) -> WindowCache:
+    """Window cache for requests with contexts ``ctx_lens``: request r (context c) holds positions
+    max(0, c - draft - window) .. c - 1 in fresh pages handed out by a seeded permutation (records
+    drawn like make_paged_cache's); its other logical pages map to the null page 0.  Slots of a held
+    page outside that range, and the null page, hold NaN records.  ``idx`` row r lists those positions
+    ascending, -1 padded to ``width`` (one row per request)."""
+    g = _gen(seed, device)
+    ctx = [int(c) for c in ctx_lens.tolist()]
+    max_pages = max_pages or max(1, max((c + PAGE - 1) // PAGE for c in ctx))
+    spans = []
+    for c in ctx:
+        lo = max(0, c - draft - window)
+        spans.append((lo, c, lo // PAGE, (c - 1) // PAGE if c > 0 else lo // PAGE - 1))
+    total = sum(max(0, p1 - p0 + 1) for _, _, p0, p1 in spans)
+    rec = BF16_RECORD_BYTES if kv_dtype == KV_BF16 else FP8_RECORD_BYTES
+    kv = torch.empty((total + 1, PAGE, rec), dtype=torch.uint8, device=device)
+    perm = torch.randperm(total, generator=g, device=device).cpu() + 1
+    bt = torch.zeros((len(ctx), max_pages), dtype=torch.int32)
+    ntok = total * PAGE
+    if kv_dtype == KV_BF16:
+        vals = torch.randn((ntok, D_QK), generator=g, device=device, dtype=torch.float32)
+        kv[1:] = vals.to(torch.bfloat16).view(torch.uint8).view(total, PAGE, rec)
+    else:
+        lat = torch.randn((ntok, 512), generator=g, device=device, dtype=torch.float32)
+        codes = lat.to(torch.float8_e4m3fn).view(torch.uint8)
+        expo = torch.rand((ntok, 4), generator=g, device=device, dtype=torch.float32) * 8.0 - 4.0
+        scales = torch.exp2(expo).contiguous().view(torch.uint8).view(ntok, 16)
+        rope = torch.randn((ntok, D_ROPE), generator=g, device=device, dtype=torch.float32)
+        rope_b = rope.to(torch.bfloat16).view(torch.uint8).view(ntok, 128)
+        kv[1:] = torch.cat([codes, scales, rope_b], dim=1).view(total, PAGE, rec)
+    poison = _poison_record(kv_dtype, device)
+    kv[0] = poison
+    off = 0
+    idx = torch.full((len(ctx), width), -1, dtype=torch.int32)
+    for r, (lo, c, p0, p1) in enumerate(spans):
+        for lp in range(p0, p1 + 1):
+            pg = int(perm[off])
+            off += 1
+            bt[r, lp] = pg
+            s0, s1 = max(lo, lp * PAGE), min(c, (lp + 1) * PAGE)        # held positions of this page
+            if s0 > lp * PAGE:
+                kv[pg, : s0 - lp * PAGE] = poison
+            if s1 < (lp + 1) * PAGE:
+                kv[pg, s1 - lp * PAGE:] = poison
+        n = c - lo
+        idx[r, :n] = torch.arange(lo, c, dtype=torch.int32)
+    return WindowCache(kv=kv, block_table=bt.to(device), idx=idx.to(device))
+
+
 def rope_cos_sin(max_pos: int, device, base: float = 10000.0) -> torch.Tensor:
     """A rotary table of the usual frequency schedule, fp32 [max_pos, 64]: row p holds cos(p f_i) for
     i < 32, then sin(p f_i), with f_i = base^(-i/32) (computed in float64, rounded to fp32)."""
