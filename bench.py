@@ -79,7 +79,7 @@ def parse():
 # ----------------------------------------------------------------------------------------------
 
 def _short_kernel(name: str) -> str:
-    n = name.replace("void ", "")
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
     if "smla::" in n:
         n = n[n.index("smla::"):]
         n = n.split("(")[0]
