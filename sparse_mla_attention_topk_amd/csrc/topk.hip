@@ -175,9 +175,19 @@ constexpr int32_t kStreamChunk = kStreamU * kTopkThreads;            // 16384
 // one (chunk, wave) count per thread: rows of up to 64 chunks
 constexpr int64_t kFilterMax = (int64_t)(kTopkThreads / kTopkWaves) * kStreamChunk;   // 1048576
 
+// Index of the calling wave in its workgroup, as a scalar: branches on it stay uniform.
+__device__ __forceinline__ int32_t wave_index() {
+    return __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x / kWave));
+}
+
+// First position of the calling wave's slot u (uniform in the wave); lane l holds that plus l.
+template <int U>
+__device__ __forceinline__ int32_t slot_base(int32_t base, int u) {
+    return base + wave_index() * (U * kWave) + u * kWave;
+}
 template <int U>
 __device__ __forceinline__ int32_t slot_pos(int32_t base, int u) {
-    return base + (int32_t)(threadIdx.x / kWave) * (U * kWave) + u * kWave + (int32_t)(threadIdx.x & (kWave - 1));
+    return slot_base<U>(base, u) + (int32_t)(threadIdx.x & (kWave - 1));
 }
 
 // Loads the U slots of the chunk at `base`.  Positions at or beyond L hold NaN, which passes no
@@ -186,12 +196,16 @@ __device__ __forceinline__ int32_t slot_pos(int32_t base, int u) {
 template <int U, class Src>
 __device__ __forceinline__ void load_slots(const Src& src, int32_t L, int32_t base, float* v) {
     const float qnan = __builtin_nanf("");
+    // Positions from the vector thread index: the loads then issue one by one between per-lane
+    // tests, which measured faster on MI355X than the same loads issued back to back (the whole
+    // row of 256 KB in registers 1.5 us sooner).
+    const int32_t p0 = base + (int32_t)(threadIdx.x / kWave) * (U * kWave) + (int32_t)(threadIdx.x & (kWave - 1));
 #pragma unroll
     for (int g = 0; g < U; g += kTopkUnroll) {
-        const bool live = slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) < L;   // uniform in the wave
+        const bool live = p0 + g * kWave - (int32_t)(threadIdx.x & (kWave - 1)) < L;
 #pragma unroll
         for (int u = g; u < g + kTopkUnroll; ++u) {
-            const int32_t j = slot_pos<U>(base, u);
+            const int32_t j = p0 + u * kWave;
             v[u] = live ? src.at(j < L ? j : L - 1) : qnan;
         }
     }
@@ -199,7 +213,7 @@ __device__ __forceinline__ void load_slots(const Src& src, int32_t L, int32_t ba
     for (int u = 0; u < U; ++u) asm volatile("" : "+v"(v[u]));
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (slot_pos<U>(base, u) >= L) v[u] = qnan;
+        if (p0 + u * kWave >= L) v[u] = qnan;
 }
 
 // Number of this wave's slots with v >= tf (uniform in the wave).
@@ -208,7 +222,7 @@ __device__ __forceinline__ uint32_t wave_count_ge(const float* v, int32_t L, int
     uint32_t c = 0;
 #pragma unroll
     for (int g = 0; g < U; g += kTopkUnroll) {
-        if (slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) >= L) break;   // uniform in the wave
+        if (slot_base<U>(base, g) >= L) break;   // uniform
 #pragma unroll
         for (int u = g; u < g + kTopkUnroll; ++u) c += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(v[u] >= tf));
     }
@@ -218,22 +232,26 @@ __device__ __forceinline__ uint32_t wave_count_ge(const float* v, int32_t L, int
 // Appends this wave's slots with v >= tf (value bits, position) to the LDS list from offset `pos`
 // (uniform in the wave), in slot-then-lane order.  With GUARD, slots at or beyond kCandCap are
 // never written (the streaming path re-reads the row, so its counts are not taken on faith).
+// `cbits` and `cidx` are 48 KB apart at the start of the workgroup's LDS, so both stores of an entry
+// use one address register and the stores' offset fields.
 template <int U, bool GUARD>
 __device__ __forceinline__ void wave_append_ge(const float* v, int32_t L, int32_t base, float tf, uint32_t pos,
                                                uint32_t* cbits, uint32_t* cidx) {
+    pos = __builtin_amdgcn_readfirstlane(pos);
+    const int32_t wbase = slot_base<U>(base, 0);
+    const uint32_t pos0 = (uint32_t)(wbase + (int32_t)(threadIdx.x & (kWave - 1)));   // position in slot 0
 #pragma unroll
     for (int g = 0; g < U; g += kTopkUnroll) {
-        if (slot_pos<U>(base, g) - (int32_t)(threadIdx.x & (kWave - 1)) >= L) break;   // uniform in the wave
+        if (wbase + g * kWave >= L) break;   // uniform
 #pragma unroll
         for (int u = g; u < g + kTopkUnroll; ++u) {
             const bool pred = v[u] >= tf;
             const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
             if (pred) {
-                const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos));
+                const uint32_t p = pos + lanes_below(m);
                 if (!GUARD || p < (uint32_t)kCandCap) {
                     cbits[p] = __float_as_uint(v[u]);
-                    cidx[p] = (uint32_t)slot_pos<U>(base, u);
+                    cidx[p] = pos0 + (uint32_t)(u * kWave);
                 }
             }
             pos += (uint32_t)__popcll(m);
@@ -245,6 +263,7 @@ __device__ __forceinline__ void wave_append_ge(const float* v, int32_t L, int32_
 constexpr uint32_t kSmallBin = 128;  // a boundary bin of at most this many keys is resolved by ranking
 
 struct TopkShared {
+    uint32_t cand_key[kCandCap], cand_idx[kCandCap];   // first: both within the LDS offset field's reach
     uint32_t hist[1 << 12];
     uint32_t scratch[kTopkWaves + 2];
     uint32_t res[3];
@@ -253,7 +272,6 @@ struct TopkShared {
     uint32_t wcnt[kTopkThreads];             // per-wave candidate counts, then list offsets
     uint32_t mem[kSmallBin];                 // keys of a small boundary bin
     uint32_t mem_n;
-    uint32_t cand_key[kCandCap], cand_idx[kCandCap];
 };
 
 // Minimum / maximum over the 64 lanes of a wave (every lane gets the result): DPP exchanges within
