@@ -267,7 +267,8 @@ struct TopkShared {
     uint32_t hist[1 << 12];
     uint32_t scratch[kTopkWaves + 2];
     uint32_t res[3];
-    uint32_t krange[4];                      // min / max key of the list, then of the boundary bin
+    uint32_t krange[6];                      // min / max key of the list, then of the interval (2 rounds)
+    uint32_t first[2];                       // first digit from the sample: base key, shift
     uint32_t tbl[kTopkUnroll * kTopkWaves];
     uint32_t wcnt[kTopkThreads];             // per-wave candidate counts, then list offsets
     uint32_t mem[kSmallBin];                 // keys of a small boundary bin
@@ -292,22 +293,48 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_reduce_u32<false>(v); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce_u32<true>(v); }
 
+// Shift s such that span >> s < 4096: a 12-bit digit (key - base) >> s spreads keys of that span
+// over the histogram's bins.
+__device__ __forceinline__ int fitted_shift(uint32_t span) {
+    const int s = span == 0u ? 0 : 32 - (int)__builtin_clz(span) - 12;
+    return s < 0 ? 0 : s;
+}
+
 // Filter threshold from the four sampled values per thread: a value tf such that, judging by the
 // sample, about 1.25 n + 4 sigma candidates of the row have v >= tf.  Returns false when the sample
 // offers none.  Every workgroup that samples the same row at the same positions derives the same tf.
+// With `first`, also the first digit for resolve_list: {key of tf, shift fitted to the span from
+// that key to the largest sampled key} in first[0..1] (LDS words, readable after the next barrier).
 __device__ __forceinline__ bool sample_threshold(const float* sv, int64_t L, int32_t n, uint32_t* hist,
-                                                 uint32_t* scratch, uint32_t* res, float* tf) {
+                                                 uint32_t* scratch, uint32_t* res, float* tf,
+                                                 uint32_t* first = nullptr) {
     for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+    if (first && threadIdx.x == 0) first[1] = 0u;
     lds_barrier();
+    uint32_t mx = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) atomicAdd(&hist[score_key(sv[i]) >> 20], 1u);
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t key = score_key(sv[i]);
+        atomicAdd(&hist[key >> 20], 1u);
+        mx = max(mx, key);
+    }
+    if (first) {
+        mx = wave_max_u32(mx);
+        if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&first[1], mx);
+    }
     lds_barrier();
+    const uint32_t smax = first ? first[1] : 0u;     // read before find_digit's barriers
     const float expect = (float)n * (float)(1 << kSampleLog2) / (float)L;
     const uint32_t want = (uint32_t)(1.25f * expect + 4.f * sqrtf(expect) + 8.f);
     if (want >= (uint32_t)(1 << kSampleLog2)) return false;
     find_digit<12>(hist, want, scratch, res);
     if (res[0] < 8u) return false;
     *tf = digit_floor_value(res[0]);
+    if (first && threadIdx.x == 0) {                 // read only after a later barrier
+        const uint32_t tkey = res[0] << 20;          // every listed key is at least this
+        first[0] = tkey;
+        first[1] = (uint32_t)fitted_shift(smax - tkey);   // smax >= tkey: the want-th sample is listed
+    }
     return true;
 }
 
@@ -329,78 +356,110 @@ __device__ __forceinline__ bool filter_eligible(int64_t L, int32_t n) {
     return L > kCandCap && L <= kFilterMax && n <= kCandCap;
 }
 
+// Clears what resolve_list counts into; a barrier must follow before resolve_list runs.
+__device__ __forceinline__ void resolve_prepare(TopkShared& sm) {
+    for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) sm.hist[i] = 0u;
+    if (threadIdx.x == 0) {
+        sm.krange[0] = sm.krange[2] = sm.krange[4] = 0xffffffffu;
+        sm.krange[1] = sm.krange[3] = sm.krange[5] = 0u;
+        sm.mem_n = 0u;
+    }
+}
+
 // Finishes a selection from the candidate list sm.cand_key (value bits) / sm.cand_idx (positions),
 // entries [0, total), which holds every selected candidate, in ascending position order, with
-// n <= total <= kCandCap.  The n-th key is found by radix selection on the keys relative to the
-// list's smallest key, with a first digit fitted to the list's key range (so the listed keys spread
-// over the 4096 bins instead of piling into a few LDS counters); a boundary bin whose keys are all
-// equal, or that holds at most kSmallBin keys, is settled directly (equal keys; ranking).  Then the
-// output slot of each selected candidate is the number of selected candidates before it in the list.
+// n <= total <= kCandCap.  resolve_prepare and a barrier must precede it.
+//
+// The n-th key T is narrowed down as an interval [lo, hi] of keys holding it, with `need` = how many
+// of the interval's keys are selected (all keys above hi are).  The first digit is
+// min((key - base) >> s, 4095): base and s come from `first` (the sample's threshold key, a lower
+// bound of every listed key, and a shift fitted to the sampled span; keys above the sample's
+// largest land in the top bin) or, without it, from the list's own key range.  Fitted digits spread
+// the keys over the 4096 bins instead of piling them into a few LDS counters.  While the interval
+// holds more keys than are needed, it is settled directly when its keys are all equal or number at
+// most kSmallBin (ranking), else narrowed by a digit fitted to its keys' own range.  A selected
+// candidate's output slot is the number of selected candidates before it in the list.
 template <class Src>
 __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int32_t n, int32_t k,
-                                             int32_t* __restrict__ o, TopkShared& sm) {
+                                             int32_t* __restrict__ o, TopkShared& sm,
+                                             const uint32_t* first = nullptr) {
     uint32_t* hist = sm.hist;
     uint32_t* scratch = sm.scratch;
     uint32_t* res = sm.res;
     uint32_t* cand_key = sm.cand_key;
     const int lane = threadIdx.x & (kWave - 1);
-    for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-    if (threadIdx.x == 0) {
-        sm.krange[0] = sm.krange[2] = 0xffffffffu;
-        sm.krange[1] = sm.krange[3] = 0u;
-        sm.mem_n = 0u;
-    }
     const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
     const uint32_t c0 = threadIdx.x * per;
     const uint32_t c1 = c0 + per < total ? c0 + per : total;
-    lds_barrier();                                   // the list is complete; hist cleared, range words set
-    // keys and their range
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t key = score_key(__uint_as_float(cand_key[c]));
-        cand_key[c] = key;
-        lo = min(lo, key);
-        hi = max(hi, key);
+    uint32_t base;
+    int s;
+    if (first) {
+        base = first[0];
+        s = (int)first[1];
+        for (uint32_t c = c0; c < c1; ++c) {
+            const uint32_t key = score_key(__uint_as_float(cand_key[c]));
+            cand_key[c] = key;
+            const uint32_t d = (key - base) >> s;
+            atomicAdd(&hist[d < 4095u ? d : 4095u], 1u);
+        }
+    } else {
+        uint32_t lo = 0xffffffffu, hi = 0u;
+        for (uint32_t c = c0; c < c1; ++c) {
+            const uint32_t key = score_key(__uint_as_float(cand_key[c]));
+            cand_key[c] = key;
+            lo = min(lo, key);
+            hi = max(hi, key);
+        }
+        lo = wave_min_u32(lo);
+        hi = wave_max_u32(hi);
+        if (lane == 0) {
+            atomicMin(&sm.krange[0], lo);
+            atomicMax(&sm.krange[1], hi);
+        }
+        lds_barrier();
+        base = sm.krange[0];
+        s = fitted_shift(sm.krange[1] - base);       // digits lie in [0, 4095]
+        for (uint32_t c = c0; c < c1; ++c) atomicAdd(&hist[(cand_key[c] - base) >> s], 1u);
     }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    if (lane == 0) {
-        atomicMin(&sm.krange[0], lo);
-        atomicMax(&sm.krange[1], hi);
-    }
-    lds_barrier();
-    const uint32_t kmin = sm.krange[0];
-    const uint32_t span = sm.krange[1] - kmin;
-    int s = span == 0u ? 0 : 32 - (int)__builtin_clz(span) - 12;
-    s = s < 0 ? 0 : s;                               // digit = (key - kmin) >> s lies in [0, 4095]
-    for (uint32_t c = c0; c < c1; ++c) atomicAdd(&hist[(cand_key[c] - kmin) >> s], 1u);
     lds_barrier();
     find_digit<12>(hist, (uint32_t)n, scratch, res);
-    uint32_t p = res[0];                             // boundary prefix of (key - kmin) >> s
     uint32_t need = (uint32_t)n - res[1];
     uint32_t cnt = res[2];
-    if (need != cnt) {                               // uniform: the bin holds more keys than are needed
-        // the bin's own key range
+    uint32_t lo = base + (res[0] << s);
+    uint32_t hi = res[0] == 4095u ? 0xffffffffu
+                                  : (uint32_t)min((uint64_t)base + ((uint64_t)(res[0] + 1u) << s) - 1u,
+                                                  (uint64_t)0xffffffffu);
+    for (int round = 0; need != cnt; ++round) {      // uniform; each round shrinks the interval
+        // the interval's own key range (and, when few, its keys); krange words of this round
+        uint32_t* kr = sm.krange + 2 + 2 * (round & 1);
         uint32_t blo = 0xffffffffu, bhi = 0u;
         for (uint32_t c = c0; c < c1; ++c) {
             const uint32_t key = cand_key[c];
-            if (((key - kmin) >> s) == p) {
+            if (key >= lo && key <= hi) {
                 blo = min(blo, key);
                 bhi = max(bhi, key);
                 if (cnt <= kSmallBin) sm.mem[atomicAdd(&sm.mem_n, 1u)] = key;
             }
         }
+        for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
+        if (threadIdx.x == 0) {                       // the other round's words, for the next round
+            sm.krange[2 + 2 * ((round + 1) & 1)] = 0xffffffffu;
+            sm.krange[3 + 2 * ((round + 1) & 1)] = 0u;
+        }
         blo = wave_min_u32(blo);
         bhi = wave_max_u32(bhi);
         if (lane == 0) {
-            atomicMin(&sm.krange[2], blo);
-            atomicMax(&sm.krange[3], bhi);
+            atomicMin(&kr[0], blo);
+            atomicMax(&kr[1], bhi);
         }
         lds_barrier();
-        if (sm.krange[2] == sm.krange[3]) {          // every key of the bin is equal
-            p = sm.krange[2] - kmin;
-            s = 0;
-        } else if (cnt <= kSmallBin) {               // rank the bin's keys: the need-th largest is T
+        blo = kr[0];
+        bhi = kr[1];
+        if (blo == bhi) {                            // every key of the interval is equal: T
+            lo = hi = blo;
+            break;
+        }
+        if (cnt <= kSmallBin) {                      // rank the interval's keys: the need-th largest is T
             if (threadIdx.x < cnt) {
                 const uint32_t my = sm.mem[threadIdx.x];
                 uint32_t gt = 0, eq = 0;
@@ -415,36 +474,30 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
                 }
             }
             lds_barrier();
-            p = res[0] - kmin;
+            lo = hi = res[0];
             need -= res[1];
-            s = 0;
-        } else {                                     // radix passes below the first digit
-            while (s > 0) {
-                const int ns = s > 12 ? s - 12 : 0;
-                const uint32_t mask = (1u << (s - ns)) - 1u;
-                for (int i = threadIdx.x; i < (1 << 12); i += kTopkThreads) hist[i] = 0u;
-                lds_barrier();
-                for (uint32_t c = c0; c < c1; ++c) {
-                    const uint32_t rel = cand_key[c] - kmin;
-                    if ((rel >> s) == p) atomicAdd(&hist[(rel >> ns) & mask], 1u);
-                }
-                lds_barrier();
-                find_digit<12>(hist, need, scratch, res);
-                p = (p << (s - ns)) | res[0];
-                need -= res[1];
-                s = ns;
-                if (need == res[2]) break;           // the whole digit bin is selected
-            }
+            break;
         }
+        const int s2 = fitted_shift(bhi - blo);
+        for (uint32_t c = c0; c < c1; ++c) {
+            const uint32_t key = cand_key[c];
+            if (key >= blo && key <= bhi) atomicAdd(&hist[(key - blo) >> s2], 1u);
+        }
+        lds_barrier();
+        find_digit<12>(hist, need, scratch, res);
+        need -= res[1];
+        cnt = res[2];
+        lo = blo + (res[0] << s2);
+        hi = (uint32_t)min((uint64_t)blo + ((uint64_t)(res[0] + 1u) << s2) - 1u, (uint64_t)bhi);
     }
-    // ---- emission: with cv = (key - kmin) >> s, selected are cv > p and the first `need` (in list,
-    // i.e. position, order) with cv == p; a selected candidate's output slot is the number of
-    // selected candidates before it in the list ----
+    // ---- emission: selected are the keys above hi and the first `need` (in list, i.e. position,
+    // order) of those in [lo, hi]; a selected candidate's output slot is the number of selected
+    // candidates before it in the list ----
     uint32_t ng = 0, ne = 0;
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t cv = (cand_key[c] - kmin) >> s;
-        ng += cv > p ? 1u : 0u;
-        ne += cv == p ? 1u : 0u;
+        const uint32_t key = cand_key[c];
+        ng += key > hi ? 1u : 0u;
+        ne += key >= lo && key <= hi ? 1u : 0u;
     }
     // one scan of both counts, packed (list totals stay below 2^16: kCandCap = 12288)
     uint32_t tot;
@@ -452,12 +505,12 @@ __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int
     uint32_t gb = ex >> 16, eb = ex & 0xffffu;
     uint32_t* cand_idx = sm.cand_idx;
     for (uint32_t c = c0; c < c1; ++c) {
-        const uint32_t cv = (cand_key[c] - kmin) >> s;
+        const uint32_t key = cand_key[c];
         uint32_t dst = 0xffffffffu;
-        if (cv > p) {
+        if (key > hi) {
             dst = gb + (eb < need ? eb : need);
             ++gb;
-        } else if (cv == p) {
+        } else if (key >= lo) {
             if (eb < need) dst = gb + eb;
             ++eb;
         }
@@ -569,6 +622,8 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
                 sm.cand_idx[j] = (uint32_t)j;
             }
         }
+        resolve_prepare(sm);
+        lds_barrier();
         resolve_list(src, (uint32_t)L32, n, k, o, sm);
         return;
     }
@@ -582,8 +637,9 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
 #pragma unroll
         for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(sv[i]));
         float tf = 0.f;
-        if (sample_threshold(sv, L, n, sm.hist, sm.scratch, sm.res, &tf)) {
+        if (sample_threshold(sv, L, n, sm.hist, sm.scratch, sm.res, &tf, sm.first)) {
             const int nch = resident ? 1 : (L32 + kStreamChunk - 1) / kStreamChunk;
+            resolve_prepare(sm);   // ordered before resolve_list by the barriers below
             if (resident) {
                 const uint32_t c = wave_count_ge<kResidentU>(v, L32, 0, tf);
                 if (lane == 0) sm.wcnt[wid] = c;
@@ -613,7 +669,7 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
                     }
                 }
                 lds_barrier();
-                resolve_list(src, total, n, k, o, sm);
+                resolve_list(src, total, n, k, o, sm, sm.first);
                 return;
             }
         }
@@ -774,6 +830,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
                     sm.cand_idx[e] = v[j].y;
                 }
             }
+            resolve_prepare(sm);
             lds_barrier();
             resolve_list(src, total, n, k, o, sm);
             return;
