@@ -58,6 +58,29 @@ def test_fp8_decode_shape_all_rows():
     _check(s, lens, 2048, what="128 rows L~U[32K,128K] (all rows)")
 
 
+def test_clustered_candidates():
+    """Rows whose best candidates crowd into a narrow band of positions (so far more of them than
+    average fall to one 4096-position stretch of the row), rows with the band at the start, middle
+    and end, with and without ties, at lengths that fill the registers-resident form; plus plain rows
+    in the same batch.  Bit-exact against the oracle."""
+    g = torch.Generator(device="cpu").manual_seed(21)
+    rows, L = 12, 65536
+    s = torch.randn((rows, L), generator=g, dtype=torch.float32)
+    lengths = torch.full((rows,), L, dtype=torch.int32)
+    for r, (start, width, tied) in enumerate([(0, 4096, False), (8192, 4096, False), (61440, 4096, False),
+                                             (30000, 2500, False), (12288, 6000, True), (4000, 1000, True),
+                                             (49152, 16384, False), (0, 3000, True)]):
+        band = torch.randn((width,), generator=g, dtype=torch.float32).abs() + 4.0
+        if tied:
+            band = torch.round(band * 4) / 4          # few distinct values: heavy ties inside the band
+        s[r, start:start + width] = band
+    lengths[8] = 50000                                   # a band ending past the row's length
+    s[8, 45000:52000] = 6.0
+    lengths[9] = 20000
+    s[9, 16000:20000] = torch.randn((4000,), generator=g).abs() + 5.0
+    _check(s.to(DEV), lengths.to(DEV), 2048, what="clustered best candidates")
+
+
 @pytest.mark.parametrize("k", [1, 2, 63, 192, 256, 2000, 2048, 4096, 16384])
 def test_k_values_and_ragged_lengths(k):
     g = torch.Generator(device=DEV).manual_seed(1000 + k)
