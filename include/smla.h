@@ -119,9 +119,9 @@ smla_status smla_fill_causal_lengths(int64_t first_pos, int32_t T, int32_t* leng
  * scores: fp32, 4-byte aligned; row_offsets: int64 [rows] or NULL; lengths: int32 [rows] or NULL;
  * out_idx: int32 [rows, k].  Requires 1 <= k <= 16384, 1 <= row_stride <= 2^31 - 1, rows >= 0.
  * ws/ws_bytes: optional top-k workspace, 256-byte aligned (NULL/0 allowed).  With fewer than 256
- *   rows and 114688 < row_stride <= 262144, a workspace of at least 256 + ceil(row_stride/16384) *
+ *   rows and 114688 < row_stride <= 524288, a workspace of at least 256 + ceil(row_stride/32768) *
  *   98304 bytes per row lets the filtering pass over each row run on several workgroups (one per
- *   16384-candidate chunk); smla_workspace_size reports the size for 255 rows.  The output is
+ *   32768-candidate chunk); smla_workspace_size reports the size for 255 rows.  The output is
  *   identical with or without it.  Calls sharing a workspace must be stream-ordered. */
 smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, int64_t row_stride,
                               const int32_t* lengths, int32_t rows, int32_t k, int32_t* out_idx,

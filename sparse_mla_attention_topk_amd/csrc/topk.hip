@@ -216,6 +216,42 @@ __device__ __forceinline__ void load_slots(const Src& src, int32_t L, int32_t ba
         if (p0 + u * kWave >= L) v[u] = qnan;
 }
 
+// The loads of load_slots, issued through a buffer resource over the row's L scores without waiting
+// for them: loads at or past the end return 0 and never touch memory, and the slot step sits in each
+// load's offset field, so the loads need no address registers (the chunk workgroups of the split
+// filter run two to a CU).
+template <int U>
+__device__ __forceinline__ void issue_slots_buffer(const DirectScores& src, int32_t L, int32_t base, float* v) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src.s, (short)0, L * (int32_t)sizeof(float), 0x00020000);
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int g = 0; g < U; g += kTopkUnroll) {
+        if (slot_base<U>(base, g) < L) {   // uniform
+            const int32_t voff = slot_pos<U>(base, g) * (int32_t)sizeof(float);
+#pragma unroll
+            for (int u = g; u < g + kTopkUnroll; ++u)
+                v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rs, voff + (u - g) * kWave * (int32_t)sizeof(float), 0, 0));
+        } else {
+#pragma unroll
+            for (int u = g; u < g + kTopkUnroll; ++u) v[u] = qnan;
+        }
+    }
+}
+
+// Waits for the slots of issue_slots_buffer: the values become opaque register contents, and the lanes
+// of a slot that straddles L get NaN (which passes no threshold test).
+template <int U>
+__device__ __forceinline__ void settle_slots_buffer(int32_t L, int32_t base, float* v) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (slot_base<U>(base, u) + kWave > L)   // uniform: only a slot that straddles L has lanes to fix
+            v[u] = slot_pos<U>(base, u) < L ? v[u] : __builtin_nanf("");
+}
+
 // Number of this wave's slots with v >= tf (uniform in the wave).
 template <int U>
 __device__ __forceinline__ uint32_t wave_count_ge(const float* v, int32_t L, int32_t base, float tf) {
@@ -696,7 +732,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     select_topk(DirectScores{scores + off}, L, k, out + (int64_t)row * k, sm);
 }
 
-// ---- few long rows: the filter pass split over the row's chunks of kStreamChunk positions ----
+// ---- few long rows: the filter pass split over the row's chunks of kFilterChunk positions ----
 // Per row, the workspace holds kSplitHeader bytes of chunk counts, then for each chunk a list of up
 // to kCandCap (value bits, position) pairs.  Every chunk workgroup derives the same threshold from
 // the same sample of the row, and lists its candidates in position order; the select kernel
@@ -704,14 +740,45 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
 // the one-workgroup filtered path does.  Rows whose filter fails (a chunk reports kFilterFailed, or
 // the total is out of range) are selected by the general path in the select kernel.
 constexpr size_t kSplitHeader = 256;
-constexpr int kMaxSplitChunks = 16;
-constexpr int kMinSplitChunks = 8;
+constexpr int kFilterU = 32;                                         // slots per thread of a chunk workgroup
+constexpr int32_t kFilterChunk = kFilterU * kTopkThreads;            // 32768 candidates per chunk
+constexpr int kMaxSplitChunks = 16;                                  // rows of up to 524288 candidates
+constexpr int64_t kMinSplitCandidates = 7 * kStreamChunk + 1;        // rows longer than 114688
 constexpr uint32_t kFilterFailed = 0xffffffffu;
 
 __host__ __device__ __forceinline__ size_t split_row_bytes(int nch) {
     return kSplitHeader + (size_t)nch * kCandCap * sizeof(uint2);
 }
 
+// Appends this wave's slots with v >= tf to a chunk list in global memory (buffer resource lr), from
+// entry `pos` on, in slot-then-lane (position) order.
+template <int U>
+__device__ __forceinline__ void filter_append(const float* v, int32_t L, int32_t base, float tf, uint32_t pos,
+                                              __amdgpu_buffer_rsrc_t lr) {
+    pos = __builtin_amdgcn_readfirstlane(pos);
+    const int32_t wbase = slot_base<U>(base, 0);
+    const uint32_t pos0 = (uint32_t)(wbase + (int32_t)(threadIdx.x & (kWave - 1)));
+#pragma unroll
+    for (int g = 0; g < U; g += kTopkUnroll) {
+        if (wbase + g * kWave >= L) break;   // uniform
+#pragma unroll
+        for (int u = g; u < g + kTopkUnroll; ++u) {
+            const bool pred = v[u] >= tf;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+            if (pred) {
+                const uint32_t p = pos + lanes_below(m);   // below the chunk's total, at most kCandCap
+                // two 32-bit stores: a 64-bit one would keep every value in the low half of a register pair
+                const int32_t off = (int32_t)(p * sizeof(uint2));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[u]), lr, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(pos0 + (uint32_t)(u * kWave), lr, off + 4, 0, 0);
+            }
+            pos += (uint32_t)__popcll(m);
+        }
+    }
+}
+
+// At 42 registers per lane two chunk workgroups fit on a CU, so a launch of up to 512 of them runs in
+// one round.
 __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                    const int64_t* __restrict__ row_offsets,
                                                                    int64_t row_stride,
@@ -730,15 +797,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* 
     uint32_t* counts = (uint32_t*)rws;
     uint2* list = (uint2*)(rws + kSplitHeader) + (size_t)c * kCandCap;
     const int32_t L32 = (int32_t)L;
-    const int32_t base = c * kStreamChunk;
+    const int32_t base = c * kFilterChunk;
     if (base >= L32) {
         if (threadIdx.x == 0) counts[c] = 0u;
         return;
     }
     const DirectScores src{scores + (row_offsets ? row_offsets[row] : (int64_t)row * row_stride)};
-    float sv[4], v[kStreamU];
+    // The chunk is two halves of kStreamChunk positions (the streaming layout, one after the other).
+    // The first half's loads go out before the sample is evaluated and land meanwhile; the second
+    // half's after it, so the two halves' values and the threshold's working registers are never all
+    // live together.
+    const int32_t base1 = base + kStreamChunk;
+    float sv[4], va[kStreamU], vb[kStreamU];
     load_sample(src, L, sv);
-    load_slots<kStreamU>(src, L32, base, v);
+    issue_slots_buffer<kStreamU>(src, L32, base, va);
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(sv[i]));
     float tf = 0.f;
@@ -746,26 +818,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* 
         if (threadIdx.x == 0) counts[c] = kFilterFailed;
         return;
     }
-    const uint32_t wc = wave_count_ge<kStreamU>(v, L32, base, tf);
-    if (lane == 0) wcnt[wid] = wc;
+    issue_slots_buffer<kStreamU>(src, L32, base1, vb);
+    settle_slots_buffer<kStreamU>(L32, base, va);
+    const uint32_t ca = wave_count_ge<kStreamU>(va, L32, base, tf);
+    settle_slots_buffer<kStreamU>(L32, base1, vb);
+    const uint32_t cb = wave_count_ge<kStreamU>(vb, L32, base1, tf);
+    if (lane == 0) {
+        wcnt[wid] = ca;
+        wcnt[kTopkWaves + wid] = cb;
+    }
     lds_barrier();
     uint32_t total;
-    const uint32_t before = block_exclusive_scan(threadIdx.x < kTopkWaves ? wcnt[threadIdx.x] : 0u, scratch, &total);
-    if (threadIdx.x < kTopkWaves) wcnt[threadIdx.x] = before;
+    const uint32_t before =
+        block_exclusive_scan(threadIdx.x < 2 * kTopkWaves ? wcnt[threadIdx.x] : 0u, scratch, &total);
+    if (threadIdx.x < 2 * kTopkWaves) wcnt[threadIdx.x] = before;
     lds_barrier();
     if (threadIdx.x == 0) counts[c] = total;
     if (total > (uint32_t)kCandCap) return;   // uniform; the row's total is then out of range too
-    uint32_t pos = wcnt[wid];
-#pragma unroll
-    for (int u = 0; u < kStreamU; ++u) {
-        const bool pred = v[u] >= tf;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
-        if (pred) {
-            const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos));
-            list[p] = make_uint2(__float_as_uint(v[u]), (uint32_t)slot_pos<kStreamU>(base, u));   // p < total
-        }
-        pos += (uint32_t)__popcll(m);
-    }
+    // The chunk's list through a buffer resource: each store's address is one 32-bit offset.
+    const __amdgpu_buffer_rsrc_t lr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)list, (short)0, (int32_t)(kCandCap * sizeof(uint2)), 0x00020000);
+    filter_append<kStreamU>(va, L32, base, tf, wcnt[wid], lr);
+    filter_append<kStreamU>(vb, L32, base1, tf, wcnt[kTopkWaves + wid], lr);
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* __restrict__ scores,
@@ -784,7 +858,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
         const unsigned char* rws = ws + (size_t)row * split_row_bytes(nch);
         const uint32_t* counts = (const uint32_t*)rws;
         const uint2* lists = (const uint2*)(rws + kSplitHeader);
-        const int used = (int)((L + kStreamChunk - 1) / kStreamChunk);   // chunks the filter kernel ran
+        const int used = (int)((L + kFilterChunk - 1) / kFilterChunk);   // chunks the filter kernel ran
+        // Entry i of every chunk's list is loaded by thread i (i < 1024) together with the counts, one
+        // round trip for both: every chunk of the row has its list region (entries past a chunk's count
+        // are left over from earlier calls and are dropped below).
+        uint2 v0[kMaxSplitChunks];
+#pragma unroll
+        for (int c = 0; c < kMaxSplitChunks; ++c)
+            if (c < nch) v0[c] = lists[(size_t)c * kCandCap + threadIdx.x];
         if ((int)threadIdx.x < used) sm.wcnt[threadIdx.x] = counts[threadIdx.x];
         lds_barrier();
         uint32_t total = 0;
@@ -796,39 +877,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
         }
         ok = ok && total >= (uint32_t)n && total <= (uint32_t)kCandCap;   // uniform
         if (ok) {
-            // Entry e of the concatenated lists (chunk order = position order) goes to list slot e.
-            // Thread t moves entries t, t + 1024, ...: the chunk offsets are read into registers
-            // first, so that every list load is issued before any is waited for.
-            constexpr int kPerThread = kCandCap / kTopkThreads;   // 12
-            uint32_t ends[kMaxSplitChunks];                        // end of chunk c's entries
-            uint32_t run = 0;
+            // Chunk c's entries go to list slots from the sum of the earlier chunks' counts (chunk order
+            // is position order): entry i < 1024 from the registers loaded above, entries from 1024 on (a
+            // chunk holding more candidates than threads) in a second loop.
+            uint32_t cnt[kMaxSplitChunks];   // read before any list store, so the reads do not wait on them
+#pragma unroll
+            for (int c = 0; c < kMaxSplitChunks; ++c) cnt[c] = c < used ? sm.wcnt[c] : 0u;
+            uint32_t before = 0;
 #pragma unroll
             for (int c = 0; c < kMaxSplitChunks; ++c) {
-                run += c < used ? sm.wcnt[c] : 0u;
-                ends[c] = run;
-            }
-            uint2 v[kPerThread];
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
-                const uint32_t e = threadIdx.x + (uint32_t)j * kTopkThreads;
-                uint32_t c = 0, off = 0;
-#pragma unroll
-                for (int cc = 0; cc + 1 < kMaxSplitChunks; ++cc) {   // chunk of entry e: ends[c-1] <= e < ends[c]
-                    if (e >= ends[cc]) {
-                        c = cc + 1;
-                        off = ends[cc];
-                    }
+                if (threadIdx.x < cnt[c]) {
+                    sm.cand_key[before + threadIdx.x] = v0[c].x;
+                    sm.cand_idx[before + threadIdx.x] = v0[c].y;
                 }
-                const bool live = e < total;
-                v[j] = lists[(size_t)(live ? c : 0u) * kCandCap + (live ? e - off : 0u)];
+                before += cnt[c];
             }
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
-                const uint32_t e = threadIdx.x + (uint32_t)j * kTopkThreads;
-                if (e < total) {
-                    sm.cand_key[e] = v[j].x;
-                    sm.cand_idx[e] = v[j].y;
+            before = 0;
+            for (int c = 0; c < used; ++c) {   // uniform
+                const uint32_t cc = sm.wcnt[c];
+                for (uint32_t i = threadIdx.x + kTopkThreads; i < cc; i += kTopkThreads) {
+                    const uint2 e = lists[(size_t)c * kCandCap + i];
+                    sm.cand_key[before + i] = e.x;
+                    sm.cand_idx[before + i] = e.y;
                 }
+                before += cc;
             }
             resolve_prepare(sm);
             lds_barrier();
@@ -844,8 +916,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
 
 size_t topk_ws_bytes_per_row(int64_t row_stride, int32_t k) {
     (void)k;
-    const int64_t nch = (row_stride + kStreamChunk - 1) / kStreamChunk;
-    if (nch < kMinSplitChunks || nch > kMaxSplitChunks) return 0;
+    const int64_t nch = (row_stride + kFilterChunk - 1) / kFilterChunk;
+    if (row_stride < kMinSplitCandidates || nch > kMaxSplitChunks) return 0;
     return split_row_bytes((int)nch);
 }
 
@@ -855,12 +927,13 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
     if (rows == 0) return hipSuccess;
     const size_t per_row = topk_ws_bytes_per_row(row_stride, k);
     // Few very long rows leave most of the GPU idle at one workgroup per row, each streaming its row
-    // twice: split the filter pass over the rows' chunks when the workspace allows (rows of at least
-    // 8 chunks, fewer than 256 rows).  Measured on 64 rows of up to 65536 candidates (4 chunks) the
-    // split is slower, 25.2 against 18.8 us: the kernel boundary costs about 2.5 us and the select
-    // kernel's load of the freshly written lists about 5 us.  The result is identical either way.
-    const int nch = (int)((row_stride + kStreamChunk - 1) / kStreamChunk);
-    if (per_row > 0 && nch >= kMinSplitChunks && rows < 256 && ws && ws_bytes >= per_row) {
+    // twice: split the filter pass over the rows' 32768-candidate chunks when the workspace allows
+    // (rows of more than 114688 candidates, fewer than 256 rows).  Measured on MI355X: 128 rows of up
+    // to 131072 candidates take 28.6 us split (chunk workgroups in one round, two per CU) against
+    // 35.2 us at one workgroup per row.  Rows of up to 65536 candidates stay whole: the kernel
+    // boundary alone costs about 3 us there.  The result is identical either way.
+    const int nch = (int)((row_stride + kFilterChunk - 1) / kFilterChunk);
+    if (per_row > 0 && rows < 256 && ws && ws_bytes >= per_row) {
         const int per_batch = (int)min((size_t)rows, ws_bytes / per_row);
         for (int r0 = 0; r0 < rows; r0 += per_batch) {
             const int nr = min(per_batch, rows - r0);

@@ -72,13 +72,15 @@ def test_unsupported_capacity_names_the_parameter(field, value, needle):
 
 def test_workspace_size_derives_from_capacity_only():
     tk, at = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=131072))
-    assert tk == 64 * (256 + 8 * 12288 * 8)    # rows x (chunk counts + 8 chunk lists of 12288 pairs)
+    assert tk == 64 * (256 + 4 * 12288 * 8)    # rows x (chunk counts + 4 lists of 12288 pairs, 32768-candidate chunks)
     tk_short, _ = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=114688))
-    assert tk_short == 0                         # 7 chunks: rows are never split
-    tk_long, _ = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=262145))
+    assert tk_short == 0                         # rows of at most 114688 candidates are never split
+    tk_long, _ = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=524289))
     assert tk_long == 0                          # more than 16 chunks: rows are never split
+    tk_max, _ = smla.workspace_size(_cap(max_rows=2, max_k=2048, num_heads=64, max_candidates=524288))
+    assert tk_max == 2 * (256 + 16 * 12288 * 8)   # 16 chunks, the most a split row has
     tk_many, _ = smla.workspace_size(_cap(max_rows=4096, max_k=512, num_heads=64, max_candidates=120000))
-    assert tk_many == 255 * (256 + 8 * 12288 * 8)   # the split serves calls of fewer than 256 rows
+    assert tk_many == 255 * (256 + 4 * 12288 * 8)   # the split serves calls of fewer than 256 rows
     _, at = smla.workspace_size(_cap(max_rows=64, max_k=2048, num_heads=64, max_candidates=65536))
     assert at == 64 * 4 * 64 * (512 * 2 + 4)    # rows x splits x heads x (bf16 partial + fp32 LSE)
     _, at1 = smla.workspace_size(_cap(max_rows=1, max_k=512, num_heads=64))

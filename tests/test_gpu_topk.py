@@ -142,20 +142,21 @@ def test_causal_lengths_match_oracle():
         assert np.array_equal(got, ref), (first_pos, T)
 
 
-@pytest.mark.parametrize("stride", [114689, 131072, 200003, 262144])
+@pytest.mark.parametrize("stride", [114689, 131072, 200003, 262144, 524288])
 def test_chunked_rows_equal_single_workgroup_rows(stride):
-    """Few long rows are split into 16384-wide chunks and merged; the result must equal both the
+    """Few long rows are split into 32768-wide chunks and merged; the result must equal both the
     oracle and the one-workgroup-per-row path, including selections that straddle chunks, ties
     across chunk borders and rows shorter than k."""
     g = torch.Generator(device=DEV).manual_seed(stride)
     k = 2048
     lens = [0, 1, k - 1, k, k + 1, 16383, 16384, 16385, 16384 + k, stride - 1, stride, stride + 5,
-            (stride * 3) // 4, 40000, 9000, 2**31 - 1]
+            (stride * 3) // 4, 40000, 9000, 2**31 - 1, 32767, 32768, 32769, 32768 + k]
     R = len(lens)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     s = torch.round(torch.randn((R, stride), generator=g, device=DEV) * 2) / 2       # heavy ties
     s[0:4] = 1.0                                            # all equal: the first k indices win
-    s[4, 16384 - 1000:] = 50.0                              # winners straddle the first chunk border
+    s[4, 32768 - 1000:] = 50.0                              # winners straddle the first chunk border
+    s[17, 32768 - 300:32768 + 300] = 7.0                    # a tie straddling the first chunk border
     s[5, ::5] = float("nan")
     s[6, -k:] = float("inf")
     log(f"[topk] chunked stride={stride}")
