@@ -787,7 +787,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(const float* 
     __shared__ uint32_t hist[1 << 12];
     __shared__ uint32_t scratch[kTopkWaves + 2];
     __shared__ uint32_t res[3];
-    __shared__ uint32_t wcnt[kTopkWaves];
+    __shared__ uint32_t wcnt[2 * kTopkWaves];   // per (half, wave) counts, then list offsets
     const int row = blockIdx.x / nch, c = blockIdx.x % nch;
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const int64_t L = clamped_length(lengths, row, row_stride);
