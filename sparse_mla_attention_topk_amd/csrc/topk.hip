@@ -152,6 +152,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
 
 // LDS capacity of the filtered path.
 constexpr int kCandCap = 12288;      // candidates passing the filter, resolved in LDS
+constexpr uint32_t kSegCap = kCandCap / 16;   // one wave's segment of the list (one-pass streaming)
 static_assert(kCandCap < (1 << 16), "the emission scan packs two list counts into 16 bits each");
 constexpr int kSampleLog2 = 12;      // 4096 sampled candidates, 4 per thread
 
@@ -250,6 +251,64 @@ __device__ __forceinline__ void settle_slots_buffer(int32_t L, int32_t base, flo
     for (int u = 0; u < U; ++u)
         if (slot_base<U>(base, u) + kWave > L)   // uniform: only a slot that straddles L has lanes to fix
             v[u] = slot_pos<U>(base, u) < L ? v[u] : __builtin_nanf("");
+}
+
+// Issues every load of the U slots of the chunk at `base` through the row's buffer resource, with no
+// branch: slots at or past L read 0 without touching memory (settle_slots_buffer makes them NaN).
+// Because no path skips the loads, a later wait for these values can leave loads issued after them
+// in flight, which lets a streaming loop keep the next chunk's loads going while it works on this one.
+template <int U>
+__device__ __forceinline__ void issue_chunk_buffer(const DirectScores& src, int32_t L, int32_t base, float* v) {
+    static_assert(U * kWave * (int)sizeof(float) <= 4096, "slot steps must fit the load offset field");
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src.s, (short)0, L * (int32_t)sizeof(float), 0x00020000);
+    const int32_t voff = slot_pos<U>(base, 0) * (int32_t)sizeof(float);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = __builtin_bit_cast(float,
+                                  __builtin_amdgcn_raw_buffer_load_b32(rs, voff + u * kWave * (int32_t)sizeof(float), 0, 0));
+}
+
+// One-pass streaming of a long row: wave w takes the positions [w * span, (w + 1) * span) of the row
+// (span a multiple of 1024), in steps of kStreamU slots of 64 positions; a step starting at position
+// `pb` holds pb + u * 64 + lane in slot u.  Loads go through the row's buffer resource `rs` with no
+// branch (positions at or past L read 0 without touching memory).
+__device__ __forceinline__ void issue_stretch(__amdgpu_buffer_rsrc_t rs, int32_t pb, float* v) {
+    const int32_t voff = (pb + (int32_t)(threadIdx.x & (kWave - 1))) * (int32_t)sizeof(float);
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u)
+        v[u] = __builtin_bit_cast(float,
+                                  __builtin_amdgcn_raw_buffer_load_b32(rs, voff + u * kWave * (int32_t)sizeof(float), 0, 0));
+}
+// Waits for a step's values; positions at or past L become NaN (only a slot that straddles L has
+// lanes to fix, decided per wave).
+__device__ __forceinline__ void settle_stretch(int32_t pb, int32_t L, float* v) {
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u)
+        if (pb + u * kWave + kWave > L)   // uniform
+            v[u] = pb + u * kWave + (int32_t)(threadIdx.x & (kWave - 1)) < L ? v[u] : __builtin_nanf("");
+}
+// Appends a step's candidates with v >= tf to the LDS list from `pos` (uniform), in position order;
+// entries at or beyond `limit` are counted but not written.  Returns the offset after the last one.
+__device__ __forceinline__ uint32_t append_stretch(const float* v, int32_t pb, float tf, uint32_t pos,
+                                                   uint32_t limit, uint32_t* cbits, uint32_t* cidx) {
+    const uint32_t pos0 = (uint32_t)(pb + (int32_t)(threadIdx.x & (kWave - 1)));
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        const bool pred = v[u] >= tf;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+        if (pred) {
+            const uint32_t p = pos + lanes_below(m);
+            if (p < limit) {
+                cbits[p] = __float_as_uint(v[u]);
+                cidx[p] = pos0 + (uint32_t)(u * kWave);
+            }
+        }
+        pos += (uint32_t)__popcll(m);
+    }
+    return pos;
 }
 
 // Number of this wave's slots with v >= tf (uniform in the wave).
@@ -415,18 +474,30 @@ __device__ __forceinline__ void resolve_prepare(TopkShared& sm) {
 // holds more keys than are needed, it is settled directly when its keys are all equal or number at
 // most kSmallBin (ranking), else narrowed by a digit fitted to its keys' own range.  A selected
 // candidate's output slot is the number of selected candidates before it in the list.
+//
+// With `seg`, the list is kTopkWaves segments instead of one run: segment w starts at w * kSegCap and
+// holds seg[w] entries, and wave w walks segment w (the segments in order are position order).
 template <class Src>
 __device__ __forceinline__ void resolve_list(const Src& src, uint32_t total, int32_t n, int32_t k,
                                              int32_t* __restrict__ o, TopkShared& sm,
-                                             const uint32_t* first = nullptr) {
+                                             const uint32_t* first = nullptr, const uint32_t* seg = nullptr) {
     uint32_t* hist = sm.hist;
     uint32_t* scratch = sm.scratch;
     uint32_t* res = sm.res;
     uint32_t* cand_key = sm.cand_key;
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
-    const uint32_t c0 = threadIdx.x * per;
-    const uint32_t c1 = c0 + per < total ? c0 + per : total;
+    uint32_t c0, c1;
+    if (seg) {
+        const uint32_t w = (uint32_t)wave_index(), cw = seg[w];
+        const uint32_t per = (cw + kWave - 1) / kWave;                 // <= kSegCap / 64 = 12
+        const uint32_t lo = (uint32_t)lane * per < cw ? (uint32_t)lane * per : cw;
+        c0 = w * kSegCap + lo;
+        c1 = w * kSegCap + (lo + per < cw ? lo + per : cw);
+    } else {
+        const uint32_t per = (total + kTopkThreads - 1) / kTopkThreads;   // <= 12
+        c0 = threadIdx.x * per;
+        c1 = c0 + per < total ? c0 + per : total;
+    }
     uint32_t base;
     int s;
     if (first) {
@@ -636,7 +707,10 @@ __device__ __forceinline__ void select_general(const Src& src, int64_t L, int32_
 // is preceded by all those at or above tf), so the selection is finished on that short list.  The
 // sample only decides how fast the row goes; if the count check fails the row takes the general
 // path, with the same result.  Rows of at most kCandCap candidates list all of them.
-template <class Src>
+// LONG: rows may be longer than kResident (the streaming forms are compiled in); without it every row
+// is at most kResident long and the kernel holds the registers-resident form alone, whose register
+// allocation the streaming code would otherwise crowd.
+template <bool LONG, class Src>
 __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k, int32_t* __restrict__ o,
                                             TopkShared& sm) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -665,7 +739,7 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
     }
     if (filter_eligible(L, n)) {   // uniform
         const int32_t L32 = (int32_t)L;
-        const bool resident = L <= kResident;
+        const bool resident = !LONG || L <= kResident;
         float v[kResidentU];
         float sv[4];
         load_sample(src, L, sv);
@@ -680,11 +754,65 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
                 const uint32_t c = wave_count_ge<kResidentU>(v, L32, 0, tf);
                 if (lane == 0) sm.wcnt[wid] = c;
             } else {
-                for (int ch = 0; ch < nch; ++ch) {
-                    float cv[kStreamU];
-                    load_slots<kStreamU>(src, L32, ch * kStreamChunk, cv);
-                    const uint32_t c = wave_count_ge<kStreamU>(cv, L32, ch * kStreamChunk, tf);
-                    if (lane == 0) sm.wcnt[ch * kTopkWaves + wid] = c;
+                // One pass: each wave streams its own stretch of the row (double-buffered: the next
+                // step's loads are in flight while this one is appended) into its own list segment;
+                // the segments in wave order are position order.  A stretch with more candidates than
+                // its segment holds (candidates crowded into few positions) sends the row to the
+                // two-pass form below, which lists it as one run.
+                const int32_t span = ((L32 + kTopkThreads * kStreamU - 1) / (kTopkThreads * kStreamU)) *
+                                     (kWave * kStreamU);
+                const int32_t ws = wave_index() * span;
+                const int32_t we = min(ws + span, L32);
+                const int steps = we > ws ? (we - ws + kWave * kStreamU - 1) / (kWave * kStreamU) : 0;   // uniform
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)src.s, (short)0, L32 * (int32_t)sizeof(float), 0x00020000);
+                const uint32_t s0 = (uint32_t)wave_index() * kSegCap;
+                uint32_t pos = s0;
+                float sa[kStreamU], sb[kStreamU];
+                issue_stretch(rs, ws, sa);
+                for (int it = 0; it < steps; it += 2) {   // uniform; stops at the stretch's end, no barrier
+                    const int32_t p0 = ws + it * kWave * kStreamU, p1 = p0 + kWave * kStreamU;
+                    issue_stretch(rs, p1, sb);
+                    settle_stretch(p0, L32, sa);
+                    pos = append_stretch(sa, p0, tf, pos, s0 + kSegCap, sm.cand_key, sm.cand_idx);
+                    issue_stretch(rs, p1 + kWave * kStreamU, sa);
+                    settle_stretch(p1, L32, sb);
+                    if (it + 1 < steps)   // uniform
+                        pos = append_stretch(sb, p1, tf, pos, s0 + kSegCap, sm.cand_key, sm.cand_idx);
+                }
+                if (lane == 0) sm.wcnt[wid] = pos - s0;
+                lds_barrier();
+                uint32_t total1 = 0;
+                bool fits = true;
+#pragma unroll
+                for (int w = 0; w < kTopkWaves; ++w) {
+                    total1 += sm.wcnt[w];
+                    fits = fits && sm.wcnt[w] <= kSegCap;
+                }
+                if (fits) {   // uniform
+                    if (total1 >= (uint32_t)n) {
+                        resolve_list(src, total1, n, k, o, sm, sm.first, sm.wcnt);
+                        return;
+                    }
+                    lds_barrier();
+                    select_general(src, L, n, k, o, sm);   // too few candidates passed the sample's threshold
+                    return;
+                }
+                lds_barrier();   // every wave has read the counts before the two-pass form rewrites them
+                // Chunks in pairs, double-buffered: the next chunk's loads are in flight while this one
+                // is counted.  The loop issues up to two chunks past the row, which read nothing.
+                float ca[kStreamU], cb[kStreamU];
+                issue_chunk_buffer<kStreamU>(src, L32, 0, ca);
+                for (int ch = 0; ch < nch; ch += 2) {   // uniform
+                    const int32_t b0 = ch * kStreamChunk, b1 = b0 + kStreamChunk;
+                    issue_chunk_buffer<kStreamU>(src, L32, b1, cb);
+                    settle_slots_buffer<kStreamU>(L32, b0, ca);
+                    const uint32_t c0 = wave_count_ge<kStreamU>(ca, L32, b0, tf);
+                    if (lane == 0) sm.wcnt[ch * kTopkWaves + wid] = c0;
+                    issue_chunk_buffer<kStreamU>(src, L32, b1 + kStreamChunk, ca);
+                    settle_slots_buffer<kStreamU>(L32, b1, cb);
+                    const uint32_t c1 = wave_count_ge<kStreamU>(cb, L32, b1, tf);
+                    if (lane == 0 && ch + 1 < nch) sm.wcnt[(ch + 1) * kTopkWaves + wid] = c1;
                 }
             }
             lds_barrier();
@@ -696,12 +824,20 @@ __device__ __forceinline__ void select_topk(const Src& src, int64_t L, int32_t k
             if (total >= (uint32_t)n && total <= (uint32_t)kCandCap) {   // uniform
                 if (resident) {
                     wave_append_ge<kResidentU, false>(v, L32, 0, tf, sm.wcnt[wid], sm.cand_key, sm.cand_idx);
-                } else {
-                    for (int ch = 0; ch < nch; ++ch) {
-                        float cv[kStreamU];
-                        load_slots<kStreamU>(src, L32, ch * kStreamChunk, cv);
-                        wave_append_ge<kStreamU, true>(cv, L32, ch * kStreamChunk, tf, sm.wcnt[ch * kTopkWaves + wid],
-                                                       sm.cand_key, sm.cand_idx);
+                } else {   // the same double-buffered pairs of chunks as the count
+                    float ca[kStreamU], cb[kStreamU];
+                    issue_chunk_buffer<kStreamU>(src, L32, 0, ca);
+                    for (int ch = 0; ch < nch; ch += 2) {   // uniform
+                        const int32_t b0 = ch * kStreamChunk, b1 = b0 + kStreamChunk;
+                        issue_chunk_buffer<kStreamU>(src, L32, b1, cb);
+                        settle_slots_buffer<kStreamU>(L32, b0, ca);
+                        wave_append_ge<kStreamU, true>(ca, L32, b0, tf, sm.wcnt[ch * kTopkWaves + wid], sm.cand_key,
+                                                       sm.cand_idx);
+                        issue_chunk_buffer<kStreamU>(src, L32, b1 + kStreamChunk, ca);
+                        settle_slots_buffer<kStreamU>(L32, b1, cb);
+                        if (ch + 1 < nch)   // uniform
+                            wave_append_ge<kStreamU, true>(cb, L32, b1, tf, sm.wcnt[(ch + 1) * kTopkWaves + wid],
+                                                           sm.cand_key, sm.cand_idx);
                     }
                 }
                 lds_barrier();
@@ -719,7 +855,8 @@ __device__ __forceinline__ int64_t clamped_length(const int32_t* lengths, int ro
     return len < 0 ? 0 : (len > row_stride ? row_stride : len);   // clamp before any decision
 }
 
-// One workgroup per row.
+// One workgroup per row (LONG: see select_topk).
+template <bool LONG>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ scores,
                                                                  const int64_t* __restrict__ row_offsets,
                                                                  int64_t row_stride,
@@ -729,7 +866,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     const int row = blockIdx.x;
     const int64_t L = clamped_length(lengths, row, row_stride);
     const int64_t off = row_offsets ? row_offsets[row] : (int64_t)row * row_stride;
-    select_topk(DirectScores{scores + off}, L, k, out + (int64_t)row * k, sm);
+    select_topk<LONG>(DirectScores{scores + off}, L, k, out + (int64_t)row * k, sm);
 }
 
 // ---- few long rows: the filter pass split over the row's chunks of kFilterChunk positions ----
@@ -911,7 +1048,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const float* 
         select_general(src, L, n, k, o, sm);
         return;
     }
-    select_topk(src, L, k, o, sm);
+    select_topk<true>(src, L, k, o, sm);
 }
 
 size_t topk_ws_bytes_per_row(int64_t row_stride, int32_t k) {
@@ -947,8 +1084,12 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
         }
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_offsets,
-                       row_stride, lengths, k, out);
+    if (row_stride > kResident)
+        hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_offsets,
+                           row_stride, lengths, k, out);
+    else
+        hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_offsets,
+                           row_stride, lengths, k, out);
     return hipGetLastError();
 }
 

@@ -81,6 +81,37 @@ def test_clustered_candidates():
     _check(s.to(DEV), lengths.to(DEV), 2048, what="clustered best candidates")
 
 
+def test_long_rows_one_workgroup_clustered_and_spread():
+    """Rows longer than the registers hold (131072 and 200003 candidates), one workgroup per row: spread
+    candidates (one pass, every wave listing its own stretch of the row) and candidates crowded into one
+    stretch (a wave's list overflows and the row is listed in two passes), with ties, bit-exact against
+    the oracle and against the split path."""
+    g = torch.Generator(device="cpu").manual_seed(23)
+    k = 2048
+    for stride in (131072, 200003):
+        R = 8
+        s = torch.randn((R, stride), generator=g, dtype=torch.float32)
+        lens = torch.full((R,), stride, dtype=torch.int32)
+        for r, (start, width, tied) in enumerate([(0, 6000, False), (70000, 3000, True), (stride - 5000, 5000, False),
+                                                 (12000, 9000, True)]):
+            band = torch.randn((width,), generator=g, dtype=torch.float32).abs() + 4.0
+            if tied:
+                band = torch.round(band * 4) / 4
+            s[r, start:start + width] = band
+        s[5] = torch.round(s[5] * 2) / 2                       # spread, heavy ties
+        lens[6] = 100001                                        # a stretch that ends inside the row
+        lens[7] = 70000
+        s_d, lens_d = s.to(DEV), lens.to(DEV)
+        log(f"[topk] long rows stride={stride}, one workgroup per row")
+        whole = smla.topk_per_row(s_d, k, lengths=lens_d, split=False)
+        split = smla.topk_per_row(s_d, k, lengths=lens_d)
+        torch.cuda.synchronize()
+        assert torch.equal(whole, split)
+        ref = _oracle(s.numpy(), lens.numpy(), k)
+        bad = np.nonzero((whole.cpu().numpy() != ref).any(axis=1))[0]
+        assert bad.size == 0, f"stride {stride}: rows {bad[:5].tolist()} differ"
+
+
 @pytest.mark.parametrize("k", [1, 2, 63, 192, 256, 2000, 2048, 4096, 16384])
 def test_k_values_and_ragged_lengths(k):
     g = torch.Generator(device=DEV).manual_seed(1000 + k)
