@@ -1063,14 +1063,20 @@ hipError_t launch_topk(const float* scores, const int64_t* row_offsets, int64_t 
                        hipStream_t stream) {
     if (rows == 0) return hipSuccess;
     const size_t per_row = topk_ws_bytes_per_row(row_stride, k);
-    // Few very long rows leave most of the GPU idle at one workgroup per row, each streaming its row
-    // twice: split the filter pass over the rows' 32768-candidate chunks when the workspace allows
-    // (rows of more than 114688 candidates, fewer than 256 rows).  Measured on MI355X: 128 rows of up
-    // to 131072 candidates take 28.6 us split (chunk workgroups in one round, two per CU) against
-    // 35.2 us at one workgroup per row.  Rows of up to 65536 candidates stay whole: the kernel
-    // boundary alone costs about 3 us there.  The result is identical either way.
+    // Few very long rows leave most of the GPU idle at one workgroup per row: split the filter pass
+    // over the rows' 32768-candidate chunks when the workspace allows (rows of more than 114688
+    // candidates, fewer than 256 rows) and the split pays.  Measured on MI355X (lengths uniform in
+    // [stride/4, stride], us, split against one workgroup per row, which lists a long row in one pass):
+    //   64 rows: 23.1 / 25.0 at stride 131072, 29.6 / 37.5 at 262144, 45.7 / 112 at 524288;
+    //   128 rows: 28.9 / 25.9 at 131072, 44.5 / 38.7 at 262144, 57.6 / 53.2 at 393216, 76.1 / 113 at 524288;
+    //   200 rows: 43.0 / 26.8 at 131072, 79.8 / 59.4 at 393216, 111 / 172 at 524288.
+    // So the split runs for launches of at most a third as many rows as CUs, or rows of more than
+    // 393216 candidates.  The result is identical either way.
+    int dev = 0, num_cu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    const bool split_pays = 3 * rows <= num_cu || row_stride > 393216;
     const int nch = (int)((row_stride + kFilterChunk - 1) / kFilterChunk);
-    if (per_row > 0 && rows < 256 && ws && ws_bytes >= per_row) {
+    if (per_row > 0 && rows < 256 && split_pays && ws && ws_bytes >= per_row) {
         const int per_batch = (int)min((size_t)rows, ws_bytes / per_row);
         for (int r0 = 0; r0 < rows; r0 += per_batch) {
             const int nr = min(per_batch, rows - r0);
