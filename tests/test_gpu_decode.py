@@ -163,6 +163,51 @@ def test_head_split_invariance(big):
     assert bits_equal(o1[0], outs[5][0][9]) and bits_equal(l1[0], outs[5][1][9])
 
 
+@pytest.mark.parametrize("k,with_sink", [(2048, True), (2048, False), (1024, True)])
+def test_ragged_rows_in_multi_split_workgroups(k, with_sink):
+    """320 rows x 64 heads is a launch large enough that each workgroup runs all 64 heads of several
+    consecutive splits of its row; a batch of 7 rows runs one split of 16 heads per workgroup.  The
+    shared rows -- an empty row, rows whose later splits have few or no valid slots (a split followed
+    by one without tiles), a row with no valid slot at all -- must agree bit for bit, sink or not, and
+    match the oracle."""
+    B = 320
+    wl = W.decode_workload(f"merge_{k}", B=B, H=64, k=k, ctx_lo=1, ctx_hi=2 * k + 100, kv_dtype=W.KV_BF16,
+                           seed=500 + k, device=DEV)
+    rs = wl.sets[0]
+    lens = rs.lengths.clone()
+    lens[5] = 0           # empty row
+    lens[6] = 300         # splits 1.. empty
+    lens[7] = min(513, int(rs.lengths[7]))
+    idx = smla.topk_per_row(rs.scores, k, lengths=lens)
+    idx[8] = -1           # no valid slot in any split
+    if with_sink:
+        g = torch.Generator(device="cpu").manual_seed(k)
+        sink = torch.randn(64, generator=g) * 3.0 + 2.0
+        sink[1::5] = -float("inf")
+        sink = sink.to(DEV)
+    else:
+        sink = None
+
+    def run(rows):
+        lse = torch.empty((len(rows), 64), dtype=torch.float32, device=DEV)
+        out, _ = smla.sparse_mla_decode(rs.q[rows].contiguous(), wl.cache.kv, wl.cache.block_table,
+                                        idx[rows].contiguous(), wl.scale, row_req=rs.row_req[rows].contiguous(),
+                                        lse=lse, sink=sink)
+        torch.cuda.synchronize()
+        return out, lse
+
+    out, lse = run(list(range(B)))
+    rows = [0, 5, 6, 7, 8, 100, 319]
+    o1, l1 = run(rows)
+    assert bits_equal(o1, out[rows]) and bits_equal(l1, lse[rows])
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(rs.q[rows]), kv_np(wl.cache.kv), W.KV_BF16,
+                                      wl.cache.block_table.cpu().numpy(), rs.row_req.cpu().numpy()[rows],
+                                      idx.cpu().numpy()[rows], wl.scale,
+                                      sink=None if sink is None else sink.cpu().numpy().astype(np.float64))
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, f"ragged rows, multi-split workgroups k={k} sink={with_sink}")
+    log(f"[decode] ragged rows in multi-split workgroups k={k} sink={with_sink} {st}")
+
+
 def test_maximum_k_and_many_splits():
     """k = 16384, the largest supported width: 32 splits, combined in order by the split-combine kernel
     in several groups of loads."""

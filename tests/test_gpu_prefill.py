@@ -90,3 +90,29 @@ def test_mixed_batch_bit_identical(pf):
     assert bits_equal(mout[dec_slots], dout[src[dec_slots] - T])
     assert bits_equal(mlse[dec_slots], dlse[src[dec_slots] - T])
     log(f"[prefill] mixed batch of {T + n_dec} rows bit-identical")
+
+
+def test_prefill_from_position_zero():
+    """A chunk of 3072 query tokens at positions 0..3071 of a new sequence (causal: row t has t + 1
+    candidates, so the rows below 2048 fill only their first splits and leave the rest without
+    tiles): the large launch, whose workgroups run all heads of consecutive splits of a row, against
+    the oracle on seeded rows, and bit for bit against the same rows in a launch of 10 rows."""
+    T = 3072
+    wl = W.prefill_chunk(DEV, seed=41, T=T, ctx=T, n_dec=1, dec_lo=64, dec_hi=64)
+    lengths = smla.fill_causal_lengths(wl.first_pos, T, device=DEV)
+    idx = smla.topk_per_row(wl.scores, wl.k, lengths=lengths)
+    bt = wl.cache.block_table[0].contiguous()
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_prefill_chunk(wl.q, wl.cache.kv, bt, idx, wl.scale, lse=lse)
+    rows = [0, 1, 63, 511, 512, 700, 1500, 2047, 2048, 3071]
+    lse1 = torch.empty((len(rows), wl.H), dtype=torch.float32, device=DEV)
+    o1, _ = smla.sparse_mla_prefill_chunk(wl.q[rows].contiguous(), wl.cache.kv, bt, idx[rows].contiguous(), wl.scale,
+                                          lse=lse1)
+    torch.cuda.synchronize()
+    assert bits_equal(o1, out[rows]) and bits_equal(lse1, lse[rows])
+    ref_idx = O.topk_rows(wl.scores[rows].cpu().numpy(), lengths.cpu().numpy()[rows], wl.k)
+    assert np.array_equal(idx.cpu().numpy()[rows], ref_idx)
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(wl.q[rows]), kv_np(wl.cache.kv), W.KV_BF16,
+                                      wl.cache.block_table.cpu().numpy(), [0] * len(rows), ref_idx, wl.scale)
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, f"prefill from position 0 ({len(rows)} rows)")
+    log(f"[prefill] from position 0: {st}")
