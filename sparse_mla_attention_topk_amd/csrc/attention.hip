@@ -201,10 +201,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // tile it+1 is expanded)
     __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
-    // Per-head output multiplier at the end of a split, one table per split parity: after a split's
-    // final barrier the score waves may run through a next split without tiles (no barrier) into its
-    // end before the value waves have read this split's multipliers.
-    __shared__ float xmul[2][4][16];
+    // Per-head output multiplier at the end of a split, one table per split parity (bf16): after a
+    // split's final barrier the score waves may run through a next split without tiles (no barrier)
+    // into its end before the value waves have read this split's multipliers.  FP8 workgroups run one
+    // split each and keep one table.
+    constexpr int kMulTables = KV_FP8 ? 1 : 2;
+    __shared__ float xmul[kMulTables][4][16];
     __shared__ int s_first[kMaxGroup], s_last[kMaxGroup];
     auto xs = [&](int b, int j) -> f32x4_t* { return &xs_own[b][j][0]; };
     auto pw32 = [&](int b, int j) -> f32x4_t* { return (f32x4_t*)&pfrag[b][0][0] + j * kWave; };   // FP8 weights
@@ -733,7 +735,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 mult = c / lall;
                 lse_v = (mn + __log2f(lall)) * kLn2;
             }
-            xmul[ls & 1][shb][lane] = mult;
+            xmul[KV_FP8 ? 0 : (ls & 1)][shb][lane] = mult;
         }
         __syncthreads();
         if (score_ok && !half && lane < 16) {
@@ -872,7 +874,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if (b >= nhb) break;
-            float inv = xmul[ls & 1][b][lane & 15];
+            float inv = xmul[KV_FP8 ? 0 : (ls & 1)][b][lane & 15];
             if (KV_FP8 && e_run > 0) inv = __builtin_ldexpf(inv, e_run - 127);   // undo the scale normalization
             int head = head0 + 16 * b + (lane & 15);
             if (KV_FP8) asm volatile("" : "+v"(head));   // FP8: addresses computed per split (not held across splits)
