@@ -8,19 +8,22 @@
 //     (key descending, index ascending), so the n = min(k, L) selected candidates are exactly
 //       { j : key_j > T } U { the first `need` indices j with key_j == T }
 //     for the key T of the n-th candidate and need = n - #{key > T};
-//   * pass 1 histograms the top 12 key bits in LDS and finds the boundary bucket;
-//   * pass 2 marks every candidate above the bucket in an LDS bitmask (wave ballots) and gathers the
-//     bucket's candidates into LDS, where T is resolved by radix selection on the remaining 20 bits
-//     (or the whole bucket is taken when it holds exactly the missing count);
-//   * the selection is emitted by an ordered scan of the bitmasks: block-wide prefix sums of the
-//     per-word popcounts give each selected candidate its output slot, so the output is ascending
-//     by construction (no sort) and the -1 tail is filled afterwards.
-//   Rows longer than the LDS masks, or with a boundary bucket too large for LDS (massive ties),
-//   take the general path: further radix passes over the row and an ordered compaction that
-//   rereads it with wave ballots and block prefix sums.
-// One 1024-thread workgroup owns one row; every decision is made from the clamped length that all
-// threads read, so the result is a pure function of the row (batch-invariant, no inter-workgroup
-// synchronization of any kind).
+//   * filtered path (select_topk): a threshold from a fixed sample of the row lets roughly 1.25 n
+//     candidates through; they are listed in LDS in position order (counts, a block scan, appends),
+//     and T is found on that short list by narrowing a key interval with LDS histograms
+//     (resolve_list).  Rows of at most kCandCap candidates list all of them;
+//   * general path (select_general), for rows the filter cannot serve (a threshold that lets too few
+//     or too many through, massive ties): radix passes over the whole row find T, and an ordered
+//     compaction rereads it with wave ballots and block prefix sums;
+//   * either way a selected candidate's output slot is the number of selected candidates before it in
+//     position order, so the output is ascending by construction (no sort), and the -1 tail is filled
+//     afterwards;
+//   * few long rows may split the filter pass over several workgroups per row (topk_filter_kernel),
+//     whose position-ordered lists one workgroup per row then concatenates and resolves
+//     (topk_select_kernel).
+// One 1024-thread workgroup owns one row (or one chunk of it); every decision is made from the clamped
+// length that all threads read, so the result is a pure function of the row (batch-invariant, no
+// inter-workgroup synchronization of any kind).
 #include "smla_device.h"
 #include "smla_internal.h"
 
