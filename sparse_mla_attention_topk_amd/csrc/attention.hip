@@ -8,10 +8,14 @@
 //   lse[h] = log sum_j exp(s[h, j])
 // for the tokens j listed in the row's index slots (entries < 0 skipped).
 //
-// Work decomposition.  One workgroup of 16 waves owns one (row, split, 64-head block) and is the only
-// workgroup on its CU.  A split is 512 consecutive index slots (FP8 caches: 1024, two units of 512
-// run one after the other with one softmax state); the number of splits depends on k and the cache
-// type only, so the reduction order of a row never depends on the batch.  The split's slots are processed
+// Work decomposition.  One workgroup of 16 waves is the only workgroup on its CU and owns one work
+// item: a run of consecutive units of one row (a unit is 512 consecutive index slots) for a block of
+// 64 heads.  A split is one unit (FP8 caches: two units run one after the other with one softmax
+// state); the number of splits depends on k and the cache type only, so the reduction order of a row
+// never depends on the batch.  Large launches give a workgroup 2 or 4 consecutive splits of a row, one
+// after the other (the index translation and Q serve them all); small launches split the 64 heads over
+// 2 or 4 workgroups of 32 or 16 heads.  Either way every split is reduced in the same order with its
+// own softmax state, so the bits do not change.  The split's slots are processed
 // in tiles of 32 tokens through a 3-stage LDS ring.  The gather of a tile (36 loads of 1 KB, direct
 // to LDS with global_load_lds_dwordx4) is spread over all 16 waves: the rate at which random records
 // arrive grows with the number of waves per CU issuing loads, measured on MI355X.  Records are stored
