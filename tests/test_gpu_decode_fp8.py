@@ -70,7 +70,7 @@ def test_fp8_batch_invariance(fp8):
     assert bits_equal(o2, out[perm]) and bits_equal(l2, lse[perm])
 
 
-@pytest.mark.parametrize("H,k", [(16, 1), (16, 192), (48, 513), (64, 1024), (128, 2048), (64, 2500)])
+@pytest.mark.parametrize("H,k", [(16, 1), (16, 192), (48, 513), (64, 1024), (128, 2048), (64, 2500), (16, 16384)])
 def test_fp8_heads_and_widths(H, k):
     wl = W.decode_workload(f"fp8_hk_{H}_{k}", B=5, H=H, k=k, ctx_lo=max(1, k // 2), ctx_hi=3 * k + 70,
                            kv_dtype=W.KV_FP8, seed=200 + H + k, device=DEV, score_kind="eighths")

@@ -87,11 +87,15 @@ def test_sink_row_alone_equals_in_batch(wl):
     assert bits_equal(o1[0], out[1]) and bits_equal(l1[0], lse[1])
 
 
-def test_sink_fp8_cache():
-    wl8 = W.decode_workload("tiny_fp8", B=3, H=32, k=1024, ctx_lo=1500, ctx_hi=4000, kv_dtype=W.KV_FP8, seed=12, device=DEV)
+@pytest.mark.parametrize("k", [1024, 2048, 4500])
+def test_sink_fp8_cache(k):
+    """FP8 caches: one split (k=1024, the sink in the attention epilogue) and several (the sink in the
+    combine of fp32 partials), a ragged last split at k=4500."""
+    wl8 = W.decode_workload(f"tiny_fp8_{k}", B=3, H=32, k=k, ctx_lo=k // 2 + 500, ctx_hi=2 * k + 2000,
+                            kv_dtype=W.KV_FP8, seed=12 + k, device=DEV)
     rs = wl8.sets[0]
-    sink = _sinks(32, 12)
-    idx, out, lse = _decode(wl8, rs, 1024, sink)
+    sink = _sinks(32, 12 + k)
+    idx, out, lse = _decode(wl8, rs, k, sink)
     O_ref, lse_ref = O.attention_rows(bf16_bits_np(rs.q), kv_np(wl8.cache.kv), W.KV_FP8,
                                       wl8.cache.block_table.cpu().numpy(), rs.row_req.cpu().numpy(),
                                       idx.cpu().numpy(), wl8.scale, sink=sink.cpu().numpy().astype(np.float64))

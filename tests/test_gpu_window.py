@@ -2,6 +2,8 @@
 one softmax) against the oracle, bit-identity of a row alone vs in a batch, empty window lists, and the
 width check."""
 
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -15,22 +17,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _call(wl, rs, idx, win, q=None, row_req=None, idx_win=None):
+def _call(wl, rs, idx, win, q=None, row_req=None, idx_win=None, sink=None):
     q = rs.q if q is None else q
     lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=DEV)
     out, _ = smla.sparse_mla_decode_with_window(q, wl.cache.kv, wl.cache.block_table, idx, win.kv, win.block_table,
                                                 win.idx if idx_win is None else idx_win, wl.scale,
                                                 row_req=rs.row_req if row_req is None else row_req,
-                                                kv_dtype=wl.cache.kv_dtype, lse=lse)
+                                                kv_dtype=wl.cache.kv_dtype, lse=lse, sink=sink)
     torch.cuda.synchronize()
     return out, lse
 
 
-def _oracle(wl, rs, idx, win, rows):
+def _oracle(wl, rs, idx, win, rows, sink=None):
     return O.attention_rows_with_window(bf16_bits_np(rs.q), kv_np(wl.cache.kv), wl.cache.kv_dtype,
                                         wl.cache.block_table.cpu().numpy(), idx.cpu().numpy(), kv_np(win.kv),
                                         win.block_table.cpu().numpy(), win.idx.cpu().numpy(),
-                                        rs.row_req.cpu().numpy(), wl.scale, rows=rows)
+                                        rs.row_req.cpu().numpy(), wl.scale, rows=rows,
+                                        sink=None if sink is None else sink.cpu().numpy().astype(np.float64))
 
 
 @pytest.fixture(scope="module")
@@ -97,6 +100,30 @@ def test_window_decode_fp8():
     O_ref, lse_ref = _oracle(wl, rs, idx, win, list(range(8)))
     st = assert_attention_close(out, lse, O_ref, lse_ref, "window decode fp8 k=2048 k_win=192", relative=True)
     log(f"[window] fp8 {st}")
+
+
+@pytest.mark.parametrize("k,kv_dtype", [(700, W.KV_BF16), (2048, W.KV_BF16), (2048, W.KV_FP8)])
+def test_window_decode_with_sink(k, kv_dtype):
+    """Per-head sink logits (some -inf) with the window part: one split (k=700, width 192 in one unit per
+    split) and several (k=2048), bf16 and FP8 caches; a row alone equals the row in the batch."""
+    wl = W.decode_workload(f"win_sink_{k}_{kv_dtype}", B=6, H=64, k=k, ctx_lo=50, ctx_hi=3 * k, kv_dtype=kv_dtype,
+                           seed=80 + k + kv_dtype, device=DEV)
+    win = W.window_cache(wl.cache.ctx_lens, kv_dtype, DEV, seed=81 + k, max_pages=int(wl.cache.block_table.shape[1]))
+    rs = wl.sets[0]
+    g = torch.Generator(device="cpu").manual_seed(k + kv_dtype)
+    sink = torch.randn(64, generator=g) * 3.0 + 2.0
+    sink[2::7] = -float("inf")
+    sink = sink.to(DEV)
+    idx = smla.topk_per_row(rs.scores, wl.k, lengths=rs.lengths)
+    out, lse = _call(wl, rs, idx, win, sink=sink)
+    O_ref, lse_ref = _oracle(wl, rs, idx, win, list(range(6)), sink=sink)
+    st = assert_attention_close(out, lse, O_ref, lse_ref, f"window decode + sink k={k} kv={kv_dtype}",
+                                relative=kv_dtype == W.KV_FP8)
+    one = types.SimpleNamespace(kv=win.kv, block_table=win.block_table, idx=win.idx[2:3].contiguous())
+    o1, l1 = _call(wl, rs, idx[2:3].contiguous(), one, q=rs.q[2:3].contiguous(), row_req=rs.row_req[2:3].contiguous(),
+                   sink=sink)
+    assert bits_equal(o1[0], out[2]) and bits_equal(l1[0], lse[2])
+    log(f"[window] sink k={k} kv={kv_dtype} {st}")
 
 
 def test_window_decode_rejects_unpadded_width(big):
