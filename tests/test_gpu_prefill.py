@@ -116,3 +116,36 @@ def test_prefill_from_position_zero():
                                       wl.cache.block_table.cpu().numpy(), [0] * len(rows), ref_idx, wl.scale)
     st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, f"prefill from position 0 ({len(rows)} rows)")
     log(f"[prefill] from position 0: {st}")
+
+
+def test_prefill_fp8_cache_with_sink():
+    """A prefill chunk over an FP8 cache with per-head sink logits (some -inf): 1024 rows at positions
+    3072..4095 of a 4096-token context, k=2048 (several FP8 splits).  Seeded rows against the oracle, and
+    every row bit-identical to the same rows run as a decode batch of the one request."""
+    T, ctx, k, H = 1024, 4096, 2048, 64
+    g = torch.Generator(device=DEV).manual_seed(91)
+    cache = W.make_paged_cache(torch.tensor([ctx]), W.KV_FP8, g, DEV)
+    q = torch.randn((T, H, 576), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    scores = torch.randn((T, ctx), generator=g, device=DEV, dtype=torch.float32)
+    gs = torch.Generator(device="cpu").manual_seed(92)
+    sink = torch.randn(H, generator=gs) * 3.0 + 2.0
+    sink[3::6] = -float("inf")
+    sink = sink.to(DEV)
+    lengths = smla.fill_causal_lengths(ctx - T, T, device=DEV)
+    idx = smla.topk_per_row(scores, k, lengths=lengths)
+    bt = cache.block_table[0].contiguous()
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    out, _ = smla.sparse_mla_prefill_chunk(q, cache.kv, bt, idx, W.SOFTMAX_SCALE, kv_dtype=W.KV_FP8, lse=lse,
+                                           sink=sink)
+    lse2 = torch.empty_like(lse)
+    out2, _ = smla.sparse_mla_decode(q, cache.kv, cache.block_table, idx, W.SOFTMAX_SCALE, kv_dtype=W.KV_FP8,
+                                     lse=lse2, sink=sink)
+    torch.cuda.synchronize()
+    assert bits_equal(out, out2) and bits_equal(lse, lse2)
+    rows = sorted(set(sample_rows(T, 24, 93) + [0, T - 1]))
+    O_ref, lse_ref = O.attention_rows(bf16_bits_np(q[rows]), kv_np(cache.kv), W.KV_FP8, cache.block_table.cpu().numpy(),
+                                      [0] * len(rows), idx.cpu().numpy()[rows], W.SOFTMAX_SCALE,
+                                      sink=sink.cpu().numpy().astype(np.float64))
+    st = assert_attention_close(out[rows], lse[rows], O_ref, lse_ref, f"prefill fp8 + sink ({len(rows)} rows)",
+                                relative=True)
+    log(f"[prefill] fp8 + sink: {st}")
