@@ -60,7 +60,6 @@ constexpr int kAttnWaves = 16;
 constexpr int kAttnThreads = kAttnWaves * kWave;               // 1024
 constexpr int kScoreWaves = 8;
 constexpr int kTileTok = 32;
-constexpr int kTilesPerSplit = kSplitSlots / kTileTok;         // 16
 constexpr int kMaxUnitTiles = kMaxUnitSlots / kTileTok;        // 24
 constexpr int kStageBytes = kTileTok * kBf16Record;             // 36864
 constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-LDS loads of 1 KB per tile
