@@ -563,7 +563,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     };
     // After the second barrier of tile it, the stage of tile it-1 receives tile it+2: bf16, its value
     // product ends before that barrier; FP8, it was expanded before the first barrier of tile it.
-    auto issue_after_second = [&](int it) { issue_ahead(it + kStages - 1); };
+    // FP8: the value waves issue at the highest wave priority, so their requests go out before the other
+    // waves' work in the phase (measured 1% faster per FP8 call; no gain for bf16, where all waves load).
+    auto issue_after_second = [&](int it) {
+        if (KV_FP8) __builtin_amdgcn_s_setprio(3);
+        issue_ahead(it + kStages - 1);
+        if (KV_FP8) __builtin_amdgcn_s_setprio(0);
+    };
     // FP8: before the third barrier of tile it, this (value) wave's loads of tile it+1 have landed.
     auto wait_next_fp8 = [&](int it) {
         if (KV_FP8 && nload > 0 && it + 1 < ntiles) {
