@@ -26,7 +26,7 @@
 //
 // Roles (at most 128 registers per wave at 16 waves per CU):
 //   score waves 0..7:  wave (hb, half) computes the partial scores of heads hb*16 .. +16 over dims
-//                      288*half .. +288 for the tile's 32 tokens with Q in AGPRs:
+//                      288*half .. +288 for the tile's 32 tokens with Q in registers:
 //                        S^T[16 tok x 16 heads] += K[16 tok x 32 dims] . Q^T    (A = K rows, ds_read_b128)
 //                      The second halves publish their partials through LDS; the first halves add them
 //                      (first half + second half, always in this order), keep the online-softmax state
@@ -176,11 +176,13 @@ constexpr float kRescaleSlack = 8.f;
 // the bf16 path: the 512 e4m3 codes as fp16 (exact: every e4m3 value is an fp16 value), the bf16 rope
 // copied, and the four fp32 group scales of each token into a small table.  The latent part of the
 // scores is an fp16 product: each score wave holds its latent Q slice in fp16, divided per head by a
-// power of two 2^e that keeps it inside the fp16 range (e = 0 unless |q| reaches 2^15, so the
-// conversion from bf16 is exact); the rope part stays bf16.  The scales are applied in fp32: the
-// score waves keep one partial per 128-dim scale group and sum 2^e x scale x partial; the softmax
-// publishes the fp32 weights, and a value wave, whose 64 dims lie in one group, multiplies them by
-// that group's scales, rounds to fp16 and runs the value product in fp16 on the codes as they are.
+// power of two 2^e that keeps it inside the fp16 range (e = 0 unless |q| reaches 2^15).  Entries of at
+// least 2^-14 * 2^e convert from bf16 exactly; smaller ones land in fp16's subnormal range, off by at
+// most 2^-25 * 2^e, far below the score's own fp32 rounding.  The rope part stays bf16.  The scales are
+// applied in fp32: the score waves keep one partial per 128-dim scale group and sum
+// 2^e x scale x partial; the softmax publishes the fp32 weights, and a value wave, whose 64 dims lie in
+// one group, multiplies them by that group's scales, rounds to fp16 and runs the value product in fp16
+// on the codes as they are.
 // At the magnitudes these scales produce, rounding the scaled values, or the scaled weights, to bf16
 // costs far more accuracy than the fp16 weights.
 template <bool KV_FP8>
