@@ -21,12 +21,13 @@
 //   x / s is clamped to [-448, 448] (saturation) and converted by the hardware OCP E4M3 conversion,
 //   which rounds to nearest even.  An all-zero group stores s = 0 and zero codes.  Lane 16g stores
 //   s_g; lanes 0..7 store the rope.
-//   Inverse RoPE (optional): lanes 0..7 hold rope pairs 4l .. 4l+3 (values 8l .. 8l+7); pair i
-//   (a, b) of a token at position p becomes (a c + b s, -a s + b c) with c = cos_sin[p][i],
-//   s = cos_sin[p][32 + i].  Both products are exact in fp64 (8 x 24 significant bits), their sum is
-//   rounded once in fp64 and then to bf16 (nearest even) by scaling to the bf16 unit in the last
-//   place and rounding to an integer, so the stored value is the exactly rounded rotation unless the
-//   fp64 sum itself needed rounding next to a bf16 rounding boundary (at most one bf16 unit apart).
+//   Inverse RoPE (optional): the wave's two tokens have 64 rope pairs, one per lane (lane l: token
+//   l / 32, pair l % 32), so every lane rotates one pair and stores its 4 bytes.  Pair i (a, b) of a
+//   token at position p becomes (a c + b s, -a s + b c) with c = cos_sin[p][i], s = cos_sin[p][32 + i].
+//   Both products are exact in fp64 (8 x 24 significant bits), their sum is rounded once in fp64 and
+//   then to bf16 (nearest even) by scaling to the bf16 unit in the last place and rounding to an
+//   integer, so the stored value is the exactly rounded rotation unless the fp64 sum itself needed
+//   rounding next to a bf16 rounding boundary (at most one bf16 unit apart).
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -67,23 +68,18 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
     return __float_as_uint(r) >> 16;
 }
 
-// One rope chunk (8 bf16 values = 4 pairs) with the rotation of the token's position undone.
-__device__ __forceinline__ uint4 inverse_rope_chunk(uint4 x, float4 c, float4 s) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double a = (double)__uint_as_float(w[i] << 16), b = (double)__uint_as_float(w[i] & 0xffff0000u);
-        const double ci = (double)cc[i], si = (double)ss[i];
-        const double y0 = __builtin_fma(a, ci, b * si);     // b * si is exact in fp64
-        const double y1 = __builtin_fma(b, ci, -(a * si));  // a * si is exact in fp64
-        o[i] = f64_to_bf16_rne(y0) | (f64_to_bf16_rne(y1) << 16);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+// One rope pair (two bf16 values) with the rotation of the token's position undone.
+__device__ __forceinline__ uint32_t inverse_rope_pair(uint32_t w, float c, float s) {
+    const double a = (double)__uint_as_float(w << 16), b = (double)__uint_as_float(w & 0xffff0000u);
+    const double ci = (double)c, si = (double)s;
+    const double y0 = __builtin_fma(a, ci, b * si);     // b * si is exact in fp64
+    const double y1 = __builtin_fma(b, ci, -(a * si));  // a * si is exact in fp64
+    return f64_to_bf16_rne(y0) | (f64_to_bf16_rne(y1) << 16);
 }
 
-// One token's FP8 record from the lane's 8 latent values `lat`.
+// One token's FP8 record from the lane's 8 latent values `lat`; with COPY_ROPE lanes 0..7 also store
+// the rope chunk `rope`.
+template <bool COPY_ROPE>
 __device__ __forceinline__ void write_fp8_record(uint8_t* dst, int lane, uint4 lat, uint4 rope) {
     const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
     float x[8];
@@ -110,7 +106,7 @@ __device__ __forceinline__ void write_fp8_record(uint8_t* dst, int lane, uint4 l
     }
     *(uint2*)(dst + 8 * lane) = make_uint2(lo, hi);
     if ((lane & 15) == 0) *(float*)(dst + 512 + 4 * (lane >> 4)) = s;
-    if (lane < 8) *(uint4*)(dst + 528 + 16 * lane) = rope;
+    if (COPY_ROPE && lane < 8) *(uint4*)(dst + 528 + 16 * lane) = rope;
 }
 
 template <bool FP8, bool ROPE>
@@ -120,10 +116,13 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(const uint16_t* __r
                                                              const float* __restrict__ cos_sin, int64_t max_pos,
                                                              int32_t T, uint8_t* __restrict__ cache,
                                                              int64_t num_slots) {
+    static_assert(kTokPerWave * 32 == kWave, "ROPE: one rope pair per lane");
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kTokPerWave;
+    const int jr = lane >> 5, pr = lane & 31;   // ROPE: this lane's token (of the wave's two) and rope pair
     uint4 lat[kTokPerWave], rope[kTokPerWave];
     int64_t slot[kTokPerWave], pos[kTokPerWave];
+    uint32_t rp = 0u;                           // ROPE: the lane's rope pair
 #pragma unroll
     for (int j = 0; j < kTokPerWave; ++j) {   // every load first (wave-uniform guards)
         const int64_t t = t0 + j;
@@ -135,26 +134,19 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(const uint16_t* __r
             if (ROPE) pos[j] = positions[t];
             const uint16_t* src = in + t * in_row_stride;
             lat[j] = *(const uint4*)(src + 8 * lane);
-            if (lane < 8) rope[j] = *(const uint4*)(src + 512 + 8 * lane);
+            if (!ROPE && lane < 8) rope[j] = *(const uint4*)(src + 512 + 8 * lane);
         }
     }
-    if constexpr (ROPE) {   // a position outside [0, max_pos) leaves the token unwritten
+    if constexpr (ROPE) {
+        if (t0 + jr < T) rp = *(const uint32_t*)(in + (t0 + jr) * in_row_stride + 512 + 2 * pr);
 #pragma unroll
-        for (int j = 0; j < kTokPerWave; ++j)
+        for (int j = 0; j < kTokPerWave; ++j)   // a position outside [0, max_pos) leaves the token unwritten
             if (pos[j] < 0 || pos[j] >= max_pos) slot[j] = -1;
-        float4 c[kTokPerWave], s[kTokPerWave];
-#pragma unroll
-        for (int j = 0; j < kTokPerWave; ++j) {
-            c[j] = s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (slot[j] >= 0 && lane < 8) {
-                const float* row = cos_sin + pos[j] * 64;
-                c[j] = *(const float4*)(row + 4 * lane);
-                s[j] = *(const float4*)(row + 32 + 4 * lane);
-            }
+        const int64_t ps = jr ? pos[1] : pos[0];
+        if ((jr ? slot[1] : slot[0]) >= 0) {
+            const float* row = cos_sin + ps * 64;
+            rp = inverse_rope_pair(rp, row[pr], row[32 + pr]);
         }
-#pragma unroll
-        for (int j = 0; j < kTokPerWave; ++j)
-            if (lane < 8) rope[j] = inverse_rope_chunk(rope[j], c[j], s[j]);
     }
 #pragma unroll
     for (int j = 0; j < kTokPerWave; ++j) {
@@ -162,10 +154,15 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(const uint16_t* __r
         if constexpr (!FP8) {
             uint8_t* dst = cache + slot[j] * kBf16Record;
             *(uint4*)(dst + 16 * lane) = lat[j];
-            if (lane < 8) *(uint4*)(dst + 1024 + 16 * lane) = rope[j];
+            if (!ROPE && lane < 8) *(uint4*)(dst + 1024 + 16 * lane) = rope[j];
         } else {
-            write_fp8_record(cache + slot[j] * kFp8Record, lane, lat[j], rope[j]);
+            write_fp8_record<!ROPE>(cache + slot[j] * kFp8Record, lane, lat[j], rope[j]);
         }
+    }
+    if constexpr (ROPE) {   // lanes 32 j .. 32 j + 31 store token j's 32 pairs (128 contiguous bytes)
+        const int64_t sl = jr ? slot[1] : slot[0];
+        if (sl >= 0 && sl < num_slots)
+            *(uint32_t*)(cache + sl * (FP8 ? kFp8Record : kBf16Record) + (FP8 ? 528 : 1024) + 4 * pr) = rp;
     }
 }
 
