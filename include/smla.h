@@ -239,7 +239,7 @@ smla_status smla_kv_cache_write(const void* kv_in, int64_t in_row_stride, const 
  * fused RoPE and KV-insert operator).  The pages do not define the rotation; the convention here:
  *   positions: int64 [T], the position of each token; 8-byte aligned.
  *   cos_sin:   fp32 [max_pos, 64]: row p holds cos(theta_p,i) for i < 32, then sin(theta_p,i);
- *              16-byte aligned.  Rope pair i is (rope[2i], rope[2i+1]).
+ *              4-byte aligned.  Rope pair i is (rope[2i], rope[2i+1]).
  *   The stored rope pair is (a c + b s, -a s + b c) for the input pair (a, b), c = cos_sin[p][i],
  *   s = cos_sin[p][32 + i]: the rotation by -theta, which undoes a rotation by +theta.  It is
  *   evaluated with exact products and one fp64 sum, then rounded to bf16 (nearest even); the result

@@ -332,7 +332,7 @@ smla_status smla_kv_cache_write_rope(const void* kv_in, int64_t in_row_stride, c
     if (!positions) return fail(SMLA_ERR_INVALID_ARG, "positions is NULL");
     if (!cos_sin) return fail(SMLA_ERR_INVALID_ARG, "cos_sin is NULL");
     if (!aligned(positions, 8)) return fail(SMLA_ERR_ALIGNMENT, "positions must be 8-byte aligned");
-    if (!aligned(cos_sin, 16)) return fail(SMLA_ERR_ALIGNMENT, "cos_sin must be 16-byte aligned");
+    if (!aligned(cos_sin, 4)) return fail(SMLA_ERR_ALIGNMENT, "cos_sin must be 4-byte aligned");
     return hip_status(smla::launch_kv_cache_write(kv_in, in_row_stride, slot_mapping, positions, cos_sin, max_pos, T,
                                                   cache, kv_dtype, num_pages, (hipStream_t)stream),
                       "kv_cache_write_rope");

@@ -194,6 +194,27 @@ def test_kv_cache_write_validation(lib):
     assert f(None, 576, None, 0, None, 1, 10, None) == 0        # T = 0: nothing to do
 
 
+def test_kv_cache_write_rope_validation(lib):
+    """The inverse-RoPE write checks its own arguments on the host before enqueueing anything (the
+    cache-write checks it shares are covered above)."""
+    f = lib.smla_kv_cache_write_rope
+    P = _fake
+    # kv_in, in_row_stride, slot_mapping, positions, cos_sin, max_pos, T, cache, kv_dtype, num_pages, stream
+    st = f(P(0x1000), 576, P(0x2000), None, P(0x5000), 64, 4, P(0x3000), 1, 10, None)
+    assert st == 1 and b"positions is NULL" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), P(0x4000), None, 64, 4, P(0x3000), 1, 10, None)
+    assert st == 1 and b"cos_sin is NULL" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), P(0x4000), P(0x5000), 0, 4, P(0x3000), 1, 10, None)
+    assert st == 1 and b"max_pos=0" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), P(0x4004), P(0x5000), 64, 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"positions must be 8-byte aligned" in lib.smla_last_error()
+    st = f(P(0x1000), 576, P(0x2000), P(0x4000), P(0x5002), 64, 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"cos_sin must be 4-byte aligned" in lib.smla_last_error()
+    st = f(P(0x1008), 576, P(0x2000), P(0x4000), P(0x5000), 64, 4, P(0x3000), 1, 10, None)
+    assert st == 4 and b"kv_in must be 16-byte aligned" in lib.smla_last_error()
+    assert f(None, 576, None, None, None, 64, 0, None, 1, 10, None) == 0   # T = 0: nothing to do
+
+
 def test_paged_mqa_logits_validation(lib):
     f = lib.smla_paged_mqa_logits
     P = _fake
