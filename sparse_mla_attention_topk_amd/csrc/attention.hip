@@ -602,14 +602,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
             if (score_ok) {
                 if constexpr (!KV_FP8) {
-#pragma unroll
-                    for (int kk = 0; kk < 9; ++kk) {
+                    // The K operands are read kKAhead steps ahead of the MFMAs that use them, and the
+                    // scheduling barriers keep that order: left to itself, the scheduler put each read
+                    // right before its MFMA in the steady-state tile loop, so every MFMA waited for a
+                    // whole LDS round trip.
+                    constexpr int kKAhead = 2;
+                    bf16x8_t ka0[9], ka1[9];
+                    auto read_k = [&](int kk) {
                         const int kg = 9 * half + kk;      // kk step over the full 576 dims
                         const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
-                        const bf16x8_t a0 = *(const bf16x8_t*)(ap);
-                        const bf16x8_t a1 = *(const bf16x8_t*)(ap + 16 * kBf16Record);
-                        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[kk], s0, 0, 0, 0);
-                        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[kk], s1, 0, 0, 0);
+                        ka0[kk] = *(const bf16x8_t*)(ap);
+                        ka1[kk] = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                    };
+#pragma unroll
+                    for (int kk = 0; kk < kKAhead; ++kk) read_k(kk);
+#pragma unroll
+                    for (int kk = 0; kk < 9; ++kk) {
+                        if (kk + kKAhead < 9) read_k(kk + kKAhead);
+                        __builtin_amdgcn_sched_barrier(0);
+                        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kk], qv[kk], s0, 0, 0, 0);
+                        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[kk], qv[kk], s1, 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
                     // One partial per scale group.  Steps kk (32 dims each) of the first half: 0..3 group 0,
@@ -617,12 +630,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     f32x4_t acc[3][2];
 #pragma unroll
                     for (int j = 0; j < 3; ++j) acc[j][0] = acc[j][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    auto step = [&](int kk, int slot, bool rope) {
+                    // As for bf16, the operands are read ahead of their MFMAs, here one step ahead: two
+                    // steps need more registers than this instance has left.
+                    constexpr int kKAhead = 1;
+                    bf16x8_t ka0[9], ka1[9];
+                    auto read_k = [&](int kk) {
                         const int kg = 9 * half + kk;
                         const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
+                        ka0[kk] = *(const bf16x8_t*)(ap);
+                        ka1[kk] = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                    };
+                    auto step = [&](int kk, int slot, bool rope) {
+                        if (kk + kKAhead < 9) read_k(kk + kKAhead);
+                        __builtin_amdgcn_sched_barrier(0);
                         union { bf16x8_t b; f16x8_t h; } a0, a1, qq;
-                        a0.b = *(const bf16x8_t*)(ap);
-                        a1.b = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                        a0.b = ka0[kk];
+                        a1.b = ka1[kk];
                         qq.b = qv[kk];
                         if (rope) {   // bf16 rope x bf16 Q
                             acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.b, qq.b, acc[slot][0], 0, 0, 0);
@@ -631,7 +654,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                             acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qq.h, acc[slot][0], 0, 0, 0);
                             acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qq.h, acc[slot][1], 0, 0, 0);
                         }
+                        __builtin_amdgcn_sched_barrier(0);
                     };
+#pragma unroll
+                    for (int kk = 0; kk < kKAhead; ++kk) read_k(kk);
                     if (!half) {
 #pragma unroll
                         for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2), false);
