@@ -202,9 +202,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
     // Second-half partial scores of each head block.
     __shared__ __attribute__((aligned(16))) f32x4_t xs_own[4][2][kWave];
-    // FP8: scales of the tile's tokens, one table per expanded tile (the value waves read tile it's while
-    // tile it+1 is expanded)
-    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][KV_FP8 ? kTileTok : 1][4];
+    // FP8: scales of the tile's tokens, [group][token], one table per expanded tile (the value waves read
+    // tile it's while tile it+1 is expanded); one 16-byte read gives a group's scales of 4 tokens
+    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][4][KV_FP8 ? kTileTok : 1];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     // Per-head output multiplier at the end of a split, one table per split parity (bf16): after a
     // split's final barrier the score waves may run through a next split without tiles (no barrier)
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
             make_uint4(fp8x2_to_f16x2<false>(codes.z) & keep, fp8x2_to_f16x2<true>(codes.z) & keep,
                        fp8x2_to_f16x2<false>(codes.w) & keep, fp8x2_to_f16x2<true>(codes.w) & keep);
-        if ((c & 7) == 0) tscale[tile & 1][t][c >> 3] = __uint_as_float(scale & keep);   // +0 when invalid
+        if ((c & 7) == 0) tscale[tile & 1][c >> 3][t] = __uint_as_float(scale & keep);   // +0 when invalid
         if (u < kTileTok * 8) {
             const uint32_t rkeep = 0u - ((vm >> rt) & 1u);
             r.x &= rkeep; r.y &= rkeep; r.z &= rkeep; r.w &= rkeep;
@@ -667,13 +667,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     }
                     // lane: tokens 4g + i (block 0) and 16 + 4g + i (block 1); scale slots per half; the
                     // latent partials carry the Q factor 2^e, the rope partial (second half) does not
+                    // Scale slot j of the lane's tokens 4g + i: group j (first half) or 2 + j (second half;
+                    // its slot 2, the rope, has none).  One 16-byte read holds a group's scales of 4 tokens.
+                    const int g0 = half ? 2 : 0;
+                    const f32x4_t* ts = (const f32x4_t*)tscale[it & 1][0];   // [group][8 quads of tokens]
+                    const f32x4_t sa0 = ts[8 * g0 + g], sb0 = ts[8 * g0 + 4 + g];
+                    const f32x4_t sa1 = ts[8 * (g0 + 1) + g], sb1 = ts[8 * (g0 + 1) + 4 + g];
+                    f32x4_t sa2 = {1.f, 1.f, 1.f, 1.f}, sb2 = {1.f, 1.f, 1.f, 1.f};
+                    if (!half) {
+                        sa2 = ts[16 + g];
+                        sb2 = ts[16 + 4 + g];
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const f32x4_t ta = *(const f32x4_t*)tscale[it & 1][4 * g + i];
-                        const f32x4_t tb = *(const f32x4_t*)tscale[it & 1][16 + 4 * g + i];
-                        const float a0s = (half ? ta[2] : ta[0]) * qscale, a1s = (half ? ta[3] : ta[1]) * qscale;
-                        const float b0s = (half ? tb[2] : tb[0]) * qscale, b1s = (half ? tb[3] : tb[1]) * qscale;
-                        const float a2s = half ? 1.f : ta[2] * qscale, b2s = half ? 1.f : tb[2] * qscale;
+                        const float a0s = sa0[i] * qscale, a1s = sa1[i] * qscale;
+                        const float b0s = sb0[i] * qscale, b1s = sb1[i] * qscale;
+                        const float a2s = half ? 1.f : sa2[i] * qscale, b2s = half ? 1.f : sb2[i] * qscale;
                         s0[i] = a0s * acc[0][0][i] + a1s * acc[1][0][i] + a2s * acc[2][0][i];
                         s1[i] = b0s * acc[0][1][i] + b1s * acc[1][1][i] + b2s * acc[2][1][i];
                     }
@@ -810,8 +819,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 float sc8[8];                // scales of the lane's tokens 4g + i and 16 + 4g + i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sc8[i] = tscale[it & 1][4 * g + i][gv];
-                    sc8[4 + i] = tscale[it & 1][16 + 4 * g + i][gv];
+                    sc8[i] = tscale[it & 1][gv][4 * g + i];
+                    sc8[4 + i] = tscale[it & 1][gv][16 + 4 * g + i];
                 }
                 // Power-of-two normalization of the scales: every scale of the tile lies below
                 // 2^(eb - 126) for the biased exponent eb of the tile's largest scale (lanes l, l^16,
