@@ -168,9 +168,10 @@ def _bf16_order(bits):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
-@pytest.mark.parametrize("kv_dtype", [W.KV_FP8, W.KV_BF16])
-def test_inverse_rope_cache_write(kv_dtype):
-    T, pages, max_pos = 384, 12, 70000
+@pytest.mark.parametrize("kv_dtype,T", [(W.KV_FP8, 384), (W.KV_BF16, 384), (W.KV_FP8, 37), (W.KV_BF16, 37)])
+def test_inverse_rope_cache_write(kv_dtype, T):
+    """Inverse-RoPE write against the oracle; T = 37 leaves the last wave of two tokens half empty."""
+    pages, max_pos = 12, 70000
     log(f"inverse-rope cache write kv_dtype={kv_dtype} T={T}")
     wl = W.cache_write_tokens(DEV, T=T, num_pages=pages, seed=15, spread=3.0)
     g = torch.Generator(device="cpu").manual_seed(16)
