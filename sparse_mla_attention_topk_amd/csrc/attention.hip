@@ -66,13 +66,20 @@ constexpr int kTileLoads = kStageBytes / (16 * kWave);          // 36 direct-to-
 static_assert(kTileLoads * 16 * kWave == kStageBytes, "tile must split into whole wave loads");
 constexpr int kMaxLoadsPerWave = (kTileLoads + kAttnWaves - 1) / kAttnWaves;   // 3 (waves 0..3), else 2
 // FP8 records: [512 e4m3 codes | 4 fp32 scales, one per 128 latent dims | 64 bf16 rope] = 656 B,
-// 41 chunks of 16 B.  A tile's 1312 chunks take 21 loads of 1 KB, the last with 32 active lanes.
-
+// 41 chunks of 16 B.  In a stage, tokens 0..15 sit at 656 t and tokens 16..31 at 656 t + 128: at the
+// 656-byte pitch tokens t and t + 16 start in the same LDS bank, and the transposed value reads take a
+// token from each half in one access.  The stage's 1320 16-byte positions (8 of them the gap) take 21
+// loads of 1 KB, the last with 40 active lanes.
 constexpr int kFp8Chunks = kFp8Record / 16;                           // 41
-constexpr int kFp8StageBytes = kTileTok * kFp8Record;                 // 20992
-constexpr int kFp8TileChunks = kTileTok * kFp8Chunks;                 // 1312
-constexpr int kFp8TileLoads = (kFp8TileChunks + kWave - 1) / kWave;   // 21
-static_assert(kFp8StageBytes % 16 == 0, "FP8 stages must stay 16-byte aligned");
+constexpr int kFp8Gap = 128;                                          // bytes between tokens 15 and 16
+constexpr int kFp8HalfPos = 16 * kFp8Chunks;                          // 656 positions of tokens 0..15
+constexpr int kFp8StageBytes = kTileTok * kFp8Record + kFp8Gap;       // 21120
+constexpr int kFp8StagePos = kFp8StageBytes / 16;                     // 1320
+constexpr int kFp8TileLoads = (kFp8StagePos + kWave - 1) / kWave;     // 21
+static_assert(kFp8StageBytes % 16 == 0 && kFp8Gap % 16 == 0, "FP8 stages must stay 16-byte aligned");
+constexpr int kFp8Stages = 3;                                         // FP8 ring depth
+// byte offset of tile-local token t in an FP8 stage
+__device__ __forceinline__ int fp8_tok(int t) { return t * kFp8Record + (t >= 16 ? kFp8Gap : 0); }
 constexpr uint32_t kNoToken = 0xffffffffu;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -172,24 +179,25 @@ __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
 // in between, weights exp2(s - m) stay below 2^8 and the accumulators need no rescale.
 constexpr float kRescaleSlack = 8.f;
 
-// KV_FP8: the ring holds FP8 records, and every tile is first expanded into a tile with the layout of
-// the bf16 path: the 512 e4m3 codes as fp16 (exact: every e4m3 value is an fp16 value), the bf16 rope
-// copied, and the four fp32 group scales of each token into a small table.  The latent part of the
-// scores is an fp16 product: each score wave holds its latent Q slice in fp16, divided per head by a
-// power of two 2^e that keeps it inside the fp16 range (e = 0 unless |q| reaches 2^15).  Entries of at
-// least 2^-14 * 2^e convert from bf16 exactly; smaller ones land in fp16's subnormal range, off by at
-// most 2^-25 * 2^e, far below the score's own fp32 rounding.  The rope part stays bf16.  The scales are
-// applied in fp32: the score waves keep one partial per 128-dim scale group and sum
-// 2^e x scale x partial; the softmax publishes the fp32 weights, and a value wave, whose 64 dims lie in
-// one group, multiplies them by that group's scales, rounds to fp16 and runs the value product in fp16
-// on the codes as they are.
+// KV_FP8: the ring holds the FP8 records as they are, and both roles read the e4m3 codes from it and
+// widen them in registers (exact: every e4m3 value is an fp16 value).  A score wave reads 8 codes of a
+// token per MFMA operand; a value wave reads 8 tokens' codes of one dim with one transposed LDS read
+// (ds_read_b64_tr_b8).  The latent part of the scores is an fp16 product: each score wave holds its
+// latent Q slice in fp16, divided per head by a power of two 2^e that keeps it inside the fp16 range
+// (e = 0 unless |q| reaches 2^15).  Entries of at least 2^-14 * 2^e convert from bf16 exactly; smaller
+// ones land in fp16's subnormal range, off by at most 2^-25 * 2^e, far below the score's own fp32
+// rounding.  The rope part stays bf16.  The scales are applied in fp32: the score waves keep one
+// partial per 128-dim scale group and sum 2^e x scale x partial; the softmax publishes the fp32
+// weights, and a value wave, whose 64 dims lie in one group, multiplies them by that group's scales,
+// rounds to fp16 and runs the value product in fp16 on the codes as they are.
 // At the magnitudes these scales produce, rounding the scaled values, or the scaled weights, to bf16
 // costs far more accuracy than the fp16 weights.
 template <bool KV_FP8>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnParams p) {
-    // FP8: the ring of FP8 stages, then two expanded tiles (tile it is read while tile it+1 is expanded)
-    constexpr int kStages = 3;   // ring depth: tiles are loaded two tiles ahead
-    constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes + 2 * kStageBytes : kStages * kStageBytes;
+    // Ring depth: tiles are loaded kStages - 1 tiles ahead.  An FP8 tile is 21 KB, so FP8 keeps more of
+    // them in flight.
+    constexpr int kStages = KV_FP8 ? kFp8Stages : 3;
+    constexpr int kRingBytes = KV_FP8 ? kStages * kFp8StageBytes : kStages * kStageBytes;
     constexpr int kRecBytes = KV_FP8 ? kFp8Record : kBf16Record;
     constexpr int kRingStage = KV_FP8 ? kFp8StageBytes : kStageBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
@@ -202,9 +210,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) uint32_t pfrag[4][KV_FP8 ? 8 : 4][kWave];
     // Second-half partial scores of each head block.
     __shared__ __attribute__((aligned(16))) f32x4_t xs_own[4][2][kWave];
-    // FP8: scales of the tile's tokens, [group][token], one table per expanded tile (the value waves read
-    // tile it's while tile it+1 is expanded); one 16-byte read gives a group's scales of 4 tokens
-    __shared__ __attribute__((aligned(16))) float tscale[KV_FP8 ? 2 : 1][4][KV_FP8 ? kTileTok : 1];
     __shared__ float xalpha[4][16];    // per-head rescale factor of the current tile
     // Per-head output multiplier at the end of a split, one table per split parity (bf16): after a
     // split's final barrier the score waves may run through a next split without tiles (no barrier)
@@ -354,8 +359,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // The split being run (ls of the group): its tile count (tiles end at its last valid slot), a valid
     // record for the loads of its invalid slots (record 0 if it has none), and its slot offset.
     // Tile t of the split sits in ring stage (sbase + t) % kStages; sbase runs on from split to split,
-    // since a split with at least two tiles requests the next split's tiles 0 and 1 in the slots where
-    // its own tiles ntiles and ntiles + 1 would go (pf), so the next split starts with them in flight.
+    // since a split with at least kStages - 1 tiles requests the next split's first kStages - 1 tiles in
+    // the slots where its own tiles ntiles, ntiles + 1, ... would go (pf), so the next split starts with
+    // them in flight.
     int cur = 0, ntiles = 0, cur_slot0 = 0, sbase = 0, nx_ntiles = 0;
     bool pf = false, pref_done = false;   // this split requests the next one's first tiles / was requested
     auto split_tiles = [&](int ls) {
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         cur_slot0 = ls * U;
         ntiles = split_tiles(ls);
         nx_ntiles = ls + 1 < ns ? split_tiles(ls + 1) : 0;
-        pf = ntiles >= 2 && nx_ntiles >= 1;
+        pf = ntiles >= kStages - 1 && nx_ntiles >= 1;
     };
     auto end_split = [&]() {
         pref_done = pf;
@@ -380,8 +386,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
     // the second barrier, while the score waves run the softmax), value wave v issues i = v, v + 8,
     // v + 16 (below 21).  Lane l of instruction i moves 16-byte chunk Q = 64 i + l of the stage.
     // bf16: token t = Q / 72 at 16-byte position Q % 72, which holds the record's chunk position ^ f(t).
-    // FP8: token t = Q / 41, chunk Q % 41 in place; chunks past the tile (Q >= 1312, lanes 32..63 of
-    // load 20) are not loaded.
+    // FP8: positions below 656 hold token Q / 41, chunk Q % 41; the 8 gap positions are not loaded;
+    // position Q >= 664 holds token 16 + (Q - 664) / 41, chunk (Q - 664) % 41; positions past the stage
+    // (Q >= 1320, lanes 40..63 of load 20) are not loaded.
     constexpr int kLoads = KV_FP8 ? kFp8TileLoads : kTileLoads;
     constexpr int kLoadWaves = KV_FP8 ? kAttnWaves - kScoreWaves : kAttnWaves;
     static_assert(kLoads <= kMaxLoadsPerWave * kLoadWaves, "loads per wave");
@@ -400,9 +407,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             const int i = lw + kLoadWaves * r;
             const int qd = kWave * (i < kLoads ? i : 0) + ln;
             if (KV_FP8) {
-                const int qc = qd < kFp8TileChunks ? qd : kFp8TileChunks - 1;
+                const int hi = qd >= kFp8HalfPos;
+                int qc = hi ? qd - kFp8HalfPos - kFp8Gap / 16 : qd;   // chunk index within the half
+                qc = qc < 0 ? 0 : (qc < kFp8HalfPos ? qc : kFp8HalfPos - 1);   // gap and tail: not loaded
                 const int t = qc / kFp8Chunks;
-                dtok[r] = 4u * (uint32_t)t;
+                dtok[r] = 4u * (uint32_t)(t + 16 * hi);
                 doff[r] = 16u * (uint32_t)(qc - kFp8Chunks * t);
             } else {
                 const int t = qd / 72;
@@ -412,7 +421,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
     };
     const uint32_t ring_lds = lds_offset(ring);
-    const bool half_load = KV_FP8 && lw + kLoadWaves * (nload - 1) == kFp8TileLoads - 1;   // the 32-lane load
+    // FP8: whether stage position qd is loaded (the gap sits in load 10, load 20 ends the stage)
+    auto fp8_pos_loaded = [](int qd) {
+        return qd < kFp8StagePos && (qd < kFp8HalfPos || qd >= kFp8HalfPos + kFp8Gap / 16);
+    };
+    // The lane id behind a compiler barrier: per-lane offsets derived from it are recomputed where they
+    // are used instead of being held in registers across the tile loop.
+    auto opaque_lane = [&]() {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        return ln;
+    };
     // Slots at or past k_main of the row (the window part) read the window cache; an invalid slot loads
     // record 0 of its cache (always present: num_pages >= 1), whose bytes are replaced by zeros.
     // (slot0 + tile * 32 is the tile's first slot in the group; the group starts at row slot slot_base.)
@@ -430,18 +449,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             src[r] = ((int)(dtok[r] >> 2) >= win_from ? p.kv_win : p.kv) + (uint64_t)ph * kRecBytes + doff[r];
         }
         const uint32_t m0 = ring_lds + (uint32_t)stage * kRingStage + 1024u * (uint32_t)lw;
+        const int ln = opaque_lane();
+        auto fp8_lane_loads = [&](int r) { return fp8_pos_loaded(kWave * (lw + kLoadWaves * r) + ln); };
         if (!KV_FP8) {
             dma_b128(src[0], m0);
             dma_b128(src[1], m0 + 1024u * kAttnWaves);
             if (nload == 3) dma_b128(src[2], m0 + 2048u * kAttnWaves);
-        } else {   // value waves 0..4: 3 loads (the third of wave 4 is the 32-lane load), 5..7: 2
-            dma_b128(src[0], m0);
-            dma_b128(src[1], m0 + 1024u * kLoadWaves);
-            if (nload == 3) {
-                if (!half_load) dma_b128(src[2], m0 + 2048u * kLoadWaves);
-                else if (lane < kFp8TileChunks - kWave * (kFp8TileLoads - 1))
-                    dma_b128(src[2], m0 + 2048u * kLoadWaves);
-            }
+        } else {   // value waves 0..4: 3 loads (the third of wave 4 is the 40-lane load), 5..7: 2; a load
+                   // is never issued with no active lane, so the wave's vmcnt counts stay exact
+            if (fp8_lane_loads(0)) dma_b128(src[0], m0);
+            if (fp8_lane_loads(1)) dma_b128(src[1], m0 + 1024u * kLoadWaves);
+            if (nload == 3 && fp8_lane_loads(2)) dma_b128(src[2], m0 + 2048u * kLoadWaves);
         }
     };
     auto issue_tile = [&](int tile, int stage) { issue_tile_of(cur_slot0, tile, stage); };
@@ -450,121 +468,87 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         if (t < ntiles) issue_tile(t, stg(t));
         else if (pf && t - ntiles < nx_ntiles) issue_tile_of(cur_slot0 + U, t - ntiles, stg(t));
     };
-    // bf16: zero this wave's chunks of invalid tokens (after their dummy data has landed).
+    // Zero this wave's chunks of invalid tokens (after their dummy data has landed).
     auto zero_invalid = [&](int tile, int stage) {
         const uint32_t vm = tile_valid[cur * kMaxUnitTiles + tile];
         if (vm != 0xffffffffu) {
-            uint8_t* sbase = ring + stage * kStageBytes;
+            uint8_t* sbase = ring + stage * kRingStage;
+            const int ln = opaque_lane();
 #pragma unroll
             for (int r = 0; r < kMaxLoadsPerWave; ++r) {
                 if (r < nload) {
-                    const int qd = kWave * (lw + kLoadWaves * r) + lane;
-                    if (!((vm >> (qd / 72)) & 1u)) *(uint4*)(sbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
+                    const int qd = kWave * (lw + kLoadWaves * r) + ln;
+                    int t;
+                    if (KV_FP8) {
+                        if (!fp8_pos_loaded(qd)) continue;
+                        t = qd < kFp8HalfPos ? qd / kFp8Chunks : 16 + (qd - kFp8HalfPos - kFp8Gap / 16) / kFp8Chunks;
+                    } else {
+                        t = qd / 72;
+                    }
+                    if (!((vm >> t) & 1u)) *(uint4*)(sbase + 16 * qd) = make_uint4(0u, 0u, 0u, 0u);
                 }
             }
         }
     };
-    // FP8 (A6): expand the stage's records into an expanded tile, one unit per thread: thread u converts
-    // codes 16c .. 16c+15 of token t = u / 32 (c = u % 32) into fp16 chunks 2c, 2c+1 and, for
-    // c % 8 == 0, stores scale c / 8 of the token; threads 0..255 also copy one 16-byte rope chunk.
-    // Invalid tokens become zeros (codes, rope and scales).
-    auto btile_of = [&](int tile) { return ring + kStages * kFp8StageBytes + (tile & 1) * kStageBytes; };
-    auto dequant_tile = [&](int tile, int stage) {
-        const uint8_t* st = ring + stage * kFp8StageBytes;
-        uint8_t* const btile = btile_of(tile);
-        const uint32_t vm = tile_valid[cur * kMaxUnitTiles + tile];
-        // Invalid tokens are cleared with a bit mask (a select between vectors would go through
-        // scratch memory, whose wait would also wait for the tile loads in flight).
-        int u = tid;
-        asm volatile("" : "+v"(u));   // recompute the unit's offsets per tile (not held across the loop)
-        const int t = u >> 5, c = u & 31;
-        const int rt = (u & (kTileTok * 8 - 1)) >> 3, j = u & 7;   // rope unit (threads below 256 store it)
-        // Every LDS read is issued before any store and waited for once: the codes, the scale of the
-        // unit's group and a rope chunk (the last two read by every thread, stored by some).
-        const uint4 codes = *(const uint4*)(st + t * kFp8Record + 16 * c);
-        const uint32_t scale = *(const uint32_t*)(st + t * kFp8Record + 512 + 4 * (c >> 3));
-        uint4 r = *(const uint4*)(st + rt * kFp8Record + 528 + 16 * j);
-        const uint32_t keep = 0u - ((vm >> t) & 1u);
-        const int f = swz_key(t);
-        uint8_t* dst = btile + t * kBf16Record;
-        // codes 0..7 of the chunk -> fp16 chunk 2c, codes 8..15 -> fp16 chunk 2c+1; the conversion
-        // with scale 1.0 is exact
-        *(uint4*)(dst + 16 * ((2 * c) ^ f)) =
-            make_uint4(fp8x2_to_f16x2<false>(codes.x) & keep, fp8x2_to_f16x2<true>(codes.x) & keep,
-                       fp8x2_to_f16x2<false>(codes.y) & keep, fp8x2_to_f16x2<true>(codes.y) & keep);
-        *(uint4*)(dst + 16 * ((2 * c + 1) ^ f)) =
-            make_uint4(fp8x2_to_f16x2<false>(codes.z) & keep, fp8x2_to_f16x2<true>(codes.z) & keep,
-                       fp8x2_to_f16x2<false>(codes.w) & keep, fp8x2_to_f16x2<true>(codes.w) & keep);
-        if ((c & 7) == 0) tscale[tile & 1][c >> 3][t] = __uint_as_float(scale & keep);   // +0 when invalid
-        if (u < kTileTok * 8) {
-            const uint32_t rkeep = 0u - ((vm >> rt) & 1u);
-            r.x &= rkeep; r.y &= rkeep; r.z &= rkeep; r.w &= rkeep;
-            *(uint4*)(btile + rt * kBf16Record + 16 * ((64 + j) ^ swz_key(rt))) = r;
-        }
-    };
-
     // Per-lane LDS byte offsets inside a stage.
-    //  score operand: token (lane & 15) (+16 for the second block), chunk 4kk + g -> ka[kk & 1] + 128 (kk >> 1)
-    //  transposed value reads: lane supplies token 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3 of a
+    //  bf16 score operand: token (lane & 15) (+16 for the second block), chunk 4kk + g -> ka[kk & 1] + 128 (kk >> 1)
+    //  bf16 transposed value reads: lane supplies token 4g + ((lane & 15) >> 2) and dims 4(lane & 3)..+3 of a
     //  16-dim block db, i.e. chunk 2db + ((lane >> 1) & 1), half (lane & 1) -> vb[db & 3] + 128 (db >> 2)
+    //  FP8 score operand: token (lane & 15) at ka[0] (+16: ka[1]); the step's codes at byte dim + 8g
+    //  FP8 transposed value reads (ds_read_b64_tr_b8: lane i of a 16-lane group receives byte i & 7 of the
+    //  8 bytes supplied by lanes 2e + (i >> 3), e = 0..7): lane supplies token T = 4g + e (e < 4) or
+    //  16 + 4g + e - 4 (e >= 4) for e = (lane & 15) >> 1, and codes 8(lane & 1)..+7 of a 16-dim block, so
+    //  lane i receives dim i of the 8 tokens in the order of the weights' MFMA operand -> vb[0] + dim0
     uint32_t ka[2], vb[4];
     {
         const int lr = lane & 15;
-        const int fa = swz_key(lr);
-        const int tv = 4 * g + (lr >> 2);
-        const int fv = swz_key(tv);
+        if constexpr (!KV_FP8) {
+            const int fa = swz_key(lr);
+            const int tv = 4 * g + (lr >> 2);
+            const int fv = swz_key(tv);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ka[j] = lr * kBf16Record + 16 * ((4 * j + g) ^ fa);
+            for (int j = 0; j < 2; ++j) ka[j] = lr * kBf16Record + 16 * ((4 * j + g) ^ fa);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vb[j] = tv * kBf16Record + 8 * (lane & 1) + 16 * ((2 * j + ((lane >> 1) & 1)) ^ fv);
+            for (int j = 0; j < 4; ++j) vb[j] = tv * kBf16Record + 8 * (lane & 1) + 16 * ((2 * j + ((lane >> 1) & 1)) ^ fv);
+        } else {
+            ka[0] = fp8_tok(lr);
+            ka[1] = fp8_tok(16 + lr);
+            const int e = lr >> 1;
+            const int tv = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+            vb[0] = fp8_tok(tv) + 8 * (lr & 1);
+            vb[1] = vb[2] = vb[3] = 0u;
+        }
     }
 
     // Start of split ls of the group (both roles, after the previous split's final barrier): its first
-    // tiles are requested and, for FP8, tile 0 is expanded.
+    // tiles are requested.
     auto start_split = [&](int ls) {
         begin_split(ls);
         if (!pref_done)
             for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t, stg(t));
-        if (KV_FP8 && ntiles > 0) {
-            if (ntiles > 1 && !pref_done) {   // tile 1 stays in flight (score waves load nothing)
-                if (nload == 3) wait_vmcnt<3>();
-                else if (nload == 2) wait_vmcnt<2>();
-            } else if (nload > 0) {   // (requested by the previous split: the split's output stores may follow them)
-                wait_vmcnt<0>();
-            }
-            wait_lgkmcnt0();
-            __builtin_amdgcn_s_barrier();   // the FP8 data of tile 0 is visible
-            dequant_tile(0, stg(0));
-        }
     };
 
-    // Start of tile `it`, common to both roles.
-    // bf16: wait for this wave's loads of the tile, zero its invalid chunks and make the tile visible
-    //   (first barrier); tile it+1 stays in flight.
-    // FP8: the tile was expanded into expansion buffer it % 2 after the third barrier of tile it-1 (or
-    //   before the loop); the first barrier makes it visible.  The value waves request tile it+2 after
-    //   the second barrier of tile it and wait for their loads of tile it+1 before the third, after
-    //   which all waves expand tile it+1.
+    // Start of tile `it`, common to both roles: wait for this wave's loads of the tile (FP8: only the
+    // value waves load), zero its invalid chunks and make the tile visible (first barrier); tile it+1
+    // stays in flight.
     auto tile_top = [&](int it) {
         const int stage = stg(it);
-        if (!KV_FP8) {
-            if (it == 0 && pref_done) {   // requested by the previous split: its output stores may follow
-                wait_vmcnt<0>();
-            } else if (it + 1 < ntiles || pf) {   // tile it+1 (or the next split's tile 0) stays in flight
-                if (nload == 3) wait_vmcnt<3>();
-                else wait_vmcnt<2>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            zero_invalid(it, stage);
+        if (it == 0 && pref_done) {   // requested by the previous split: its output stores may follow
+            wait_vmcnt<0>();
+        } else {   // the requests after tile it (up to tile it + kStages - 2, or the next split's first) stay in flight
+            int ahead = 0;
+#pragma unroll
+            for (int j = 1; j <= kStages - 2; ++j)
+                ahead += (it + j < ntiles || (pf && it + j - ntiles < nx_ntiles)) ? 1 : 0;
+            wait_vmcnt_upto<3 * (kStages - 2)>(ahead * nload);
         }
+        zero_invalid(it, stage);
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (KV_FP8) return (const uint8_t*)btile_of(it);
-        return (const uint8_t*)(ring + stage * kStageBytes);
+        return (const uint8_t*)(ring + stage * kRingStage);
     };
-    // After the second barrier of tile it, the stage of tile it-1 receives tile it+2: bf16, its value
-    // product ends before that barrier; FP8, it was expanded before the first barrier of tile it.
+    // After the second barrier of tile it, the stage of tile it-1 receives tile it+2: its value product
+    // ends before that barrier.
     // FP8: the value waves issue at the highest wave priority, so their requests go out before the other
     // waves' work in the phase (measured 1% faster per FP8 call; no gain for bf16, where all waves load).
     auto issue_after_second = [&](int it) {
@@ -572,18 +556,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         issue_ahead(it + kStages - 1);
         if (KV_FP8) __builtin_amdgcn_s_setprio(0);
     };
-    // FP8: before the third barrier of tile it, this (value) wave's loads of tile it+1 have landed.
-    auto wait_next_fp8 = [&](int it) {
-        if (KV_FP8 && nload > 0 && it + 1 < ntiles) {
-            if (it + 2 < ntiles || pf) {   // tile it+2 (or the next split's tile 0) stays in flight
-                if (nload == 3) wait_vmcnt<3>();
-                else wait_vmcnt<2>();
-            } else {
-                wait_vmcnt<0>();
-            }
-        }
-    };
-
     // The two roles run separate loops with the same barriers per tile, so the registers of
     // one role (Q, the score accumulators) and of the other (the output accumulators) can share storage.
     float m_run = -INFINITY, l_run = 0.f;   // first-half score waves: reference max, weight sum (lane's tokens)
@@ -630,53 +602,74 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     f32x4_t acc[3][2];
 #pragma unroll
                     for (int j = 0; j < 3; ++j) acc[j][0] = acc[j][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                    // As for bf16, the operands are read ahead of their MFMAs, here one step ahead: two
-                    // steps need more registers than this instance has left.
+                    // As for bf16, the operands are read ahead of their MFMAs: 8 codes of the lane's token
+                    // per latent step (widened to fp16 right before the MFMA), 8 bf16 values per rope step.
                     constexpr int kKAhead = 1;
-                    bf16x8_t ka0[9], ka1[9];
-                    auto read_k = [&](int kk) {
-                        const int kg = 9 * half + kk;
-                        const uint8_t* ap = sb + ka[kg & 1] + 128 * (kg >> 1);
-                        ka0[kk] = *(const bf16x8_t*)(ap);
-                        ka1[kk] = *(const bf16x8_t*)(ap + 16 * kBf16Record);
+                    const uint8_t* kb0 = sb + ka[0] + 288 * half + 8 * g;   // latent codes, block 0 / 1
+                    const uint8_t* kb1 = sb + ka[1] + 288 * half + 8 * g;
+                    uint2 kc0[9], kc1[9];
+                    bf16x8_t kr0[2], kr1[2];
+                    auto read_k = [&](int kk, bool rope) {
+                        if (!rope) {
+                            kc0[kk] = *(const uint2*)(kb0 + 32 * kk);
+                            kc1[kk] = *(const uint2*)(kb1 + 32 * kk);
+                        } else {      // rope dims 512 + 32 (kk - 7) + 8g .. +8: bytes 528 + 64 (kk - 7) + 16g
+                            kr0[kk - 7] = *(const bf16x8_t*)(sb + ka[0] + 528 + 64 * (kk - 7) + 16 * g);
+                            kr1[kk - 7] = *(const bf16x8_t*)(sb + ka[1] + 528 + 64 * (kk - 7) + 16 * g);
+                        }
                     };
-                    auto step = [&](int kk, int slot, bool rope) {
-                        if (kk + kKAhead < 9) read_k(kk + kKAhead);
+                    auto widen = [](uint2 c) {
+                        union { uint32_t u[4]; f16x8_t h; } r;
+                        r.u[0] = fp8x2_to_f16x2<false>(c.x);
+                        r.u[1] = fp8x2_to_f16x2<true>(c.x);
+                        r.u[2] = fp8x2_to_f16x2<false>(c.y);
+                        r.u[3] = fp8x2_to_f16x2<true>(c.y);
+                        return r.h;
+                    };
+                    auto step = [&](int kk, int slot, bool rope, int nlat) {
+                        if (kk + kKAhead < 9) read_k(kk + kKAhead, kk + kKAhead >= nlat);
                         __builtin_amdgcn_sched_barrier(0);
-                        union { bf16x8_t b; f16x8_t h; } a0, a1, qq;
-                        a0.b = ka0[kk];
-                        a1.b = ka1[kk];
-                        qq.b = qv[kk];
                         if (rope) {   // bf16 rope x bf16 Q
-                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0.b, qq.b, acc[slot][0], 0, 0, 0);
-                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1.b, qq.b, acc[slot][1], 0, 0, 0);
+                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr0[kk - 7], qv[kk], acc[slot][0], 0, 0, 0);
+                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr1[kk - 7], qv[kk], acc[slot][1], 0, 0, 0);
                         } else {      // fp16 codes x fp16 Q
-                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qq.h, acc[slot][0], 0, 0, 0);
-                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qq.h, acc[slot][1], 0, 0, 0);
+                            union { bf16x8_t b; f16x8_t h; } qq;
+                            qq.b = qv[kk];
+                            acc[slot][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen(kc0[kk]), qq.h, acc[slot][0], 0, 0, 0);
+                            acc[slot][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(widen(kc1[kk]), qq.h, acc[slot][1], 0, 0, 0);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     };
-#pragma unroll
-                    for (int kk = 0; kk < kKAhead; ++kk) read_k(kk);
                     if (!half) {
 #pragma unroll
-                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2), false);
+                        for (int kk = 0; kk < kKAhead; ++kk) read_k(kk, false);
+#pragma unroll
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 4 ? 0 : (kk < 8 ? 1 : 2), false, 9);
                     } else {
 #pragma unroll
-                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 3 ? 0 : (kk < 7 ? 1 : 2), kk >= 7);
+                        for (int kk = 0; kk < kKAhead; ++kk) read_k(kk, false);
+#pragma unroll
+                        for (int kk = 0; kk < 9; ++kk) step(kk, kk < 3 ? 0 : (kk < 7 ? 1 : 2), kk >= 7, 7);
                     }
                     // lane: tokens 4g + i (block 0) and 16 + 4g + i (block 1); scale slots per half; the
-                    // latent partials carry the Q factor 2^e, the rope partial (second half) does not
-                    // Scale slot j of the lane's tokens 4g + i: group j (first half) or 2 + j (second half;
-                    // its slot 2, the rope, has none).  One 16-byte read holds a group's scales of 4 tokens.
+                    // latent partials carry the Q factor 2^e, the rope partial (second half) does not.
+                    // Scale slot j of a token: group j (first half) or 2 + j (second half; its slot 2, the
+                    // rope, has none).  A token's 4 group scales follow its codes in the record.
                     const int g0 = half ? 2 : 0;
-                    const f32x4_t* ts = (const f32x4_t*)tscale[it & 1][0];   // [group][8 quads of tokens]
-                    const f32x4_t sa0 = ts[8 * g0 + g], sb0 = ts[8 * g0 + 4 + g];
-                    const f32x4_t sa1 = ts[8 * (g0 + 1) + g], sb1 = ts[8 * (g0 + 1) + 4 + g];
+                    const uint8_t* sp = sb + fp8_tok(4 * g) + 512 + 4 * g0;   // + 656 i: token 4g + i
+                    constexpr int kHi = 16 * kFp8Record + kFp8Gap;            // token 16 + 4g + i
+                    f32x4_t sa0, sb0, sa1, sb1;
                     f32x4_t sa2 = {1.f, 1.f, 1.f, 1.f}, sb2 = {1.f, 1.f, 1.f, 1.f};
-                    if (!half) {
-                        sa2 = ts[16 + g];
-                        sb2 = ts[16 + 4 + g];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float2 a = *(const float2*)(sp + kFp8Record * i);
+                        const float2 b = *(const float2*)(sp + kHi + kFp8Record * i);
+                        sa0[i] = a.x; sa1[i] = a.y;
+                        sb0[i] = b.x; sb1[i] = b.y;
+                        if (!half) {
+                            sa2[i] = *(const float*)(sp + kFp8Record * i + 8);
+                            sb2[i] = *(const float*)(sp + kHi + kFp8Record * i + 8);
+                        }
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -751,10 +744,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                 }
                 if (lane < 16) xalpha[shb][lane] = 1.f;
             }
-            wait_next_fp8(it);
             wait_lgkmcnt0();
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, stg(it + 1));
         }
         // ---- A10 (score waves), after the split's last unit: output multiplier and LSE of the first
         // halves' heads.  With one split the sink joins here: it adds e^sink to the denominator and
@@ -785,7 +776,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         }
         __syncthreads();
         if (score_ok && !half && lane < 16) {
-            const int head = head0 + shb * 16 + lane;
+            const int head = head0 + shb * 16 + opaque_lane();   // address computed here, not held from the prologue
             if (p.n_splits == 1) {
                 if (p.lse) p.lse[row * p.H + head] = lse_v;
             } else {
@@ -817,10 +808,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             } else {
                 const int gv = vdim0 >> 7;   // the scale group of this wave's dims
                 float sc8[8];                // scales of the lane's tokens 4g + i and 16 + 4g + i
+                const uint8_t* sp = sb + fp8_tok(4 * g) + 512 + 4 * gv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sc8[i] = tscale[it & 1][gv][4 * g + i];
-                    sc8[4 + i] = tscale[it & 1][gv][16 + 4 * g + i];
+                    sc8[i] = *(const float*)(sp + kFp8Record * i);
+                    sc8[4 + i] = *(const float*)(sp + 16 * kFp8Record + kFp8Gap + kFp8Record * i);
                 }
                 // Power-of-two normalization of the scales: every scale of the tile lies below
                 // 2^(eb - 126) for the biased exponent eb of the tile's largest scale (lanes l, l^16,
@@ -862,34 +854,45 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     }
                 }
             }
-            const uint8_t* vp0 = sb + 128 * (vdim0 / 64);
+            if constexpr (!KV_FP8) {
+                const uint8_t* vp0 = sb + 128 * (vdim0 / 64);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {   // 16-dim block within this wave's 64 dims
-                const uint8_t* vp = vp0 + vb[d];
-                union { bf16x8_t v; i16x4_t h[2]; uint4 u; f16x8_t f; } va;
-                va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
-                va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
-                if constexpr (!KV_FP8) {
+                for (int d = 0; d < 4; ++d) {   // 16-dim block within this wave's 64 dims
+                    const uint8_t* vp = vp0 + vb[d];
+                    union { bf16x8_t v; i16x4_t h[2]; } va;
+                    va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vp));
+                    va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(vp + 16 * kBf16Record));
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         union { uint4 u; bf16x8_t v; } pv;
                         pv.u = pb[b];
                         oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pv.v, oacc[b][d], 0, 0, 0);
                     }
-                } else {   // the tile holds the codes as fp16
+                }
+            } else {   // 8 tokens' codes of one dim per lane, widened to fp16
+                const uint8_t* vp0 = sb + vb[0] + vdim0;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const i32x2_t vc = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2_t*)(vp0 + 16 * d));
+                    union { uint32_t u[4]; f16x8_t h; } va;
+                    va.u[0] = fp8x2_to_f16x2<false>((uint32_t)vc[0]);
+                    va.u[1] = fp8x2_to_f16x2<true>((uint32_t)vc[0]);
+                    va.u[2] = fp8x2_to_f16x2<false>((uint32_t)vc[1]);
+                    va.u[3] = fp8x2_to_f16x2<true>((uint32_t)vc[1]);
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         union { uint4 u; f16x8_t v; } pv;
                         pv.u = pb[b];
-                        oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.f, pv.v, oacc[b][d], 0, 0, 0);
+                        oacc[b][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pv.v, oacc[b][d], 0, 0, 0);
                     }
                 }
             }
         };
         // The value product of tile it runs after the first barrier of tile it+1, beside the scores of
         // tile it+1: its weights and rescale factors are rewritten only after the second barrier of
-        // tile it+1, its 1152-byte tile (the ring stage, or the FP8 expansion buffer) only after that too.
+        // tile it+1, its ring stage only after that too.
       for (int ls = 0; ls < ns; ++ls) {
         start_split(ls);
         const int su = split0 + ls;   // unit of the row
@@ -907,9 +910,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             wait_lgkmcnt0();                 // this wave's reads of tile it-1 are done
             __builtin_amdgcn_s_barrier();   // second-half partials published
             issue_after_second(it);
-            wait_next_fp8(it);
             __builtin_amdgcn_s_barrier();   // P fragments and rescale factors published
-            if (KV_FP8 && it + 1 < ntiles) dequant_tile(it + 1, stg(it + 1));
             sb_prev = sb;
         }
         if (ntiles > 0) value_product(ntiles - 1, sb_prev);
@@ -922,9 +923,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
             if (b >= nhb) break;
             float inv = xmul[KV_FP8 ? 0 : (ls & 1)][b][lane & 15];
             if (KV_FP8 && e_run > 0) inv = __builtin_ldexpf(inv, e_run - 127);   // undo the scale normalization
-            int head = head0 + 16 * b + (lane & 15);
-            if (KV_FP8) asm volatile("" : "+v"(head));   // FP8: addresses computed per split (not held across splits)
-            const int64_t pidx = (((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head) * kDv + vdim0 + 4 * g;
+            // FP8: the lane's addresses are computed per split from an opaque lane id (not held across the loop)
+            const int ln = KV_FP8 ? opaque_lane() : lane;
+            const int head = head0 + 16 * b + (ln & 15);
+            const int64_t pidx = (((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head) * kDv + vdim0 + 4 * (ln >> 4);
             if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
                 float* wo = (float*)p.ws_o + pidx;
 #pragma unroll
@@ -932,7 +934,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
                     *(f32x4_t*)(wo + 16 * d) = (f32x4_t){oacc[b][d][0] * inv, oacc[b][d][1] * inv,
                                                          oacc[b][d][2] * inv, oacc[b][d][3] * inv};
             } else {
-                uint16_t* orow = p.n_splits == 1 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * g
+                uint16_t* orow = p.n_splits == 1 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * (ln >> 4)
                                                  : (uint16_t*)p.ws_o + pidx;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {

@@ -8,6 +8,7 @@ namespace smla {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -24,6 +25,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt out of range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most n (wave-uniform, 0 <= n <= MAX) vector-memory operations are outstanding.
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    if constexpr (MAX > 0) {
+        if (n >= MAX) {
+            wait_vmcnt<MAX>();
+            return;
+        }
+        wait_vmcnt_upto<MAX - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
