@@ -22,7 +22,7 @@
 // unpadded (1152 B); the 16-byte chunks of tile-local token t are XOR-swizzled with f(t) = (t >> 1) & 7,
 // the mapping measured to keep the operand reads below free of LDS bank conflicts on gfx950.  FP8
 // caches: a tile is 21 loads of 656-B records, issued by the 8 value waves alone in a phase where
-// they would otherwise wait; all 16 waves then expand it into an fp16 tile of the layout above.
+// they would otherwise wait; both roles read the e4m3 codes from the ring and widen them in registers.
 //
 // Roles (at most 128 registers per wave at 16 waves per CU):
 //   score waves 0..7:  wave (hb, half) computes the partial scores of heads hb*16 .. +16 over dims
@@ -33,7 +33,8 @@
 //                      of their 16 heads and publish the bf16 weights P and the rescale factors.
 //   value waves 8..15: wave 8 + v accumulates dims 64v .. +64 of all 64 heads:
 //                        O^T[16 dims x 16 heads] += V^T[16 dims x 32 tok] . P^T[32 tok x 16 heads]
-//                      (A = V^T via ds_read_b64_tr_b16 transposed reads, each feeding 4 head blocks).
+//                      (A = V^T via ds_read_b64_tr_b16 transposed reads, FP8: ds_read_b64_tr_b8 of the
+//                      codes, each feeding 4 head blocks).
 //   The S^T accumulator layout already holds a head's token weights in the B-operand layout of the
 //   value MFMA, so no register transpose is needed.
 //
