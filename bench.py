@@ -351,6 +351,27 @@ def _copy_probe(torch, dev):
     torch.cuda.synchronize()
 
 
+def _stream_copy_GBps(torch, dev, s, reps: int = 9) -> float:
+    """Measured device-to-device copy rate of 1 GiB on the bench's stream: bytes read plus bytes written
+    per second, the median of `reps` copies (the practical streaming peak the gather is compared with)."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    with torch.cuda.stream(s):
+        a.fill_(1.0)
+        b.copy_(a)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            b.copy_(a)
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+    times.sort()
+    del a, b
+    return 2.0 * (1 << 30) / (times[len(times) // 2] * 1e-3) / 1e9
+
+
 def _base_line(args, metric, value, unit, ms, reps, dtype, config):
     return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
@@ -409,6 +430,7 @@ def bench_decode(args, cpu: CpuBaseline):
     wall = time.perf_counter() - w0
     rows_per_s = B / (ms_step * 1e-3)
     achieved = gathered / (attn_ms * 1e-3) / 1e9
+    copy_GBps = _stream_copy_GBps(torch, dev, s)
     if args.copy_probe:
         _copy_probe(torch, dev)
 
@@ -439,6 +461,7 @@ def bench_decode(args, cpu: CpuBaseline):
     line.update({
         "gathered_kv_GBps": achieved,
         "step_gathered_kv_GBps": gathered / (ms_step * 1e-3) / 1e9,
+        "stream_copy_GBps": copy_GBps, "frac_of_stream_copy": achieved / copy_GBps,
         "attention_ms": attn_ms, "topk_ms": topk_ms, "wall_s": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
