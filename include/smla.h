@@ -151,8 +151,8 @@ smla_status smla_topk_per_row(const float* scores, const int64_t* row_offsets, i
  *   out: bf16 [rows, H, 512], 16-byte aligned; lse: fp32 [rows, H] or NULL.
  *   ws: attention workspace (256-byte aligned) of at least the size smla_workspace_size reports for
  *   a capacity with max_rows >= 1; rows beyond what it holds are processed in further launches.
- *   It holds the split partials (bf16; FP8 caches: fp32) and their fp32 LSEs (only with more than
- *   one split); calls that share a
+ *   It holds the split partials (bf16; FP8 caches: fp16 with one fp32 power-of-two factor per split
+ *   and 128-dim group) and their fp32 LSEs (only with more than one split); calls that share a
  *   workspace must be ordered on one stream.
  * Requires H a multiple of 16 in [16, 128], 1 <= k <= 16384, rows >= 0, num_pages >= 1. */
 smla_status smla_sparse_mla_decode(const void* q, int64_t q_row_stride, const void* kv, int32_t kv_dtype,

@@ -117,8 +117,9 @@ struct AttnParams {
     int32_t row0;
     uint16_t* out;
     float* lse;
-    void* ws_o;          // [rows][splits][H][512] split partials: bf16 (bf16 cache) or fp32 (FP8 cache)
+    void* ws_o;          // [rows][splits][H][512] split partials: bf16 (bf16 cache) or fp16 (FP8 cache, normalized)
     float* ws_lse;       // fp32 [rows][splits][H]
+    float* ws_gsc;       // FP8: fp32 [rows][splits][4], the factor 2^(e - 127) of each 128-dim group's partials
     const float* sink;   // fp32 [H] per-head sink logits (natural-log units of the scaled scores), or null
 };
 
@@ -923,17 +924,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
         for (int b = 0; b < 4; ++b) {
             if (b >= nhb) break;
             float inv = xmul[KV_FP8 ? 0 : (ls & 1)][b][lane & 15];
-            if (KV_FP8 && e_run > 0) inv = __builtin_ldexpf(inv, e_run - 127);   // undo the scale normalization
+            // undo the scale normalization, except in FP8 split partials, which keep it (and record it)
+            if (KV_FP8 && e_run > 0 && p.n_splits == 1) inv = __builtin_ldexpf(inv, e_run - 127);
             // FP8: the lane's addresses are computed per split from an opaque lane id (not held across the loop)
             const int ln = KV_FP8 ? opaque_lane() : lane;
             const int head = head0 + 16 * b + (ln & 15);
             const int64_t pidx = (((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * p.H + head) * kDv + vdim0 + 4 * (ln >> 4);
-            if (KV_FP8 && p.n_splits > 1) {   // fp32 partials
-                float* wo = (float*)p.ws_o + pidx;
+            if (KV_FP8 && p.n_splits > 1) {   // fp16 partials in the normalized domain (|value| < 896)
+                uint16_t* wo = (uint16_t*)p.ws_o + pidx;
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    *(f32x4_t*)(wo + 16 * d) = (f32x4_t){oacc[b][d][0] * inv, oacc[b][d][1] * inv,
-                                                         oacc[b][d][2] * inv, oacc[b][d][3] * inv};
+                for (int d = 0; d < 4; ++d) {
+                    uint2 w;
+                    w.x = pack_f16x2_rne(oacc[b][d][0] * inv, oacc[b][d][1] * inv);
+                    w.y = pack_f16x2_rne(oacc[b][d][2] * inv, oacc[b][d][3] * inv);
+                    *(uint2*)(wo + 16 * d) = w;
+                }
+                if (b == 0 && ln == 0 && (vdim0 & 127) == 0)   // one wave per group records its factor
+                    p.ws_gsc[((int64_t)rloc * p.n_splits + su / kUnitsPerSplit) * 4 + (vdim0 >> 7)] =
+                        e_run > 0 ? __builtin_ldexpf(1.f, e_run - 127) : 1.f;
             } else {
                 uint16_t* orow = p.n_splits == 1 ? p.out + (row * p.H + head) * (int64_t)kDv + vdim0 + 4 * (ln >> 4)
                                                  : (uint16_t*)p.ws_o + pidx;
@@ -956,12 +964,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_kernel(const AttnP
 // out = sum_s (e^(lse_s - m) / sum) * O_s, rounded to bf16, computed as an online merge over the
 // splits in order (the running max m and sum are updated split by split), and then the head's sink
 // logit, if any, as one more term with no output.  64 threads per (row, head), 8 dims each.
-// Partials are bf16 (bf16 caches) or fp32 (FP8 caches).
+// Partials are bf16 (bf16 caches) or fp16 times a per-(split, group) power-of-two factor (FP8 caches).
 constexpr int kCombineHeads = 16;   // heads per combine workgroup (64 threads each)
 
-template <bool F32>
+template <bool FP8>
 __global__ __launch_bounds__(64 * kCombineHeads) void split_combine_kernel(const void* __restrict__ ws_o,
-                                                            const float* __restrict__ ws_lse, int S, int H,
+                                                            const float* __restrict__ ws_lse,
+                                                            const float* __restrict__ ws_gsc, int S, int H,
                                                             int row0, const float* __restrict__ sink,
                                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int hq = H / kCombineHeads;
@@ -981,14 +990,19 @@ __global__ __launch_bounds__(64 * kCombineHeads) void split_combine_kernel(const
             const int s = s0 + j < S ? s0 + j : S - 1;   // loads stay unconditional (clamped)
             l4[j] = s0 + j < S ? ls[(int64_t)s * H] : -INFINITY;
             const int64_t off = (((int64_t)rloc * S + s) * H + head) * kDv + d;
-            if (F32) {
-                const f32x4_t a = *(const f32x4_t*)((const float*)ws_o + off);
-                const f32x4_t b = *(const f32x4_t*)((const float*)ws_o + off + 4);
+            const uint4 u = *(const uint4*)((const uint16_t*)ws_o + off);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+            if (FP8) {   // fp16 pairs times the split's factor for this thread's group (d / 128)
+                const float f = ws_gsc[((int64_t)rloc * S + s) * 4 + (d >> 7)];
+                typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
+                typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { v[j][e] = a[e]; v[j][4 + e] = b[e]; }
+                for (int e = 0; e < 4; ++e) {
+                    const f2 x = __builtin_convertvector(__builtin_bit_cast(h2, wd[e]), f2);
+                    v[j][2 * e] = x[0] * f;
+                    v[j][2 * e + 1] = x[1] * f;
+                }
             } else {
-                const uint4 u = *(const uint4*)((const uint16_t*)ws_o + off);
-                const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[j][2 * e] = __uint_as_float(wd[e] << 16);
@@ -1109,10 +1123,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     p.out = (uint16_t*)a.out;
     p.lse = a.lse;
     p.sink = a.sink;
-    // Workspace per row: partials of every (split, head), then their LSEs (none with one split).  The
+    // Workspace per row: partials of every (split, head), then their LSEs, then (FP8) the group factors
+    // of every split (none with one split).  The
     // host validation sizes it for 512-slot units, at least as many splits as any unit size here.
-    const size_t o_per_row = p.n_splits > 1 ? (size_t)p.n_splits * a.H * kDv * (fp8 ? 4 : 2) : 0;
-    const size_t per_row = p.n_splits > 1 ? o_per_row + (size_t)p.n_splits * a.H * sizeof(float) : 0;
+    const size_t o_per_row = p.n_splits > 1 ? (size_t)p.n_splits * a.H * kDv * 2 : 0;
+    const size_t lse_per_row = p.n_splits > 1 ? (size_t)p.n_splits * a.H * sizeof(float) : 0;
+    const size_t gsc_per_row = p.n_splits > 1 && fp8 ? (size_t)p.n_splits * 4 * sizeof(float) : 0;
+    const size_t per_row = o_per_row + lse_per_row + gsc_per_row;
     int rows_per_launch = a.rows;
     if (per_row > 0) {
         const size_t fit = a.ws_bytes / per_row;
@@ -1125,6 +1142,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
         // Workspace regions for a launch of rows_per_launch rows: partials, then LSEs.
         p.ws_o = per_row > 0 ? a.ws : nullptr;
         p.ws_lse = per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch * o_per_row) : nullptr;
+        p.ws_gsc = gsc_per_row > 0 ? (float*)((uint8_t*)a.ws + (size_t)rows_per_launch * (o_per_row + lse_per_row))
+                                   : nullptr;
         // bf16: launches with at least twice as many (row, split) items as CUs run 2 or 4 consecutive
         // splits of a row per workgroup, one after the other: the index translation and Q serve them
         // all.  Each split reduces its own tiles in order with its own softmax state, so the bits are the
@@ -1152,11 +1171,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
             if (fp8)
                 hipLaunchKernelGGL(split_combine_kernel<true>, dim3(n * (a.H / kCombineHeads)), dim3(64 * kCombineHeads), 0,
                                    stream, p.ws_o,
-                                   p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
+                                   p.ws_lse, p.ws_gsc, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             else
                 hipLaunchKernelGGL(split_combine_kernel<false>, dim3(n * (a.H / kCombineHeads)), dim3(64 * kCombineHeads), 0,
                                    stream, p.ws_o,
-                                   p.ws_lse, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
+                                   p.ws_lse, p.ws_gsc, p.n_splits, a.H, row0, p.sink, p.out, p.lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

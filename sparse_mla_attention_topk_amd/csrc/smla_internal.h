@@ -26,21 +26,23 @@ inline int attn_unit_slots(int k, int k_win) {
     }
 }
 // Splits of a row, each reduced by one workgroup before the split combine: units of 512 slots (bf16
-// caches) or pairs of them (FP8 caches, whose fp32 partials cost twice the bytes).  A function of k and
-// the cache type only, never of the batch.
+// caches) or pairs of them (FP8 caches, whose partials carry per-group power-of-two factors).  A function
+// of k and the cache type only, never of the batch.
 inline int attn_num_splits(int k, int kv_dtype) {
     const int u = attn_num_units(k);
     return kv_dtype == 1 ? (u + kFp8UnitsPerSplit - 1) / kFp8UnitsPerSplit : u;
 }
 
 // Workspace of the attention entry points, per query row (0 when k fits one split): the partial
-// outputs of every (split, head) -- bf16 for bf16 caches, fp32 for FP8 caches, whose group scales
-// make outputs large enough that bf16 partials would cost visible accuracy -- then their fp32 LSEs.
+// outputs of every (split, head) in 16-bit form -- bf16 for bf16 caches; fp16 for FP8 caches, in the
+// kernel's normalized domain (the output times 2^(127 - e) for the biased exponent e of the largest
+// group scale the split met, which keeps them below 896) -- then their fp32 LSEs, then (FP8) the factor
+// 2^(e - 127) of every (split, 128-dim group) in fp32.
 inline size_t attn_ws_o_bytes_per_row(int H, int k, int kv_dtype) {
-    return (size_t)attn_num_splits(k, kv_dtype) * H * 512 * (kv_dtype == 1 ? 4 : 2);
+    return (size_t)attn_num_splits(k, kv_dtype) * H * 512 * 2;
 }
 inline size_t attn_ws_lse_bytes_per_row(int H, int k, int kv_dtype) {
-    return (size_t)attn_num_splits(k, kv_dtype) * H * 4;
+    return (size_t)attn_num_splits(k, kv_dtype) * (H + (kv_dtype == 1 ? 4 : 0)) * 4;
 }
 inline size_t attn_ws_bytes_per_row(int H, int k, int kv_dtype) {
     if (attn_num_splits(k, kv_dtype) <= 1) return 0;

@@ -88,7 +88,8 @@ def test_workspace_size_derives_from_capacity_only():
     _, at2 = smla.workspace_size(_cap(max_rows=3, max_k=513, num_heads=16))
     assert at2 == 3 * 2 * 16 * (512 * 2 + 4)
     _, at3 = smla.workspace_size(_cap(max_rows=2, max_k=2048, num_heads=64, kv_dtype=smla.KV_FP8))
-    assert at3 == 2 * 2 * 64 * (512 * 4 + 4)    # FP8 caches: fp32 partials, splits of 1024 slots
+    # FP8 caches: splits of 1024 slots, fp16 partials and fp32 LSEs, then 4 fp32 group factors per split
+    assert at3 == 2 * (2 * 64 * (512 * 2 + 4) + 2 * 4 * 4)
 
 
 P = ctypes.c_void_p
