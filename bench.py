@@ -125,7 +125,8 @@ def summarize_trace(d):
 
 
 def traffic_record(fetch_dir, write_dir, workload):
-    """Copy-calibrated HBM bytes per attention call: FETCH_SIZE and WRITE_SIZE are in KiB per dispatch;
+    """Copy-calibrated HBM bytes per attention call (topk_c1: per top-k call): FETCH_SIZE and WRITE_SIZE are
+    in KiB per dispatch;
     each is scaled by what the same counter reads for the 1 GiB copy of --copy-probe."""
     import hashlib
     f, w = _counter_means([fetch_dir]), _counter_means([write_dir])
@@ -133,7 +134,13 @@ def traffic_record(fetch_dir, write_dir, workload):
     ff = 1048576.0 / max(f[(copy, "FETCH_SIZE")])
     fw = 1048576.0 / max(w[(copy, "WRITE_SIZE")])
     fp8 = workload == "decode_fp8"
-    ks = [f"smla::sparse_mla_kernel<{'true' if fp8 else 'false'}>", f"smla::split_combine_kernel<{'true' if fp8 else 'false'}>"]
+    if workload == "topk_c1":   # the top-k call: every top-k kernel it dispatches
+        ks = sorted({kk for (kk, c) in f if kk.startswith("smla::topk_")})
+        src = "sparse_mla_attention_topk_amd/csrc/topk.hip"
+    else:
+        ks = [f"smla::sparse_mla_kernel<{'true' if fp8 else 'false'}>",
+              f"smla::split_combine_kernel<{'true' if fp8 else 'false'}>"]
+        src = "sparse_mla_attention_topk_amd/csrc/attention.hip"
     total = 0.0
     print(f"calibration: FETCH_SIZE x {ff:.5f}, WRITE_SIZE x {fw:.5f}")
     print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB (scaled) | written MB (scaled) |")
@@ -146,7 +153,6 @@ def traffic_record(fetch_dir, write_dir, workload):
         print(f"| `{k}` | {fv:.1f} | {wv:.1f} | {fv * ff * 1024 / 1e6:.2f} | {wv * fw * 1024 / 1e6:.2f} |")
         if k in ks:
             total += (fv * ff + wv * fw) * 1024
-    src = "sparse_mla_attention_topk_amd/csrc/attention.hip"
     sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
     print(f"\ntraffic-record: source={src} sha256={sha} bytes_per_call={int(round(total))}")
 
@@ -154,6 +160,7 @@ def traffic_record(fetch_dir, write_dir, workload):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_bf16_B64_H64_k2048_hbm_traffic.md")
 INDEXER_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "indexer_B64_Hi64_L8K-64K_hbm_traffic.md")
 FP8_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_fp8_B128_H64_k2048_hbm_traffic.md")
+TOPK_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "topk_c1_R64_L65536_k2048_hbm_traffic.md")
 
 
 def measured_traffic(record=TRAFFIC_RECORD):
@@ -499,6 +506,8 @@ def bench_topk(args, cpu: CpuBaseline):
     n = max(args.steps, copies)
     ms, reps = _timed_calls(torch, s, call, n, args.warmup, args.min_timed_ms, not args.no_graph)
     alg = R * L * 4 + R * k * 4
+    if args.copy_probe:
+        _copy_probe(torch, dev)
     achieved = alg / (ms * 1e-3) / 1e9
     cpu_line = None
     if args.cpu_rows > 0:
@@ -518,7 +527,8 @@ def bench_topk(args, cpu: CpuBaseline):
     line["steps"] = n
     line.update({
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "topk_per_row call",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(TOPK_TRAFFIC_RECORD),
+                     "kernel": "topk_per_row call",
                      "algorithmic_bytes_per_launch": alg},
         "cpu_baseline": cpu_line,
     })
